@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module only draws random tensors and describes workload shapes; it holds
+none of the attention arithmetic.  Both the GPU path and the fp64 CPU oracle are
+fed from here, so the two sides always see bit-identical bf16 inputs.
+
+Recipe (the pages give shapes, not data): Q, K, V are iid N(0, 1) drawn in fp32
+from ``torch.Generator('cpu').manual_seed(seed)`` in the order q, k, v, then
+rounded to bf16 with round-to-nearest-even.  Layout is contiguous
+[batch, seqlen, nheads, headdim] (the page "FlashAttention：快速且内存高效的准确注意力机制",
+section "参数说明", gives q/k/v as (batch_size, seqlen, nheads, headdim)).
+ALiBi slopes follow the geometric recipe 2^(-8 (i+1) / nheads), fp32, one per head.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention forward workload (shapes and mask options, no data)."""
+
+    name: str
+    batch: int
+    nheads: int
+    seqlen_q: int
+    seqlen_k: int
+    headdim: int
+    causal: bool = False
+    window_left: int = -1
+    window_right: int = -1
+    alibi: bool = False
+    num_splits: int = 0  # >0: split-KV decode pair (partial kernel + combine)
+    seed: int = 0
+
+    @property
+    def softmax_scale(self) -> float:
+        """Default scale 1/sqrt(headdim), rounded to the fp32 value the kernels receive."""
+        return float(torch.tensor(1.0 / math.sqrt(self.headdim), dtype=torch.float32))
+
+
+# The five workloads the method is checked and timed on.  Seeds 0..4 follow the
+# list order; the causal and non-causal variants of the benchmark shape share
+# one seed (same tensors).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 128, 64, seed=0),
+    "bench_s2048": Workload("bench_s2048", 8, 16, 2048, 2048, 128, seed=1),
+    "bench_s2048_causal": Workload("bench_s2048_causal", 8, 16, 2048, 2048, 128, causal=True, seed=1),
+    "local_alibi_s8192": Workload("local_alibi_s8192", 2, 32, 8192, 8192, 64, causal=True,
+                                  window_left=1024, window_right=0, alibi=True, seed=2),
+    "hd256_s16384": Workload("hd256_s16384", 1, 8, 16384, 16384, 256, seed=3),
+    "decode_s32768": Workload("decode_s32768", 8, 16, 1, 32768, 128, causal=True, num_splits=16, seed=4),
+}
+
+
+def sweep_workload(seqlen: int, causal: bool = False) -> Workload:
+    """The pages' benchmark recipe: hidden 2048 = 16 heads x 128, batch = 16384 / seqlen."""
+    return Workload(f"sweep_s{seqlen}{'_causal' if causal else ''}", 16384 // seqlen, 16,
+                    seqlen, seqlen, 128, causal=causal, seed=1)
+
+
+def make_qkv(batch: int, seqlen_q: int, seqlen_k: int, nheads: int, headdim: int, seed: int,
+             nheads_k: Optional[int] = None):
+    """Draw q [B,Sq,H,D], k and v [B,Sk,H,D] as bf16 CPU tensors from one seeded generator."""
+    hk = nheads if nheads_k is None else nheads_k
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn(batch, seqlen_q, nheads, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn(batch, seqlen_k, hk, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(batch, seqlen_k, hk, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v
+
+
+def make_alibi_slopes(nheads: int) -> torch.Tensor:
+    """fp32 slopes 2^(-8 (i+1) / nheads), i = 0..nheads-1."""
+    return torch.tensor([2.0 ** (-8.0 * (i + 1) / nheads) for i in range(nheads)], dtype=torch.float32)
+
+
+def workload_inputs(w: Workload):
+    """(q, k, v, alibi_slopes or None) for a workload, all on the CPU."""
+    q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed)
+    slopes = make_alibi_slopes(w.nheads) if w.alibi else None
+    return q, k, v, slopes

@@ -1,0 +1,285 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention (forward), TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  The GPU library never calls it and shares no code with it: this
+file is the plain definition written out, row by row, with a full-row softmax
+(no tiling, no online rescaling), so that it can be checked against the pages
+by eye.
+
+Sources (the pages are web articles; each is cited by title and section):
+  [FA-overview] "FlashAttention：快速且内存高效的准确注意力机制"
+                (cloud.tencent.com.cn/developer/article/2433927)
+    - section "使用示例": the method computes softmax(Q @ K^T * softmax_scale) @ V
+      exactly (the title says "准确", exact).
+    - section "参数说明": softmax_scale defaults to 1/sqrt(headdim); window_size
+      (left, right), (-1, -1) = no window; alibi_slopes fp32 (nheads,) add
+      -slope * |i - j| to the score of query i and key j.
+    - section "算法 / 前向传播": the forward also writes the row-wise
+      logsumexp L, which the backward uses.
+    - section "2.1：更改causal标志的行为": when seqlen_q != seqlen_k the causal
+      mask is aligned to the bottom-right corner of the score matrix (2x5 example).
+      A mask row with no kept entry gives a zero output row.
+    - section "2.2：针对推理进行优化": for very short queries the keys are split
+      across thread blocks and a separate kernel merges the partial results.
+    - section "2.3：局部（即滑动窗口）注意力": sliding-window local attention.
+
+Readings where the pages are silent (each one is a documented convention,
+shared with the GPU library by specification only):
+  * window bounds are inclusive, measured from the bottom-right-aligned key
+    position c_i = i + seqlen_k - seqlen_q of query i: key j is visible iff
+    (left < 0 or j >= c_i - left) and (right < 0 or j <= c_i + right);
+    causal forces right = 0 (causal wins over a positive right window);
+  * ALiBi uses the same aligned position, bias = -slope * |c_i - j|, and is
+    added after the scores are multiplied by softmax_scale;
+  * an empty row gives out = 0 and lse = -inf (log of an empty sum);
+  * lse is the natural logarithm of sum_j exp(scale * q_i.k_j + bias_ij);
+  * split s of num_splits covers keys [s*C, min(Sk, (s+1)*C)), C = ceil(Sk / num_splits),
+    and its partial output is normalised within the split.
+
+Every array here is float64; bf16 inputs are widened exactly before use.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact widening of a torch/numpy array (bf16, fp16, fp32, fp64) to float64."""
+    if hasattr(x, "detach"):  # torch tensor: widen inside torch, bf16 -> fp64 is exact
+        import torch  # local import: the oracle itself is NumPy
+
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def aligned_key_position(i, seqlen_q: int, seqlen_k: int):
+    """Bottom-right alignment [FA-overview §2.1]: query i sits at key position i + Sk - Sq."""
+    return i + (seqlen_k - seqlen_q)
+
+
+def visible_mask(seqlen_q: int, seqlen_k: int, causal: bool, window_left: int = -1,
+                 window_right: int = -1, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), Sk]: True where query i may attend to key j.
+
+    [FA-overview §2.1] bottom-right causal alignment; [§参数说明, §2.3] window
+    (left, right) with -1 meaning unbounded on that side.  Causal sets the right
+    side to 0.
+    """
+    if rows is None:
+        rows = np.arange(seqlen_q)
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(seqlen_k, dtype=np.int64)[None, :]
+    c = aligned_key_position(i, seqlen_q, seqlen_k)
+    right = 0 if causal else window_right
+    keep = np.ones((i.shape[0], seqlen_k), dtype=bool)
+    if window_left >= 0:
+        keep &= j >= c - window_left
+    if right >= 0:
+        keep &= j <= c + right
+    return keep
+
+
+def alibi_bias(slope: float, seqlen_q: int, seqlen_k: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """[len(rows), Sk] bias -slope * |c_i - j| [FA-overview §参数说明 (alibi_slopes), §2.4]."""
+    if rows is None:
+        rows = np.arange(seqlen_q)
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(seqlen_k, dtype=np.int64)[None, :]
+    c = aligned_key_position(i, seqlen_q, seqlen_k)
+    return -float(slope) * np.abs(c - j).astype(np.float64)
+
+
+def softmax_rows(scores: np.ndarray, keep: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Full-row softmax over the kept entries of each row.
+
+    Returns (P, lse): P[r, j] = exp(s_rj - m_r) / l_r on kept entries and 0
+    elsewhere, lse_r = m_r + ln l_r with m_r the row max over kept entries.
+    A row with no kept entry has P = 0 and lse = -inf [FA-overview §2.1].
+    """
+    s = np.where(keep, scores, -np.inf)
+    m = s.max(axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.where(keep, np.exp(s - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    p = np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, l)[:, None])
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return p, lse
+
+
+def head_rows(q_rows: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, rows: np.ndarray,
+              seqlen_q: int, softmax_scale: float, causal: bool, window_left: int,
+              window_right: int, slope: Optional[float],
+              key_range: Optional[Tuple[int, int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention for some query rows of one (batch, head).
+
+    q_rows [R, D] (the rows listed in ``rows``), k_head/v_head [Sk, D], all fp64.
+    s_ij = softmax_scale * q_i . k_j + bias_ij [FA-overview §使用示例, §参数说明];
+    out_i = sum_j P_ij v_j; lse_i = ln sum_j exp(s_ij).  ``key_range`` = (lo, hi)
+    further restricts the visible keys to lo <= j < hi (one split of the keys).
+    """
+    seqlen_k = k_head.shape[0]
+    keep = visible_mask(seqlen_q, seqlen_k, causal, window_left, window_right, rows)
+    if key_range is not None:
+        lo, hi = key_range
+        j = np.arange(seqlen_k)
+        keep &= ((j >= lo) & (j < hi))[None, :]
+    scores = softmax_scale * (q_rows @ k_head.T)
+    if slope is not None:
+        scores = scores + alibi_bias(slope, seqlen_q, seqlen_k, rows)
+    p, lse = softmax_rows(scores, keep)
+    return p @ v_head, lse
+
+
+def attention_forward(q, k, v, softmax_scale: float, causal: bool = False, window_left: int = -1,
+                      window_right: int = -1, alibi_slopes=None,
+                      row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+    """Full forward: q [B,Sq,H,D], k/v [B,Sk,H,D] -> out [B,Sq,H,D], lse [B,H,Sq] (fp64).
+
+    Rows are independent, so they are processed in chunks of ``row_chunk``; no
+    arithmetic changes with the chunking.
+    """
+    qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
+    batch, seqlen_q, nheads, headdim = qd.shape
+    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    out = np.zeros((batch, seqlen_q, nheads, headdim))
+    lse = np.zeros((batch, nheads, seqlen_q))
+    for b in range(batch):
+        for h in range(nheads):
+            kh, vh = kd[b, :, h, :], vd[b, :, h, :]
+            slope = None if slopes is None else float(slopes[h])
+            for r0 in range(0, seqlen_q, row_chunk):
+                rows = np.arange(r0, min(seqlen_q, r0 + row_chunk))
+                o, l = head_rows(qd[b, rows, h, :], kh, vh, rows, seqlen_q, softmax_scale, causal,
+                                 window_left, window_right, slope)
+                out[b, rows, h, :] = o
+                lse[b, h, rows] = l
+    return out, lse
+
+
+def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_scale: float,
+                      causal: bool = False, window_left: int = -1, window_right: int = -1,
+                      alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Oracle for a list of (b, h, i) output rows only: out [n, D], lse [n].
+
+    Same definition as attention_forward, evaluated for the sampled rows; used
+    where the full problem is too large for the CPU.  Each (b, h) slice of K/V
+    is widened to fp64 once.
+    """
+    samples = list(samples)
+    seqlen_q, headdim = q.shape[1], q.shape[3]
+    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    out = np.zeros((len(samples), headdim))
+    lse = np.zeros(len(samples))
+    groups = {}
+    for n, (b, h, i) in enumerate(samples):
+        groups.setdefault((b, h), []).append((n, i))
+    for (b, h), items in groups.items():
+        kh, vh = as_f64(k[b, :, h, :]), as_f64(v[b, :, h, :])
+        rows = np.array([i for _, i in items], dtype=np.int64)
+        qr = as_f64(q[b, :, h, :])[rows]
+        slope = None if slopes is None else float(slopes[h])
+        o, l = head_rows(qr, kh, vh, rows, seqlen_q, softmax_scale, causal, window_left, window_right, slope)
+        for r, (n, _) in enumerate(items):
+            out[n] = o[r]
+            lse[n] = l[r]
+    return out, lse
+
+
+def split_bounds(seqlen_k: int, num_splits: int) -> Sequence[Tuple[int, int]]:
+    """Key range of each split: [s*C, min(Sk, (s+1)*C)), C = ceil(Sk / num_splits)."""
+    chunk = -(-seqlen_k // num_splits)
+    return [(min(seqlen_k, s * chunk), min(seqlen_k, (s + 1) * chunk)) for s in range(num_splits)]
+
+
+def splitkv_partials(q, k, v, softmax_scale: float, num_splits: int, causal: bool = False,
+                     window_left: int = -1, window_right: int = -1,
+                     alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-split partial results [FA-overview §2.2]: each split attends only to its own keys.
+
+    Returns out_partial [S,B,H,Sq,D] (normalised within the split) and
+    lse_partial [S,B,H,Sq]; a split with no visible key gives 0 and -inf.
+    """
+    qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
+    batch, seqlen_q, nheads, headdim = qd.shape
+    seqlen_k = kd.shape[1]
+    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    out_p = np.zeros((num_splits, batch, nheads, seqlen_q, headdim))
+    lse_p = np.zeros((num_splits, batch, nheads, seqlen_q))
+    rows = np.arange(seqlen_q)
+    for s, key_range in enumerate(split_bounds(seqlen_k, num_splits)):
+        for b in range(batch):
+            for h in range(nheads):
+                slope = None if slopes is None else float(slopes[h])
+                o, l = head_rows(qd[b, :, h, :], kd[b, :, h, :], vd[b, :, h, :], rows, seqlen_q,
+                                 softmax_scale, causal, window_left, window_right, slope, key_range)
+                out_p[s, b, h] = o
+                lse_p[s, b, h] = l
+    return out_p, lse_p
+
+
+def combine(out_partial, lse_partial) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge split results [FA-overview §2.2].
+
+    With L = ln sum_s exp(lse_s): out = sum_s exp(lse_s - L) * out_s, lse = L.
+    If every split is empty (all lse_s = -inf) the row gives out = 0, lse = -inf.
+    Input out_partial [S,B,H,Sq,D], lse_partial [S,B,H,Sq]; returns
+    out [B,Sq,H,D] and lse [B,H,Sq].
+    """
+    op = as_f64(out_partial)
+    lp = as_f64(lse_partial)
+    m = lp.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lp - m_safe[None])  # exp(-inf) = 0 for empty splits
+    total = w.sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, total)))
+    wn = np.where(empty[None], 0.0, w / np.where(empty, 1.0, total)[None])
+    out = (wn[..., None] * op).sum(axis=0)  # [B,H,Sq,D]
+    return out.transpose(0, 2, 1, 3).copy(), lse
+
+
+def brute_force(q, k, v, softmax_scale: float, causal: bool = False, window_left: int = -1,
+                window_right: int = -1, alibi_slopes=None):
+    """Scalar pure-Python loops (math.exp, math.fsum) for tiny shapes.
+
+    Written independently of the NumPy path above: the visibility test and the
+    bias are spelled out per (i, j) from the same stated conventions.
+    """
+    qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
+    batch, seqlen_q, nheads, headdim = qd.shape
+    seqlen_k = kd.shape[1]
+    slopes = None if alibi_slopes is None else [float(s) for s in as_f64(alibi_slopes).reshape(-1)]
+    out = [[[[0.0] * headdim for _ in range(nheads)] for _ in range(seqlen_q)] for _ in range(batch)]
+    lse = [[[0.0] * seqlen_q for _ in range(nheads)] for _ in range(batch)]
+    for b in range(batch):
+        for h in range(nheads):
+            for i in range(seqlen_q):
+                pos = i + seqlen_k - seqlen_q
+                scores = {}
+                for j in range(seqlen_k):
+                    if window_left >= 0 and j < pos - window_left:
+                        continue
+                    if causal and j > pos:
+                        continue
+                    if (not causal) and window_right >= 0 and j > pos + window_right:
+                        continue
+                    dot = math.fsum(qd[b, i, h, d] * kd[b, j, h, d] for d in range(headdim))
+                    s = softmax_scale * dot
+                    if slopes is not None:
+                        s -= slopes[h] * abs(pos - j)
+                    scores[j] = s
+                if not scores:
+                    lse[b][h][i] = -math.inf
+                    continue
+                mx = max(scores.values())
+                weights = {j: math.exp(s - mx) for j, s in scores.items()}
+                total = math.fsum(weights.values())
+                lse[b][h][i] = mx + math.log(total)
+                for d in range(headdim):
+                    out[b][i][h][d] = math.fsum(w * vd[b, j, h, d] for j, w in weights.items()) / total
+    return np.array(out), np.array(lse)

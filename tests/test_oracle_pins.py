@@ -1,0 +1,440 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula.  Each pin is an independent
+fact: a mask the page prints, a closed form, a special case that reduces to a
+library routine, brute force with scalar loops, or an invariant.  The mutation
+tests at the bottom plant plausible mistakes in the oracle (on the CPU) and
+check that some pin catches each one.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oa
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_mask(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return np.array(rows, dtype=bool)
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------- pins
+
+
+def pin_causal_2x5():
+    """The page's printed v2.1 example (bottom-right) and not the v2.0 one (top-left)."""
+    m = oracle.visible_mask(2, 5, causal=True)
+    assert np.array_equal(m, load_mask("causal_mask_sq2_sk5_v21.txt"))
+    assert not np.array_equal(m, load_mask("causal_mask_sq2_sk5_v20.txt"))
+
+
+def pin_causal_5x2_zero_rows():
+    """5x2 causal (reading of the lost example) and zero output for the empty rows."""
+    m = oracle.visible_mask(5, 2, causal=True)
+    assert np.array_equal(m, load_mask("causal_mask_sq5_sk2_v21.txt"))
+    q, k, v = rand((1, 5, 1, 4), 1), rand((1, 2, 1, 4), 2), rand((1, 2, 1, 4), 3)
+    out, lse = oracle.attention_forward(q, k, v, 0.5, causal=True)
+    assert np.all(out[0, :3] == 0.0)
+    assert np.all(np.isneginf(lse[0, 0, :3]))
+    # row 3 sees only key 0: out = v_0 exactly, lse = its score
+    assert np.allclose(out[0, 3, 0], v[0, 0, 0], atol=1e-15)
+    assert abs(lse[0, 0, 3] - 0.5 * float(q[0, 3, 0] @ k[0, 0, 0])) < 1e-14
+    assert np.all(np.isfinite(lse[0, 0, 3:]))
+
+
+def pin_rows_sum_to_one(causal, wl, wr, slopes):
+    """V = identity makes out = P itself: rows are a probability distribution on the visible set."""
+    sq, sk = 7, 11
+    q, k = rand((1, sq, 1, 5), 4), rand((1, sk, 1, 5), 5)
+    v = np.eye(sk).reshape(1, sk, 1, sk)
+    q5 = np.concatenate([q, np.zeros((1, sq, 1, sk - 5))], axis=3)
+    k5 = np.concatenate([k, np.zeros((1, sk, 1, sk - 5))], axis=3)
+    p, _ = oracle.attention_forward(q5, k5, v, 0.7, causal, wl, wr, slopes)
+    p = p[0, :, 0, :]
+    keep = oracle.visible_mask(sq, sk, causal, wl, wr)
+    nonempty = keep.any(axis=1)
+    assert np.all(p >= 0)
+    assert np.all(p[~keep] == 0)
+    assert np.allclose(p[nonempty].sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(p[~nonempty] == 0)
+
+
+def pin_constant_v():
+    """v_j = c for all j gives out_i = c on every non-empty row."""
+    q, k = rand((2, 9, 3, 8), 6), rand((2, 13, 3, 8), 7)
+    c = rand((8,), 8)
+    v = np.broadcast_to(c, (2, 13, 3, 8)).copy()
+    for causal, wl, wr in [(False, -1, -1), (True, -1, -1), (False, 2, 1), (True, 3, 0)]:
+        out, lse = oracle.attention_forward(q, k, v, 0.3, causal, wl, wr, np.array([0.5, 0.25, 0.125]))
+        keep = oracle.visible_mask(9, 13, causal, wl, wr)
+        ne = keep.any(axis=1)
+        assert np.allclose(out[:, ne], c, atol=1e-13)
+
+
+def pin_scale_zero():
+    """scale 0, no ALiBi: uniform weights, out = mean of visible v, lse = ln |V_i|."""
+    sq = sk = 40
+    q, k, v = rand((1, sq, 2, 4), 9), rand((1, sk, 2, 4), 10), rand((1, sk, 2, 4), 11)
+    out, lse = oracle.attention_forward(q, k, v, 0.0, causal=True, window_left=10, window_right=0)
+    for i in range(sq):
+        lo = max(0, i - 10)
+        assert abs(lse[0, 0, i] - math.log(min(i, 10) + 1)) < 1e-13
+        assert np.allclose(out[0, i], v[0, lo:i + 1].mean(axis=0), atol=1e-14)
+
+
+def pin_window_zero():
+    """window (0, 0): only key c_i is visible, out_i = v_{c_i}, lse_i = s_{i, c_i}."""
+    sq, sk = 6, 10
+    q, k, v = rand((1, sq, 1, 8), 12), rand((1, sk, 1, 8), 13), rand((1, sk, 1, 8), 14)
+    out, lse = oracle.attention_forward(q, k, v, 0.9, False, 0, 0)
+    for i in range(sq):
+        c = i + sk - sq
+        assert np.array_equal(out[0, i, 0], v[0, c, 0])
+        assert abs(lse[0, 0, i] - 0.9 * float(q[0, i, 0] @ k[0, c, 0])) < 1e-14
+
+
+def pin_alibi_closed_form():
+    """Q = 0 leaves only the ALiBi bias; lse is a geometric sum in r = e^-slope.
+
+    Non-causal square: lse_i = ln[(1 - r^(i+1))/(1 - r) + r (1 - r^(S-1-i))/(1 - r)].
+    Causal + window (wl, 0): lse_i = ln[(1 - r^(m+1))/(1 - r)] with m = min(i, wl).
+    With Q = 0 the weights are r^|i-j| / Z, so out_i = sum_j r^|i-j| v_j / Z as well.
+    """
+    s, slope = 12, 0.37
+    r = math.exp(-slope)
+    q = np.zeros((1, s, 1, 4))
+    k, v = rand((1, s, 1, 4), 15), rand((1, s, 1, 4), 16)
+    # softmax_scale 0.5 multiplies Q.K^T only; the bias is added after scaling
+    out, lse = oracle.attention_forward(q, k, v, 0.5, alibi_slopes=np.array([slope]))
+    for i in range(s):
+        z = (1 - r ** (i + 1)) / (1 - r) + r * (1 - r ** (s - 1 - i)) / (1 - r)
+        assert abs(lse[0, 0, i] - math.log(z)) < 1e-13
+        w = np.array([r ** abs(i - j) for j in range(s)]) / z
+        assert np.allclose(out[0, i, 0], w @ v[0, :, 0], atol=1e-13)
+    wl = 4
+    out, lse = oracle.attention_forward(q, k, v, 0.5, causal=True, window_left=wl, window_right=0,
+                                        alibi_slopes=np.array([slope]))
+    for i in range(s):
+        m = min(i, wl)
+        assert abs(lse[0, 0, i] - math.log((1 - r ** (m + 1)) / (1 - r))) < 1e-13
+    # Sq != Sk: the bias is measured from the bottom-right aligned position
+    q2 = np.zeros((1, 3, 1, 4))
+    _, lse2 = oracle.attention_forward(q2, k, v, 0.5, causal=True, alibi_slopes=np.array([slope]))
+    for i in range(3):
+        c = i + s - 3
+        assert abs(lse2[0, 0, i] - math.log((1 - r ** (c + 1)) / (1 - r))) < 1e-13
+
+
+def pin_sdpa_library():
+    """Square, no window, no ALiBi: torch's scaled_dot_product_attention in fp64 on the CPU."""
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    for causal in (False, True):
+        q, k, v = rand((2, 33, 3, 16), 17), rand((2, 33, 3, 16), 18), rand((2, 33, 3, 16), 19)
+        out, _ = oracle.attention_forward(q, k, v, 0.21, causal)
+        tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+        ref = sdpa(tq, tk, tv, is_causal=causal, scale=0.21).permute(0, 2, 1, 3).numpy()
+        assert np.allclose(out, ref, atol=1e-12, rtol=0)
+    # Sq != Sk causal: bottom-right mask spelled as torch.tril with diagonal offset Sk - Sq
+    sq, sk = 9, 21
+    q, k, v = rand((1, sq, 2, 8), 20), rand((1, sk, 2, 8), 21), rand((1, sk, 2, 8), 22)
+    out, _ = oracle.attention_forward(q, k, v, 0.4, causal=True)
+    mask = torch.ones(sq, sk, dtype=torch.bool).tril(diagonal=sk - sq)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    ref = sdpa(tq, tk, tv, attn_mask=mask, scale=0.4).permute(0, 2, 1, 3).numpy()
+    assert np.allclose(out, ref, atol=1e-12, rtol=0)
+
+
+BRUTE_CASES = [
+    # (sq, sk, d, causal, wl, wr, alibi)
+    (4, 4, 3, False, -1, -1, False),
+    (4, 4, 3, True, -1, -1, False),
+    (3, 7, 4, True, -1, -1, True),
+    (7, 3, 4, True, -1, -1, False),
+    (6, 8, 2, False, 2, 1, False),
+    (8, 6, 5, False, 1, 3, True),
+    (9, 9, 8, True, 3, -1, True),
+    (5, 9, 3, False, -1, 0, False),
+    (9, 5, 3, False, 0, -1, True),
+    (1, 9, 8, True, -1, -1, True),
+    (2, 5, 3, True, 2, 7, False),
+]
+
+
+def pin_brute_force(case):
+    sq, sk, d, causal, wl, wr, alibi = case
+    q, k, v = rand((2, sq, 2, d), 23), rand((2, sk, 2, d), 24), rand((2, sk, 2, d), 25)
+    slopes = np.array([0.3, 0.05]) if alibi else None
+    out, lse = oracle.attention_forward(q, k, v, 0.6, causal, wl, wr, slopes)
+    bout, blse = oracle.brute_force(q, k, v, 0.6, causal, wl, wr, slopes)
+    fin = np.isfinite(blse)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(blse))
+    assert np.allclose(lse[fin], blse[fin], atol=1e-12, rtol=0)
+    assert np.allclose(out, bout, atol=1e-12, rtol=0)
+
+
+def pin_invariants():
+    q, k, v = rand((1, 10, 2, 6), 26), rand((1, 14, 2, 6), 27), rand((1, 14, 2, 6), 28)
+    base, base_lse = oracle.attention_forward(q, k, v, 0.5)
+    # joint permutation of keys and values (non-causal, no window, no ALiBi)
+    perm = np.random.default_rng(29).permutation(14)
+    o2, l2 = oracle.attention_forward(q, k[:, perm], v[:, perm], 0.5)
+    assert np.allclose(o2, base, atol=1e-13) and np.allclose(l2, base_lse, atol=1e-13)
+    # max_j s_ij <= lse_i <= max_j s_ij + ln |V_i|
+    s = 0.5 * np.einsum("bihd,bjhd->bhij", q, k)
+    assert np.all(base_lse >= s.max(-1) - 1e-13)
+    assert np.all(base_lse <= s.max(-1) + math.log(14) + 1e-13)
+    # window equivalences
+    for wl, wr in [(-1, -1), (14, 14), (100, -1)]:
+        o, l = oracle.attention_forward(q, k, v, 0.5, False, wl, wr)
+        assert np.allclose(o, base, atol=1e-14) and np.allclose(l, base_lse, atol=1e-14)
+    oc, lc = oracle.attention_forward(q, k, v, 0.5, causal=True)
+    ow, lw = oracle.attention_forward(q, k, v, 0.5, False, -1, 0)
+    assert np.array_equal(oc, ow) and np.array_equal(lc, lw)
+    # causal wins over a positive right window
+    o3, l3 = oracle.attention_forward(q, k, v, 0.5, True, -1, 5)
+    assert np.array_equal(o3, oc) and np.array_equal(l3, lc)
+    # masked keys do not matter, however large their scores would be
+    keep = oracle.visible_mask(10, 14, True, 3, 0)
+    o5, l5 = oracle.attention_forward(q, k, v, 0.5, True, 3, 0)
+    for i in (0, 4, 9):
+        kb, vb = k.copy(), v.copy()
+        kb[:, ~keep[i]] = 900.0 * np.sign(q[:, i:i + 1])
+        vb[:, ~keep[i]] = 1e6
+        o6, l6 = oracle.attention_forward(q, kb, vb, 0.5, True, 3, 0)
+        assert np.allclose(o5[:, i], o6[:, i], atol=1e-13)
+        assert np.allclose(l5[:, :, i], l6[:, :, i], atol=1e-13)
+    # zero slope is no ALiBi
+    o4, l4 = oracle.attention_forward(q, k, v, 0.5, alibi_slopes=np.zeros(2))
+    assert np.allclose(o4, base, atol=1e-15) and np.allclose(l4, base_lse, atol=1e-15)
+
+
+def pin_split_combine():
+    """Merging per-split results reproduces the full row, for any partition of the keys."""
+    q, k, v = rand((2, 5, 2, 4), 30), rand((2, 23, 2, 4), 31), rand((2, 23, 2, 4), 32)
+    for causal, wl, wr, alibi in [(False, -1, -1, None), (True, -1, -1, np.array([0.2, 0.1])),
+                                  (True, 6, 0, None), (False, 3, 2, np.array([0.4, 0.0]))]:
+        full, full_lse = oracle.attention_forward(q, k, v, 0.8, causal, wl, wr, alibi)
+        for ns in (1, 2, 3, 5, 8, 23):
+            op, lp = oracle.splitkv_partials(q, k, v, 0.8, ns, causal, wl, wr, alibi)
+            out, lse = oracle.combine(op, lp)
+            assert np.allclose(out, full, atol=1e-13)
+            fin = np.isfinite(full_lse)
+            assert np.array_equal(np.isneginf(lse), np.isneginf(full_lse))
+            assert np.allclose(lse[fin], full_lse[fin], atol=1e-13)
+    # one key per split: each partial is that key's value and score, or empty
+    op, lp = oracle.splitkv_partials(q, k, v, 0.8, 23, causal=True)
+    for s in range(23):
+        for i in range(5):
+            c = i + 23 - 5
+            if s <= c:
+                assert np.array_equal(op[s, :, :, i], v[:, s])
+                assert np.allclose(lp[s, :, :, i], 0.8 * np.einsum("bhd,bhd->bh", q[:, i], k[:, s]), atol=1e-14)
+            else:
+                assert np.all(op[s, :, :, i] == 0) and np.all(np.isneginf(lp[s, :, :, i]))
+    # every split empty: out 0, lse -inf
+    out, lse = oracle.combine(np.ones((3, 1, 1, 2, 4)), np.full((3, 1, 1, 2), -np.inf))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # split bounds cover the keys once, in order, including a ragged last split
+    assert oracle.split_bounds(10, 4) == [(0, 3), (3, 6), (6, 9), (9, 10)]
+    assert oracle.split_bounds(9, 4) == [(0, 3), (3, 6), (6, 9), (9, 9)]
+
+
+def pin_sampled_rows():
+    """The sampled-row entry point agrees with the full forward row for row."""
+    q, k, v = rand((2, 12, 3, 8), 33), rand((2, 17, 3, 8), 34), rand((2, 17, 3, 8), 35)
+    slopes = np.array([0.5, 0.1, 0.02])
+    full, full_lse = oracle.attention_forward(q, k, v, 0.3, True, 4, 0, slopes)
+    samples = [(0, 0, 0), (1, 2, 11), (0, 1, 5), (1, 0, 3)]
+    o, l = oracle.attention_sampled(q, k, v, samples, 0.3, True, 4, 0, slopes)
+    for n, (b, h, i) in enumerate(samples):
+        assert np.allclose(o[n], full[b, i, h], atol=1e-14) and abs(l[n] - full_lse[b, h, i]) < 1e-14
+
+
+def pin_bf16_widening():
+    """bf16 inputs widen exactly: the oracle sees the very values the GPU gets."""
+    t = torch.tensor([1.0, -2.5, 3.140625, 1e-3, 65280.0]).to(torch.bfloat16)
+    w = oracle.as_f64(t)
+    bits = t.view(torch.int16).numpy().astype(np.uint16).astype(np.uint32) << 16
+    assert np.array_equal(w, bits.view(np.float32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------- tests
+
+
+def test_causal_2x5_page_example():
+    pin_causal_2x5()
+
+
+def test_causal_5x2_zero_rows():
+    pin_causal_5x2_zero_rows()
+
+
+@pytest.mark.parametrize("causal,wl,wr,slopes", [
+    (False, -1, -1, None), (True, -1, -1, None), (False, 2, 3, None), (True, 4, 0, np.array([0.3])),
+    (False, -1, 1, np.array([1.5])),
+])
+def test_rows_sum_to_one(causal, wl, wr, slopes):
+    pin_rows_sum_to_one(causal, wl, wr, slopes)
+
+
+def test_constant_v():
+    pin_constant_v()
+
+
+def test_scale_zero():
+    pin_scale_zero()
+
+
+def test_window_zero():
+    pin_window_zero()
+
+
+def test_alibi_closed_form():
+    pin_alibi_closed_form()
+
+
+def test_sdpa_library():
+    pin_sdpa_library()
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_brute_force(case):
+    pin_brute_force(case)
+
+
+def test_invariants():
+    pin_invariants()
+
+
+def test_split_combine():
+    pin_split_combine()
+
+
+def test_sampled_rows():
+    pin_sampled_rows()
+
+
+def test_bf16_widening():
+    pin_bf16_widening()
+
+
+# --------------------------------------------------------------------------- planted mistakes
+
+
+def _all_pins():
+    pin_causal_2x5()
+    pin_causal_5x2_zero_rows()
+    pin_rows_sum_to_one(True, 4, 0, np.array([0.3]))
+    pin_constant_v()
+    pin_scale_zero()
+    pin_window_zero()
+    pin_alibi_closed_form()
+    pin_sdpa_library()
+    for case in BRUTE_CASES:
+        pin_brute_force(case)
+    pin_invariants()
+    pin_split_combine()
+
+
+def _top_left(i, seqlen_q, seqlen_k):
+    return i
+
+
+def _alibi_wrong_sign(slope, seqlen_q, seqlen_k, rows=None):
+    return -_ORIG_ALIBI(slope, seqlen_q, seqlen_k, rows)
+
+
+def _softmax_log2_lse(scores, keep):
+    p, lse = _ORIG_SOFTMAX(scores, keep)
+    return p, lse / math.log(2)
+
+
+def _softmax_unmasked_max(scores, keep):
+    # max taken over all keys, masked ones included: a plausible slip
+    s = np.where(keep, scores, -np.inf)
+    m = scores.max(axis=1)
+    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
+    l = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.nan_to_num(e / l[:, None])
+        lse = np.where(l > 0, m + np.log(l), -np.inf)
+    return p, lse
+
+
+def _visible_exclusive_window(seqlen_q, seqlen_k, causal, window_left=-1, window_right=-1, rows=None):
+    keep = _ORIG_VISIBLE(seqlen_q, seqlen_k, causal, window_left, window_right, rows)
+    if window_left >= 0:
+        i = np.arange(seqlen_q) if rows is None else np.asarray(rows)
+        c = i + seqlen_k - seqlen_q
+        j = np.arange(seqlen_k)
+        keep &= ~(j[None, :] == (c - window_left)[:, None])
+    return keep
+
+
+def _combine_no_weights(out_partial, lse_partial):
+    out, lse = _ORIG_COMBINE(out_partial, lse_partial)
+    op = oa.as_f64(out_partial)
+    return op.mean(axis=0).transpose(0, 2, 1, 3), lse
+
+
+def _head_rows_bias_scaled(q_rows, k_head, v_head, rows, seqlen_q, softmax_scale, causal, window_left,
+                           window_right, slope, key_range=None):
+    # bias added before the scale instead of after it
+    seqlen_k = k_head.shape[0]
+    keep = oa.visible_mask(seqlen_q, seqlen_k, causal, window_left, window_right, rows)
+    if key_range is not None:
+        j = np.arange(seqlen_k)
+        keep &= ((j >= key_range[0]) & (j < key_range[1]))[None, :]
+    raw = q_rows @ k_head.T
+    if slope is not None:
+        raw = raw + oa.alibi_bias(slope, seqlen_q, seqlen_k, rows)
+    p, lse = oa.softmax_rows(softmax_scale * raw, keep)
+    return p @ v_head, lse
+
+
+def _head_rows_k_for_v(q_rows, k_head, v_head, *args, **kwargs):
+    # operands mixed up: keys used as values
+    return _ORIG_HEAD_ROWS(q_rows, k_head, k_head, *args, **kwargs)
+
+
+_ORIG_HEAD_ROWS = oa.head_rows
+_ORIG_ALIBI = oa.alibi_bias
+_ORIG_SOFTMAX = oa.softmax_rows
+_ORIG_VISIBLE = oa.visible_mask
+_ORIG_COMBINE = oa.combine
+
+
+@pytest.mark.parametrize("target,replacement", [
+    ("aligned_key_position", _top_left),
+    ("alibi_bias", _alibi_wrong_sign),
+    ("softmax_rows", _softmax_log2_lse),
+    ("softmax_rows", _softmax_unmasked_max),
+    ("visible_mask", _visible_exclusive_window),
+    ("combine", _combine_no_weights),
+    ("head_rows", _head_rows_bias_scaled),
+    ("head_rows", _head_rows_k_for_v),
+])
+def test_planted_mistake_is_caught(monkeypatch, target, replacement):
+    """Each planted oracle mistake must make at least one pin fail."""
+    _all_pins()  # unmodified oracle passes
+    monkeypatch.setattr(oa, target, replacement)
+    monkeypatch.setattr(oracle, target, replacement, raising=False)
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            _all_pins()
