@@ -1,0 +1,176 @@
+"""MI355X (gfx950) exact-attention forward: thin Python binding over libfa_mi355x.so.
+
+The binding only marshals arguments: it checks dtypes, devices, shapes and
+contiguity, allocates outputs with torch when asked to, and passes raw device
+pointers and torch's current HIP stream to the C ABI declared in include/fa.h.
+Every step of the computation runs in the library's HIP kernels; there is no
+other implementation to fall back to.  A missing library raises at the first call.
+
+Functions
+  flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
+                  alibi_slopes=None) -> (out, lse)
+  fwd(q, k, v, out, lse, ...)                      preallocated outputs
+  fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, ...)
+  combine(out_partial, lse_partial, out, lse)
+  decode(q, k_cache, v_cache, num_splits=16, ...) -> (out, lse)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB = None
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
+
+FA_OK = 0
+
+
+class FAError(RuntimeError):
+    """A non-zero status returned by the C library."""
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa_mi355x.so (built in-tree) and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m exact_attention_56_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa_combine.restype = i
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        msg = load_library().fa_status_str(status).decode()
+        raise FAError(f"libfa_mi355x returned {status}: {msg}")
+
+
+def _stream_handle(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qkv(q, k, v):
+    _require(q, "q", torch.bfloat16, 4)
+    _require(k, "k", torch.bfloat16, 4, q.device)
+    _require(v, "v", torch.bfloat16, 4, q.device)
+    b, sq, h, d = q.shape
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
+    if k.shape[0] != b or k.shape[2] != h or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return b, sq, k.shape[1], h, d
+
+
+def _alibi(alibi_slopes, nheads, device):
+    if alibi_slopes is None:
+        return None
+    _require(alibi_slopes, "alibi_slopes", torch.float32, 1, device)
+    if alibi_slopes.shape[0] != nheads:
+        raise ValueError(f"alibi_slopes must have shape ({nheads},)")
+    return alibi_slopes
+
+
+def _scale(softmax_scale, headdim) -> float:
+    return 1.0 / math.sqrt(headdim) if softmax_scale is None else float(softmax_scale)
+
+
+def fwd(q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
+        alibi_slopes=None) -> None:
+    """fa_fwd on preallocated out [B,Sq,H,D] bf16 and lse [B,H,Sq] fp32."""
+    b, sq, sk, h, d = _check_qkv(q, k, v)
+    _require(out, "out", torch.bfloat16, 4, q.device)
+    _require(lse, "lse", torch.float32, 3, q.device)
+    if out.shape != q.shape or tuple(lse.shape) != (b, h, sq):
+        raise ValueError("out must match q and lse must be [batch, nheads, seqlen_q]")
+    slopes = _alibi(alibi_slopes, h, q.device)
+    _check(load_library().fa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), b, sq, sk, h, d,
+        _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]), int(window_size[1]),
+        _ptr(slopes), _stream_handle(q)))
+
+
+def flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
+                    alibi_slopes=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward; returns (out [B,Sq,H,D] bf16, lse [B,H,Sq] fp32)."""
+    b, sq, sk, h, d = _check_qkv(q, k, v)
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
+    fwd(q, k, v, out, lse, softmax_scale, causal, window_size, alibi_slopes)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, softmax_scale=None, causal=False,
+                window_size=(-1, -1), alibi_slopes=None) -> None:
+    """fa_fwd_splitkv: out_partial [S,B,H,Sq,D] fp32, lse_partial [S,B,H,Sq] fp32."""
+    b, sq, sk, h, d = _check_qkv(q, k, v)
+    _require(out_partial, "out_partial", torch.float32, 5, q.device)
+    _require(lse_partial, "lse_partial", torch.float32, 4, q.device)
+    if tuple(out_partial.shape) != (num_splits, b, h, sq, d) or tuple(lse_partial.shape) != (num_splits, b, h, sq):
+        raise ValueError("partials must be [num_splits, B, H, Sq, D] and [num_splits, B, H, Sq]")
+    slopes = _alibi(alibi_slopes, h, q.device)
+    _check(load_library().fa_fwd_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out_partial.data_ptr(), lse_partial.data_ptr(),
+        b, sq, sk, h, d, _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]),
+        int(window_size[1]), _ptr(slopes), int(num_splits), _stream_handle(q)))
+
+
+def combine(out_partial, lse_partial, out, lse) -> None:
+    """fa_combine: merge [S,B,H,Sq,D] / [S,B,H,Sq] partials into out [B,Sq,H,D] bf16, lse [B,H,Sq]."""
+    _require(out_partial, "out_partial", torch.float32, 5)
+    _require(lse_partial, "lse_partial", torch.float32, 4, out_partial.device)
+    _require(out, "out", torch.bfloat16, 4, out_partial.device)
+    _require(lse, "lse", torch.float32, 3, out_partial.device)
+    s, b, h, sq, d = out_partial.shape
+    if tuple(lse_partial.shape) != (s, b, h, sq) or tuple(out.shape) != (b, sq, h, d) or tuple(lse.shape) != (b, h, sq):
+        raise ValueError("inconsistent shapes for combine")
+    _check(load_library().fa_combine(out_partial.data_ptr(), lse_partial.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), b, sq, h, d, s, _stream_handle(out)))
+
+
+def decode(q, k_cache, v_cache, num_splits=16, softmax_scale=None, causal=False, window_size=(-1, -1),
+           alibi_slopes=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV forward (partials + combine on the current stream); returns (out, lse)."""
+    b, sq, sk, h, d = _check_qkv(q, k_cache, v_cache)
+    op = torch.empty(num_splits, b, h, sq, d, dtype=torch.float32, device=q.device)
+    lp = torch.empty(num_splits, b, h, sq, dtype=torch.float32, device=q.device)
+    fwd_splitkv(q, k_cache, v_cache, op, lp, num_splits, softmax_scale, causal, window_size, alibi_slopes)
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
+    combine(op, lp, out, lse)
+    return out, lse

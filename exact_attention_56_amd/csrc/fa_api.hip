@@ -1,0 +1,158 @@
+// fa_api.hip - the extern "C" entry points declared in include/fa.h.
+//
+// Validates every argument before any HIP call (so an invalid call launches
+// nothing and touches no output), fills the kernel parameter block and launches
+// on the caller's stream.  No allocation, no synchronisation, no global state.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_common.h"
+
+namespace fa {
+hipError_t launch_fwd(const FwdParams& p, int headdim, bool split, hipStream_t stream);
+long fwd_num_blocks(const FwdParams& p, bool split);
+hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream);
+}  // namespace fa
+
+namespace {
+
+constexpr int kMaxSeqlen = 1 << 30;     // keeps every position/window sum inside int32
+constexpr long kMaxBlocks = 0x7fffffffL;  // grid x dimension
+constexpr int kDecodeMaxRows = 8;       // fa_fwd_splitkv: vector-ALU path up to this seqlen_q
+constexpr int kQTile = 128;             // query rows per matrix-core workgroup
+
+bool headdim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Elements of a [a, b, c, d] tensor, or -1 when it does not fit in int64.
+long long elems4(long long a, long long b, long long c, long long d) {
+  long long r = 1;
+  const long long f[4] = {a, b, c, d};
+  for (long long x : f) {
+    if (x <= 0 || r > (long long)INT64_MAX / 2 / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+// Shared validation of fa_fwd / fa_fwd_splitkv.  Fills p on success.
+int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q, int seqlen_k,
+            int nheads, int headdim, float softmax_scale, int causal, int window_left, int window_right,
+            const float* alibi_slopes, fa::FwdParams* p) {
+  if (!q || !k || !v) return FA_ERR_INVALID_ARG;
+  if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || nheads < 1 || headdim < 1) return FA_ERR_INVALID_ARG;
+  if (seqlen_q > kMaxSeqlen || seqlen_k > kMaxSeqlen) return FA_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
+  if (elems4(batch, seqlen_q, nheads, headdim) < 0 || elems4(batch, seqlen_k, nheads, headdim) < 0)
+    return FA_ERR_INVALID_ARG;
+
+  int wl = window_left;
+  int wr = causal ? 0 : window_right;
+  // A side at least as wide as the whole key range is the same as no bound:
+  // c_i - wl < 0 <= j for every row when wl >= Sk, and c_i + wr >= Sk - 1 >= j
+  // for every row when wr >= Sq.
+  if (wl >= seqlen_k) wl = -1;
+  if (wr >= seqlen_q) wr = -1;
+
+  p->q = (const uint16_t*)q;
+  p->k = (const uint16_t*)k;
+  p->v = (const uint16_t*)v;
+  p->alibi = alibi_slopes;
+  p->batch = batch;
+  p->seqlen_q = seqlen_q;
+  p->seqlen_k = seqlen_k;
+  p->nheads = nheads;
+  p->scale_log2 = fabsf(softmax_scale) * fa::kLog2e;
+  p->q_sign = signbit(softmax_scale) ? 0x80008000u : 0u;
+  p->window_left = wl;
+  p->window_right = wr;
+  p->num_q_tiles = (seqlen_q + kQTile - 1) / kQTile;
+  p->num_splits = 1;
+  p->split_len = seqlen_k;
+  // Causal (or a right window): later query tiles see more keys; start them first.
+  p->reverse_q = (wr >= 0) ? 1 : 0;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen_q,
+           int seqlen_k, int nheads, int headdim, float softmax_scale, int causal, int window_left,
+           int window_right, const float* alibi_slopes, hipStream_t stream) {
+  if (!out || !lse) return FA_ERR_INVALID_ARG;
+  fa::FwdParams p;
+  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, &p);
+  if (st != FA_OK) return st;
+  p.out = out;
+  p.lse = lse;
+  if (fa::fwd_num_blocks(p, false) > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
+  return fa::launch_fwd(p, headdim, false, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_partial, float* lse_partial,
+                   int batch, int seqlen_q, int seqlen_k, int nheads, int headdim, float softmax_scale,
+                   int causal, int window_left, int window_right, const float* alibi_slopes, int num_splits,
+                   hipStream_t stream) {
+  if (!out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
+  fa::FwdParams p;
+  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, &p);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > seqlen_k) return FA_ERR_INVALID_ARG;
+  if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
+  p.out = out_partial;
+  p.lse = lse_partial;
+  p.num_splits = num_splits;
+  p.split_len = (seqlen_k + num_splits - 1) / num_splits;
+  (void)hipGetLastError();
+  hipError_t e;
+  if (seqlen_q <= kDecodeMaxRows) {
+    if ((long)batch * nheads * num_splits * seqlen_q > kMaxBlocks) return FA_ERR_INVALID_ARG;
+    e = fa::launch_decode(p, headdim, stream);
+  } else {
+    if (fa::fwd_num_blocks(p, true) > kMaxBlocks) return FA_ERR_INVALID_ARG;
+    e = fa::launch_fwd(p, headdim, true, stream);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,
+               int seqlen_q, int nheads, int headdim, int num_splits, hipStream_t stream) {
+  if (!out_partial || !lse_partial || !out || !lse) return FA_ERR_INVALID_ARG;
+  if (batch < 1 || seqlen_q < 1 || nheads < 1 || headdim < 1 || num_splits < 1) return FA_ERR_INVALID_ARG;
+  if (seqlen_q > kMaxSeqlen) return FA_ERR_INVALID_ARG;
+  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
+  if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
+  const long rows = (long)batch * nheads * seqlen_q;
+  if ((rows + 3) / 4 > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  fa::CombineParams p;
+  p.out_partial = out_partial;
+  p.lse_partial = lse_partial;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.batch = batch;
+  p.seqlen_q = seqlen_q;
+  p.nheads = nheads;
+  p.num_splits = num_splits;
+  (void)hipGetLastError();
+  return fa::launch_combine(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: headdim must be 64, 128 or 256";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// fa_common.h - device types, parameter blocks and small helpers shared by the
+// gfx950 attention kernels.  Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Forward problem description, filled on the host.  Sizes are in elements.
+struct FwdParams {
+  const uint16_t* q;      // bf16 [B, Sq, H, D]
+  const uint16_t* k;      // bf16 [B, Sk, H, D]
+  const uint16_t* v;      // bf16 [B, Sk, H, D]
+  void* out;              // bf16 [B, Sq, H, D]  or fp32 [S, B, H, Sq, D] (split mode)
+  float* lse;             // fp32 [B, H, Sq]     or fp32 [S, B, H, Sq]    (split mode)
+  const float* alibi;     // fp32 [H] ALiBi slopes, or nullptr
+  int batch, seqlen_q, seqlen_k, nheads;
+  float scale_log2;       // |softmax_scale| * log2(e)
+  uint32_t q_sign;        // 0x80008000 when softmax_scale < 0 (Q is negated on load), else 0
+  int window_left;        // -1 = unbounded
+  int window_right;       // -1 = unbounded; already 0 when causal
+  int num_q_tiles;        // ceil(Sq / 128)
+  int num_splits;         // 1 for the plain forward
+  int split_len;          // keys per split (ceil(Sk / num_splits))
+  int reverse_q;          // 1: visit the heaviest query tiles first (causal)
+};
+
+// Combine description.
+struct CombineParams {
+  const float* out_partial;  // [S, B, H, Sq, D]
+  const float* lse_partial;  // [S, B, H, Sq]
+  uint16_t* out;             // bf16 [B, Sq, H, D]
+  float* lse;                // [B, H, Sq]
+  int batch, seqlen_q, nheads, num_splits;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of x in lane (l ^ 32) combined with x by a symmetric operation: both
+// halves of the wave exchange their values with one v_permlane32_swap.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round two fp32 to bf16 (round-to-nearest-even) and pack them, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// Map a linear workgroup id to a work index so that the workgroups the dispatcher
+// sends to one XCD (ids congruent mod 8) receive one contiguous range of work
+// indices: neighbouring query tiles of one (batch, head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int per = nblocks >> 3;
+  const int rem = nblocks & 7;
+  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace fa

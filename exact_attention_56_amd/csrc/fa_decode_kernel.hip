@@ -1,0 +1,239 @@
+// fa_decode_kernel.hip - split-KV decode partial kernel and the combine kernel (gfx950).
+//
+// Page "FlashAttention：快速且内存高效的准确注意力机制"
+// (cloud.tencent.com.cn/developer/article/2433927), section "2.2：针对推理进行优化":
+// with very short queries the cost is reading the KV cache, so the keys are split
+// across workgroups and a separate kernel merges the per-split results.
+//
+// Partial kernel: one workgroup per (batch, head, split, query row).  A query row
+// against a KV chunk is a matrix-vector product, so it runs on the vector ALUs and
+// is bound by HBM bandwidth: each key row (headdim bf16) is read by HD/8 lanes with
+// one 16-byte load each, the dot product is finished with lane shuffles, and the
+// four waves walk interleaved slices of the chunk with their own online-softmax
+// state, merged through LDS at the end.  The output of a split is normalised
+// within the split, with its logsumexp; an empty split gives 0 and -inf.
+//
+// Combine kernel: out = sum_s exp(lse_s - L) out_s with L = ln sum_s exp(lse_s).
+#include "fa_common.h"
+
+namespace fa {
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_UNROLL = 4;  // key rows per lane per step
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+template <int HD, bool ALIBI>
+__global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) {
+  constexpr int LPR = HD / 8;    // lanes per key row
+  constexpr int RPW = 64 / LPR;  // key rows per wave per load
+  constexpr int STEP = DEC_UNROLL * RPW;
+  __shared__ float sm_m[4], sm_l[4];
+  __shared__ float sm_acc[4][HD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane / LPR;   // row group inside the wave
+  const int cidx = lane % LPR;  // 8-column chunk of the head dimension
+
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int Sq = p.seqlen_q, Sk = p.seqlen_k;
+  const int i = w % Sq;
+  w /= Sq;
+  const int split = w % p.num_splits;
+  w /= p.num_splits;
+  const int h = w % p.nheads;
+  const int b = w / p.nheads;
+
+  const long row_stride = (long)p.nheads * HD;
+  const uint16_t* __restrict__ kbase = p.k + (long)b * Sk * row_stride + (long)h * HD + cidx * 8;
+  const uint16_t* __restrict__ vbase = p.v + (long)b * Sk * row_stride + (long)h * HD + cidx * 8;
+
+  // visible keys of row i inside this split: [lo, hi)
+  const int pos = i + Sk - Sq;
+  int lo = min(Sk, split * p.split_len);
+  int hi = min(Sk, lo + p.split_len);
+  if (p.window_left >= 0) lo = max(lo, pos - p.window_left);
+  if (p.window_right >= 0) hi = min(hi, pos + p.window_right + 1);
+
+  // q chunk, pre-multiplied by softmax_scale * log2(e) (sign included)
+  const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
+  float qv[8];
+  {
+    const u32x4 raw = *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(raw[e]) * c;
+      qv[2 * e + 1] = bf16_hi(raw[e]) * c;
+    }
+  }
+  float slope = 0.f;
+  if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+  for (int base = lo + wave * STEP; base < hi; base += 4 * STEP) {
+    u32x4 kr[DEC_UNROLL], vr[DEC_UNROLL];
+#pragma unroll
+    for (int u = 0; u < DEC_UNROLL; ++u) {
+      const int key = base + u * RPW + g;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      kr[u] = key < hi ? *(const u32x4*)(kbase + (long)key * row_stride) : zero;
+      vr[u] = key < hi ? *(const u32x4*)(vbase + (long)key * row_stride) : zero;
+    }
+    float s[DEC_UNROLL];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < DEC_UNROLL; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(qv[2 * e], bf16_lo(kr[u][e]), part);
+        part = fmaf(qv[2 * e + 1], bf16_hi(kr[u][e]), part);
+      }
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+      const int key = base + u * RPW + g;
+      if constexpr (ALIBI) part -= slope * fabsf((float)(pos - key));
+      s[u] = key < hi ? part : -INFINITY;
+      bmax = fmaxf(bmax, s[u]);
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < DEC_UNROLL; ++u) {
+      const float pu = fast_exp2(s[u] - m_use);
+      l_run += pu;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(pu, bf16_lo(vr[u][e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(pu, bf16_hi(vr[u][e]), acc[2 * e + 1]);
+      }
+    }
+    m_run = m_new;
+  }
+
+  // merge the row groups of this wave (same m_run across the wave)
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+    l_run += __shfl_xor(l_run, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (lane == 0) {
+    sm_m[wave] = m_run;
+    sm_l[wave] = l_run;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_acc[wave][cidx * 8 + e] = acc[e];
+  }
+  __syncthreads();
+
+  // merge the four waves
+  float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float wgt[4], L = 0.f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    wgt[x] = fast_exp2(sm_m[x] - M_use);
+    L += sm_l[x] * wgt[x];
+  }
+  const long rowid = (((long)split * p.batch + b) * p.nheads + h) * Sq + i;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* out = (float*)p.out + rowid * HD;
+  for (int d = tid; d < HD; d += DEC_THREADS) {
+    float o = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) o = fmaf(sm_acc[x][d], wgt[x], o);
+    out[d] = o * inv;
+  }
+  if (tid == 0) p.lse[rowid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int PER_LANE = HD / 64;
+  const int lane = threadIdx.x & 63;
+  const long rows = (long)p.batch * p.nheads * p.seqlen_q;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h)*Sq + i
+  if (row >= rows) return;
+  const int i = (int)(row % p.seqlen_q);
+  const long bh = row / p.seqlen_q;
+  const int h = (int)(bh % p.nheads);
+  const int b = (int)(bh / p.nheads);
+
+  const float* lp = p.lse_partial + row;
+  const float* op = p.out_partial + row * HD;
+  const long lstride = rows, ostride = rows * HD;
+
+  float M = -INFINITY;
+  for (int s = 0; s < p.num_splits; ++s) M = fmaxf(M, lp[s * lstride]);
+
+  float o[PER_LANE];
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) o[e] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.num_splits; ++s) {
+      const float ls = lp[s * lstride];
+      const float wgt = fast_exp2((ls - M) * kLog2e);  // 0 for an empty split
+      L += wgt;
+      if (wgt != 0.f) {
+#pragma unroll
+        for (int e = 0; e < PER_LANE; ++e) o[e] = fmaf(wgt, op[s * ostride + lane + 64 * e], o[e]);
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* out = p.out + (((long)b * p.seqlen_q + i) * p.nheads + h) * HD;
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) {
+    const uint32_t pk = pack_bf16x2(o[e] * inv, 0.f);
+    out[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
+  }
+  if (lane == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+template <int HD>
+static hipError_t launch_decode_hd(const FwdParams& p, hipStream_t stream) {
+  const long nblocks = (long)p.batch * p.nheads * p.num_splits * p.seqlen_q;
+  if (p.alibi)
+    hipLaunchKernelGGL((decode_split_kernel<HD, true>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<HD, false>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream) {
+  switch (headdim) {
+    case 64: return launch_decode_hd<64>(p, stream);
+    case 128: return launch_decode_hd<128>(p, stream);
+    case 256: return launch_decode_hd<256>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream) {
+  const long rows = (long)p.batch * p.nheads * p.seqlen_q;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  switch (headdim) {
+    case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<256>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

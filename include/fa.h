@@ -1,0 +1,125 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library, libfa_mi355x.so.
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     out = softmax(Q K^T * softmax_scale + mask + ALiBi bias) V,
+ * tile by tile with an online softmax, so the seqlen_q x seqlen_k score matrix
+ * never reaches device memory, and writes the row-wise logsumexp as well.
+ * Sources (web pages, cited by title and section):
+ *   [FA-overview] "FlashAttention：快速且内存高效的准确注意力机制"
+ *                 (cloud.tencent.com.cn/developer/article/2433927)
+ *     section "使用示例"       : the computation softmax(Q K^T * softmax_scale) V, exact;
+ *     section "参数说明"       : argument meanings (softmax_scale default 1/sqrt(headdim),
+ *                                window_size (left, right) with -1 = unbounded, fp32
+ *                                alibi_slopes adding -slope * |i - j| to score (i, j));
+ *     section "算法 / 前向传播": unscaled running output, one final division by the
+ *                                row sum, and the row-wise logsumexp L as a second output;
+ *     section "2.1：更改causal标志的行为": causal mask aligned to the bottom-right corner
+ *                                when seqlen_q != seqlen_k; an all-masked row gives zeros;
+ *     section "2.2：针对推理进行优化": for very short queries the KV cache is split over
+ *                                workgroups and a separate kernel merges the results;
+ *     section "2.3：局部（即滑动窗口）注意力": sliding-window local attention.
+ *
+ * Conventions shared by every entry point
+ *   - q, k, v, out: bf16, contiguous [batch, seqlen, nheads, headdim], headdim innermost.
+ *     q and out have seqlen_q rows, k and v have seqlen_k rows, same nheads.
+ *   - lse: fp32, contiguous [batch, nheads, seqlen_q], natural logarithm of
+ *     sum_j exp(softmax_scale * q_i . k_j + bias_ij) over the visible keys.
+ *   - Visibility (bottom-right alignment): query i sits at key position
+ *     c_i = i + seqlen_k - seqlen_q.  Key j is visible iff
+ *         (window_left  < 0 || j >= c_i - window_left) &&
+ *         (window_right < 0 || j <= c_i + window_right),
+ *     bounds inclusive; causal != 0 sets window_right to 0 (causal wins).
+ *   - ALiBi: alibi_slopes is NULL (no bias) or a device fp32 array [nheads];
+ *     bias_ij = -alibi_slopes[h] * |c_i - j|, added after the scaling.
+ *   - A row with no visible key gets out = 0 and lse = -inf.
+ *   - softmax_scale is used exactly as given (any finite value, negative included).
+ *   - headdim must be 64, 128 or 256.
+ *
+ * Ownership and streams
+ *   - All pointers except the return value of fa_status_str are DEVICE pointers owned
+ *     by the caller.  The library allocates nothing, keeps no mutable global state
+ *     (calls from several host threads are safe) and never synchronises.
+ *   - Work is enqueued on `stream` (0 = the default stream); a call returns after
+ *     the enqueue.  Buffers must stay valid until the work has run.
+ *   - Inputs are read only.  Output buffers must not alias the inputs.
+ *
+ * Errors (return value)
+ *   FA_OK (0) on success.  On any error nothing is launched and no output is touched:
+ *   FA_ERR_INVALID_ARG (-1): a NULL required pointer, a size < 1, a window side < -1,
+ *                            num_splits outside [1, seqlen_k], a non-finite softmax_scale,
+ *                            or a problem whose element count overflows 64-bit indexing;
+ *   FA_ERR_UNSUPPORTED (-2): headdim not in {64, 128, 256};
+ *   FA_ERR_LAUNCH      (-3): the HIP runtime reported an error for the launch.
+ *   No exception crosses the ABI and nothing is printed.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1)
+#define FA_ERR_UNSUPPORTED (-2)
+#define FA_ERR_LAUNCH (-3)
+
+/*
+ * fa_fwd - attention forward for a padded batch [FA-overview, "使用示例", "参数说明",
+ * "算法 / 前向传播", "2.1", "2.3"].
+ *   q      [batch, seqlen_q, nheads, headdim] bf16 (device, read)
+ *   k, v   [batch, seqlen_k, nheads, headdim] bf16 (device, read)
+ *   out    [batch, seqlen_q, nheads, headdim] bf16 (device, written)
+ *   lse    [batch, nheads, seqlen_q]          fp32 (device, written)
+ *   causal, window_left, window_right, alibi_slopes: see the conventions above.
+ * One workgroup per (batch, head, block of 128 query rows); every output element
+ * is written exactly once, without atomics, so results are bitwise reproducible.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+           int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
+           float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv - first half of the split-KV forward [FA-overview, "2.2"].
+ * The keys are cut into num_splits contiguous ranges: split s covers
+ * [s*C, min(seqlen_k, (s+1)*C)) with C = ceil(seqlen_k / num_splits).  For each
+ * split it writes the attention restricted to that split's visible keys:
+ *   out_partial [num_splits, batch, nheads, seqlen_q, headdim] fp32 (device, written),
+ *               normalised within the split (0 where the split sees no key);
+ *   lse_partial [num_splits, batch, nheads, seqlen_q] fp32 (device, written),
+ *               -inf where the split sees no key.
+ * The other arguments mean what they mean for fa_fwd.  Follow with fa_combine on
+ * the same stream.  Rows of short queries (seqlen_q <= 8) run on a vector-ALU
+ * kernel that streams the KV cache; longer queries run on the matrix-core kernel.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                   float* out_partial, float* lse_partial,
+                   int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
+                   float softmax_scale, int causal, int window_left, int window_right,
+                   const float* alibi_slopes, int num_splits, hipStream_t stream);
+
+/*
+ * fa_combine - second half of the split-KV forward [FA-overview, "2.2"].
+ * Per row: L = ln sum_s exp(lse_partial[s]); out = sum_s exp(lse_partial[s] - L) *
+ * out_partial[s]; lse = L.  A row where every split is empty gets out = 0, lse = -inf.
+ *   out_partial, lse_partial: as written by fa_fwd_splitkv (device, read)
+ *   out [batch, seqlen_q, nheads, headdim] bf16 (device, written)
+ *   lse [batch, nheads, seqlen_q]          fp32 (device, written)
+ * num_splits must be >= 1 (the partial layout does not depend on seqlen_k).
+ */
+int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse,
+               int batch, int seqlen_q, int nheads, int headdim, int num_splits,
+               hipStream_t stream);
+
+/* fa_status_str - static, human-readable name of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/fa.h
+declares, and rejects invalid arguments before any GPU work (no GPU needed:
+validation returns before the first HIP call)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_56_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa_mi355x.so is not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == ["fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_status_str"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in include/fa.h but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.fa_status_str(0) == b"FA_OK"
+    for code in (-1, -2, -3):
+        s = lib.fa_status_str(code)
+        assert s and s != b"unknown status"
+    assert lib.fa_status_str(12345) == b"unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def fwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, batch=1, seqlen_q=4, seqlen_k=4, nheads=2,
+             headdim=64, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1), (dict(lse=None), -1),
+    (dict(batch=0), -1), (dict(seqlen_q=0), -1), (dict(seqlen_k=-3), -1), (dict(nheads=0), -1),
+    (dict(headdim=0), -1), (dict(wl=-2), -1), (dict(wr=-5), -1), (dict(scale=math.inf), -1),
+    (dict(scale=math.nan), -1), (dict(headdim=96), -2), (dict(headdim=32), -2), (dict(headdim=512), -2),
+    (dict(seqlen_q=(1 << 30) + 1), -1),
+])
+def test_fwd_rejects_invalid(lib, over, code):
+    assert lib.fa_fwd(*fwd_args(**over)) == code
+
+
+@pytest.mark.parametrize("over,ns,code", [
+    (dict(), 0, -1), (dict(), 5, -1), (dict(), -1, -1), (dict(out=None), 2, -1),
+    (dict(headdim=80), 2, -2), (dict(scale=math.nan), 2, -1),
+])
+def test_splitkv_rejects_invalid(lib, over, ns, code):
+    a = fwd_args(**over)
+    a.insert(15, ns)  # num_splits comes just before the stream
+    assert lib.fa_fwd_splitkv(*a) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 2, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 100, 2, None), -2),
+])
+def test_combine_rejects_invalid(lib, args, code):
+    assert lib.fa_combine(*args) == code
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_func(q, q, q)
+    with pytest.raises(TypeError):
+        fa.flash_attn_func(q.float(), q, q)
