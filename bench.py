@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward on one MI355X.
+
+Metric: attention forward TFLOP/s (bf16 inputs, fp32 accumulation) on the pages'
+benchmark shape (hidden 2048 = 16 heads x headdim 128, seqlen 2048,
+batch 16384 / seqlen = 8), as a fraction of the dense bf16 MFMA peak.
+
+One step = fa_fwd non-causal + fa_fwd causal over one batch of seeded synthetic
+Q/K/V already resident in HBM.  FLOPs are algorithmic: 4 * headdim per visible
+(query, key) pair (Q K^T and P V); masked pairs the method skips are not counted.
+
+Printed: ONE JSON line with the contract fields plus
+  roofline      the forward kernel: algorithmic FLOPs per launch / mean launch time
+                (HIP events on the launch stream), against the bf16 MFMA peak;
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the workload;
+  extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k) and the
+                split-KV decode workload in HBM GB/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import exact_attention_56_amd as fa  # noqa: E402
+from exact_attention_56_amd.inputs import WORKLOADS, Workload, make_qkv, sweep_workload  # noqa: E402
+
+METRIC = "attention fwd TFLOPS (bf16, 1 MI355X) at hd128 seqlen 2k-16k; % of MFMA peak"
+# MI355X published dense peaks: 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU, and HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs(w: Workload) -> int:
+    """(query, key) pairs the mask keeps, per (batch, head): bottom-right aligned
+    position c = i + Sk - Sq, window [c - left, c + right] (right = 0 if causal)."""
+    wr = 0 if w.causal else w.window_right
+    total = 0
+    for i in range(w.seqlen_q):
+        c = i + w.seqlen_k - w.seqlen_q
+        lo = 0 if w.window_left < 0 else max(0, c - w.window_left)
+        hi = w.seqlen_k - 1 if wr < 0 else min(w.seqlen_k - 1, c + wr)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def algorithmic_flops(w: Workload) -> float:
+    return 4.0 * w.headdim * visible_pairs(w) * w.batch * w.nheads
+
+
+def convention_flops(w: Workload) -> float:
+    f = 4.0 * w.batch * w.nheads * w.seqlen_q * w.seqlen_k * w.headdim
+    return f / 2 if w.causal else f
+
+
+class FwdCase:
+    """Device-resident inputs and outputs for repeated fa_fwd launches."""
+
+    def __init__(self, w: Workload, q, k, v, slopes=None):
+        self.w, self.q, self.k, self.v, self.slopes = w, q, k, v, slopes
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty(w.batch, w.nheads, w.seqlen_q, dtype=torch.float32, device=q.device)
+        self.flops = algorithmic_flops(w)
+
+    def launch(self):
+        fa.fwd(self.q, self.k, self.v, self.out, self.lse, self.w.softmax_scale, self.w.causal,
+               (self.w.window_left, self.w.window_right), self.slopes)
+
+
+def time_events(fn, reps: int):
+    """Mean and min duration (ms) of fn() over reps, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return sum(ts) / len(ts), min(ts)
+
+
+def cpu_baseline(cases, budget_s: float):
+    """The fp64 oracle on host cores over whole (batch, head) slices of the workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    done_flops, n_slices = 0.0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for case in cases:
+            w = case.w
+            b, h = n_slices % w.batch, (n_slices // w.batch) % w.nheads
+            q = case.q_cpu[b:b + 1, :, h:h + 1]
+            k = case.k_cpu[b:b + 1, :, h:h + 1]
+            v = case.v_cpu[b:b + 1, :, h:h + 1]
+            oracle.attention_forward(q, k, v, w.softmax_scale, w.causal, w.window_left, w.window_right)
+            done_flops += case.flops / (w.batch * w.nheads)
+        n_slices += 1
+        if n_slices >= cases[0].w.batch * cases[0].w.nheads:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_slices} (batch, head) slices of each of: "
+                      + ", ".join(c.w.name for c in cases)
+                      + f" (full seqlen rows, fp64 NumPy), {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def sweep(dev, reps: int, warmup: int):
+    res = {}
+    for s in (4096, 8192, 16384):
+        w = sweep_workload(s)
+        q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
+        case = FwdCase(w, q, k, v)
+        for _ in range(warmup):
+            case.launch()
+        mean_ms, min_ms = time_events(case.launch, reps)
+        tf = case.flops / (mean_ms * 1e-3) / 1e12
+        res[w.name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4),
+                       "shape": [w.batch, w.nheads, w.seqlen_q, w.seqlen_k, w.headdim]}
+        del q, k, v, case
+    return res
+
+
+def decode_bench(dev, reps: int, warmup: int):
+    w = WORKLOADS["decode_s32768"]
+    q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
+    ns = w.num_splits
+    op = torch.empty(ns, w.batch, w.nheads, w.seqlen_q, w.headdim, dtype=torch.float32, device=dev)
+    lp = torch.empty(ns, w.batch, w.nheads, w.seqlen_q, dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.nheads, w.seqlen_q, dtype=torch.float32, device=dev)
+
+    def partial():
+        fa.fwd_splitkv(q, k, v, op, lp, ns, w.softmax_scale, w.causal, (w.window_left, w.window_right))
+
+    def both():
+        partial()
+        fa.combine(op, lp, out, lse)
+
+    for _ in range(warmup):
+        both()
+    p_mean, p_min = time_events(partial, reps)
+    b_mean, _ = time_events(both, reps)
+    kv_bytes = 2 * k.numel() * 2
+    partial_bytes = kv_bytes + q.numel() * 2 + op.numel() * 4 + lp.numel() * 4
+    pair_bytes = partial_bytes + op.numel() * 4 + lp.numel() * 4 + out.numel() * 2 + lse.numel() * 4
+    return {"workload": "decode_s32768 (batch 8, 16 heads x 128, seqlen_q 1, seqlen_k 32768, causal, 16 splits)",
+            "splitkv_gbs": round(partial_bytes / (p_mean * 1e-3) / 1e9, 1),
+            "splitkv_frac_hbm_peak": round(partial_bytes / (p_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "splitkv_mean_us": round(p_mean * 1e3, 2), "splitkv_min_us": round(p_min * 1e3, 2),
+            "pair_mean_us": round(b_mean * 1e3, 2),
+            "pair_gbs": round(pair_bytes / (b_mean * 1e-3) / 1e9, 1),
+            "bytes_per_splitkv_launch": partial_bytes}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the seqlen sweep and the decode workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(each GPU would run fa_fwd on its own batch/head share).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    fa.load_library()
+
+    base = WORKLOADS["bench_s2048"]
+    causal = WORKLOADS["bench_s2048_causal"]
+    q_cpu, k_cpu, v_cpu = make_qkv(base.batch, base.seqlen_q, base.seqlen_k, base.nheads, base.headdim, base.seed)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    cases = [FwdCase(base, q, k, v), FwdCase(causal, q, k, v)]
+    for c in cases:
+        c.q_cpu, c.k_cpu, c.v_cpu = q_cpu, k_cpu, v_cpu
+
+    def step():
+        for c in cases:
+            c.launch()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, wall clock bracketed by synchronisation, with
+    # HIP events around every forward launch on the launch stream
+    stream = torch.cuda.current_stream()
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in cases:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            c.launch()
+            b.record(stream)
+            evs.append((c, a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_flops = sum(c.flops for c in cases)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_flops * args.steps / wall / 1e12
+    launch_ms = [a.elapsed_time(b) for _, a, b in evs]
+    launch_flops = [c.flops for c, _, _ in evs]
+    achieved = sum(launch_flops) / (sum(launch_ms) * 1e-3) / 1e12
+    per_case = {}
+    for c in cases:
+        ts = [a.elapsed_time(b) for cc, a, b in evs if cc is c]
+        m = sum(ts) / len(ts)
+        per_case[c.w.name] = {"mean_ms": round(m, 4), "min_ms": round(min(ts), 4),
+                              "tflops": round(c.flops / (m * 1e-3) / 1e12, 1),
+                              "algorithmic_gflop": round(c.flops / 1e9, 2),
+                              "convention_gflop": round(convention_flops(c.w) / 1e9, 2)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q/K/V rounded to bf16)",
+        "config": {"workload": "bench_s2048: batch 8, 16 heads x headdim 128, seqlen_q = seqlen_k = 2048, "
+                               "one non-causal + one causal fa_fwd per step",
+                   "global_batch": base.batch, "seq_len": base.seqlen_q, "nheads": base.nheads,
+                   "headdim": base.headdim, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fa::fwd_kernel<128,false,false>", "per_launch": per_case},
+    }
+    if not args.no_extra:
+        result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
+                           "decode": decode_bench(dev, reps=20, warmup=3)}
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,13 +65,22 @@ def sweep_workload(seqlen: int, causal: bool = False) -> Workload:
 
 
 def make_qkv(batch: int, seqlen_q: int, seqlen_k: int, nheads: int, headdim: int, seed: int,
-             nheads_k: Optional[int] = None):
-    """Draw q [B,Sq,H,D], k and v [B,Sk,H,D] as bf16 CPU tensors from one seeded generator."""
+             nheads_k: Optional[int] = None, device: str = "cpu"):
+    """Draw q [B,Sq,H,D], k and v [B,Sk,H,D] as bf16 tensors from one seeded generator.
+
+    device="cpu" (the default) gives the tensors the oracle and the parity tests
+    use.  A GPU device draws from that device's generator instead: same
+    distribution and seed, different values; it only serves timing runs.
+    """
     hk = nheads if nheads_k is None else nheads_k
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    q = torch.randn(batch, seqlen_q, nheads, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn(batch, seqlen_k, hk, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn(batch, seqlen_k, hk, headdim, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    g = torch.Generator(device=device).manual_seed(seed)
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+
+    q = draw(batch, seqlen_q, nheads, headdim)
+    k = draw(batch, seqlen_k, hk, headdim)
+    v = draw(batch, seqlen_k, hk, headdim)
     return q, k, v
 
 
