@@ -65,8 +65,17 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
   p->seqlen_q = seqlen_q;
   p->seqlen_k = seqlen_k;
   p->nheads = nheads;
-  p->scale_log2 = fabsf(softmax_scale) * fa::kLog2e;
-  p->q_sign = signbit(softmax_scale) ? 0x80008000u : 0u;
+  // The kernels fold the scale into Q's sign and a positive multiplier: a negative
+  // scale negates Q, a zero scale zeroes Q (every score is then exactly 0).
+  if (softmax_scale == 0.f) {
+    p->scale_log2 = 1.f;
+    p->q_and = 0u;
+    p->q_sign = 0u;
+  } else {
+    p->scale_log2 = fabsf(softmax_scale) * fa::kLog2e;
+    p->q_and = 0xffffffffu;
+    p->q_sign = signbit(softmax_scale) ? 0x80008000u : 0u;
+  }
   p->window_left = wl;
   p->window_right = wr;
   p->num_q_tiles = (seqlen_q + kQTile - 1) / kQTile;

@@ -27,7 +27,8 @@ struct FwdParams {
   float* lse;             // fp32 [B, H, Sq]     or fp32 [S, B, H, Sq]    (split mode)
   const float* alibi;     // fp32 [H] ALiBi slopes, or nullptr
   int batch, seqlen_q, seqlen_k, nheads;
-  float scale_log2;       // |softmax_scale| * log2(e)
+  float scale_log2;       // |softmax_scale| * log2(e), or 1 when softmax_scale == 0
+  uint32_t q_and;         // 0 when softmax_scale == 0 (Q is zeroed on load), else all ones
   uint32_t q_sign;        // 0x80008000 when softmax_scale < 0 (Q is negated on load), else 0
   int window_left;        // -1 = unbounded
   int window_right;       // -1 = unbounded; already 0 when causal

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
   float qv[8];
   {
-    const u32x4 raw = *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8);
+    const u32x4 raw = *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qv[2 * e] = bf16_lo(raw[e]) * c;

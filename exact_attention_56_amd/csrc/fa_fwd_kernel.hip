@@ -17,28 +17,36 @@
 //    (batch, head, query tile[, key split]); the linear block id is remapped so
 //    that each XCD works on a contiguous range of (batch, head) and keeps that
 //    head's K/V in its own L2;
-//  * key tiles of 64 rows are staged through LDS, double buffered, with one
-//    barrier per tile; the global loads of tile t+1 are in flight while tile t
-//    is computed;
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    every lane then owns one query column, so the softmax row statistics are
+//    every lane owns one query column, so the softmax row statistics are
 //    lane-local plus one v_permlane32_swap between the two half-waves;
 //  * K rows are stored in LDS with bits 2 and 3 of the row index swapped; with
 //    that order the fp32 S^T accumulator, rounded to bf16, is already laid out as
-//    the B operand of the second product O^T += V^T P^T, so P never leaves the
-//    registers;
+//    the B operand of O^T += V^T P^T, so P never leaves the registers;
 //  * V is transposed once, in registers, on its way into LDS (V^T rows of 64 keys)
 //    so the A operand of O^T += V^T P^T is a plain 16-byte LDS read;
-//  * exponentials use exp2 with scale*log2(e) folded into one FMA; only tiles that
-//    straddle a mask boundary evaluate the per-element visibility test.
+//  * two-stage software pipeline per 64-key tile t: the products for S(t+1) are
+//    issued between the exponentials of tile t, and O += V(t) P(t) between the
+//    row maxima of S(t+1), so the matrix cores and the vector ALUs work together;
+//    K runs two tiles ahead of the compute and V one tile ahead, double buffered
+//    in LDS, one barrier per tile;
+//  * the running maximum is only moved (and O, l rescaled) when a row's maximum
+//    grows by more than 2^8; otherwise the stale maximum is kept, which leaves the
+//    result exact (O and l share it) and removes the rescale from almost every tile;
+//  * exponentials use exp2 with scale*log2(e) folded into one FMA; the row sum is
+//    accumulated from the fp32 exponentials (P is rounded to bf16 only for P V);
+//  * K/V tiles are read with buffer loads whose range ends at the last valid key,
+//    so ragged tails read zeros without branches; only tiles crossing a mask
+//    boundary run the per-element visibility test.
 #include "fa_common.h"
 
 namespace fa {
 
-constexpr int BR = 128;       // query rows per workgroup
-constexpr int BC = 64;        // keys per tile
-constexpr int NTHREADS = 256; // 4 waves
-constexpr int PAD = 8;        // bf16 padding per LDS row (16 bytes) against bank conflicts
+constexpr int BR = 128;        // query rows per workgroup
+constexpr int BC = 64;         // keys per tile
+constexpr int NTHREADS = 256;  // 4 waves
+constexpr int PAD = 8;         // bf16 padding per LDS row (16 bytes) against bank conflicts
+constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
 
 template <int HD>
 struct Tile {
@@ -46,17 +54,11 @@ struct Tile {
   static constexpr int VROW = BC + PAD;   // V^T tile row pitch in LDS (elements)
   static constexpr int KELEMS = BC * KROW;
   static constexpr int VELEMS = HD * VROW;
-  static constexpr int LDS_ELEMS = 2 * (KELEMS + VELEMS);  // two buffers
+  static constexpr int LDS_ELEMS = 2 * (KELEMS + VELEMS);  // two buffers each
   static constexpr int CPR = HD / 8;      // 16-byte chunks per K/V row
   static constexpr int KU = BC * CPR / NTHREADS;  // K chunks per thread (= HD/32)
   static constexpr int KR = HD / 32;      // V rows per thread (one 8-wide column chunk)
   static constexpr int KB = BC / KR;      // V key blocks across the tile
-};
-
-template <int HD>
-struct TileRegs {
-  u32x4 k[Tile<HD>::KU];
-  u32x4 v[Tile<HD>::KR];
 };
 
 // LDS row that holds key `row` of the tile: bits 2 and 3 swapped (an involution).
@@ -64,25 +66,11 @@ __device__ __forceinline__ int k_lds_row(int row) {
   return (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
 }
 
-template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD>& r, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, long row_stride,
-                                          int j0, int key_hi, int tid) {
-  using T = Tile<HD>;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int u = 0; u < T::KU; ++u) {
-    const int id = tid + NTHREADS * u;
-    const int row = id / T::CPR, col = id % T::CPR;
-    const int key = j0 + row;
-    r.k[u] = key < key_hi ? *(const u32x4*)(kbase + (long)key * row_stride + col * 8) : zero;
-  }
-  const int kb = tid % T::KB, dc = tid / T::KB;
-#pragma unroll
-  for (int rr = 0; rr < T::KR; ++rr) {
-    const int key = j0 + kb * T::KR + rr;
-    r.v[rr] = key < key_hi ? *(const u32x4*)(vbase + (long)key * row_stride + dc * 8) : zero;
-  }
+// Buffer resource over `rows` rows of a K or V tile starting at `base`; loads past
+// the last row return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rows, int row_bytes) {
+  const int n = rows > 0 ? min(rows, BC) * row_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
 }
 
 // Two bf16 halves (`half` 0 = low, 1 = high) of a and b, packed a-first.
@@ -91,32 +79,128 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, int half) 
 }
 
 template <int HD>
-__device__ __forceinline__ void store_tile(const TileRegs<HD>& r, uint16_t* ks, uint16_t* vt, int tid) {
+__device__ __forceinline__ void store_k(const u32x4 (&kr)[Tile<HD>::KU], uint16_t* ks, int tid) {
   using T = Tile<HD>;
 #pragma unroll
   for (int u = 0; u < T::KU; ++u) {
     const int id = tid + NTHREADS * u;
     const int row = id / T::CPR, col = id % T::CPR;
-    *(u32x4*)(ks + k_lds_row(row) * T::KROW + col * 8) = r.k[u];
+    *(u32x4*)(ks + k_lds_row(row) * T::KROW + col * 8) = kr[u];
   }
-  // V^T: this thread holds KR consecutive keys x 8 consecutive columns; write each
-  // column as KR consecutive keys of one V^T row.
+}
+
+// V^T: this thread holds KR consecutive keys x 8 consecutive columns; write each
+// column as KR consecutive keys of one V^T row.
+template <int HD>
+__device__ __forceinline__ void store_vt(const u32x4 (&vr)[Tile<HD>::KR], uint16_t* vt, int tid) {
+  using T = Tile<HD>;
   const int kb = tid % T::KB, dc = tid / T::KB;
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     uint16_t* dst = vt + (dc * 8 + d) * T::VROW + kb * T::KR;
-    const int w = d >> 1, half = d & 1;
+    const int w = d >> 1, hf = d & 1;
     if constexpr (T::KR == 2) {
-      *(uint32_t*)dst = pick_pair(r.v[0][w], r.v[1][w], half);
+      *(uint32_t*)dst = pick_pair(vr[0][w], vr[1][w], hf);
     } else if constexpr (T::KR == 4) {
-      u32x2 o = {pick_pair(r.v[0][w], r.v[1][w], half), pick_pair(r.v[2][w], r.v[3][w], half)};
+      u32x2 o = {pick_pair(vr[0][w], vr[1][w], hf), pick_pair(vr[2][w], vr[3][w], hf)};
       *(u32x2*)dst = o;
     } else {
-      u32x4 o = {pick_pair(r.v[0][w], r.v[1][w], half), pick_pair(r.v[2][w], r.v[3][w], half),
-                 pick_pair(r.v[4][w], r.v[5][w], half), pick_pair(r.v[6][w], r.v[7][w], half)};
+      u32x4 o = {pick_pair(vr[0][w], vr[1][w], hf), pick_pair(vr[2][w], vr[3][w], hf),
+                 pick_pair(vr[4][w], vr[5][w], hf), pick_pair(vr[6][w], vr[7][w], hf)};
       *(u32x4*)dst = o;
     }
   }
+}
+
+template <int HD>
+struct KVStream {
+  using T = Tile<HD>;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int key_lo, key_hi, row_bytes;
+  int row_stride;          // elements between consecutive keys
+  uint32_t k_off[T::KU];   // byte offsets of this thread's K chunks inside a tile
+  uint32_t v_off[T::KR];   // byte offsets of this thread's V rows inside a tile
+
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int u = 0; u < T::KU; ++u) {
+      const int id = tid + NTHREADS * u;
+      k_off[u] = (uint32_t)((id / T::CPR) * row_bytes + (id % T::CPR) * 16);
+    }
+    const int kb = tid % T::KB, dc = tid / T::KB;
+#pragma unroll
+    for (int rr = 0; rr < T::KR; ++rr) v_off[rr] = (uint32_t)((kb * T::KR + rr) * row_bytes + dc * 16);
+  }
+  // tile t starts at key key_lo + t*BC; keys at or past key_hi read as zeros
+  __device__ __forceinline__ void load_k(u32x4 (&kr)[T::KU], int t) const {
+    const int j0 = key_lo + t * BC;
+    const auto rs = tile_rsrc(kbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
+#pragma unroll
+    for (int u = 0; u < T::KU; ++u)
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)k_off[u], 0, 0));
+  }
+  __device__ __forceinline__ void load_v(u32x4 (&vr)[T::KR], int t) const {
+    const int j0 = key_lo + t * BC;
+    const auto rs = tile_rsrc(vbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
+#pragma unroll
+    for (int rr = 0; rr < T::KR; ++rr)
+      vr[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)v_off[rr], 0, 0));
+  }
+};
+
+// S^T (64 keys x 32 queries of this wave) = K_tile Q^T, two 32x32 blocks.
+template <int HD>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint16_t* kt, const bf16x8 (&qf)[HD / 16],
+                                        int lrow, int half) {
+  using T = Tile<HD>;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < HD / 16; ++kk) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *(const bf16x8*)(kt + (32 * kb + lrow) * T::KROW + 16 * kk + 8 * half);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+    }
+  }
+}
+
+// Mask (and, with ALiBi, bias) the scores of one tile in place.  Without ALiBi the
+// scores stay raw (unscaled); with ALiBi they become scale*log2e*s + bias*log2e.
+template <bool ALIBI>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], bool full, int j0, int key_hi, int my_pos, int wl,
+                                          int wr, float c, float slope, int half) {
+  if (!ALIBI && full) return;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // key held by (lane, r): see k_lds_row for the row order
+      const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+      float tv = s[kb][r];
+      if constexpr (ALIBI) tv = tv * c - slope * fabsf((float)(my_pos - key));
+      if (!full) {
+        const bool vis = key < key_hi && (wl < 0 || key >= my_pos - wl) && (wr < 0 || key <= my_pos + wr);
+        tv = vis ? tv : -INFINITY;
+      }
+      s[kb][r] = tv;
+    }
+  }
+}
+
+// Max of the scores in log2 units: the stored max times `cs` (> 0); -inf stays -inf.
+__device__ __forceinline__ float to_log2(float mx, float cs) { return mx == -INFINITY ? mx : mx * cs; }
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+  float m0 = fmaxf(s[0][0], s[0][1]);
+  float m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) {
+    m0 = fmaxf(m0, fmaxf(s[0][r], s[0][r + 1]));
+    m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
+  }
+  return max_with_other_half(fmaxf(m0, m1));
 }
 
 template <int HD, bool ALIBI, bool SPLIT>
@@ -153,8 +237,15 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   }
   const long row_stride = (long)p.nheads * HD;
   const uint16_t* __restrict__ qbase = p.q + (long)b * Sq * row_stride + (long)h * HD;
-  const uint16_t* __restrict__ kbase = p.k + (long)b * Sk * row_stride + (long)h * HD;
-  const uint16_t* __restrict__ vbase = p.v + (long)b * Sk * row_stride + (long)h * HD;
+
+  KVStream<HD> kv;
+  kv.kbase = p.k + (long)b * Sk * row_stride + (long)h * HD;
+  kv.vbase = p.v + (long)b * Sk * row_stride + (long)h * HD;
+  kv.key_lo = key_lo;
+  kv.key_hi = key_hi;
+  kv.row_stride = (int)row_stride;
+  kv.row_bytes = (int)row_stride * 2;
+  kv.init(tid);
 
   const int i0 = qt * BR;
   const int i_last = min(i0 + BR, Sq) - 1;
@@ -170,6 +261,11 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
     t_begin = (lo - key_lo) / BC;
     t_end = (hi - key_lo) / BC + 1;
   }
+  // every (row, key) of tile t visible to every valid row of the block?
+  auto tile_full = [&](int t) {
+    const int j0 = key_lo + t * BC;
+    return (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
+  };
 
   // ---- Q fragments: B operand of S^T = K Q^T, held for the whole loop ----------
   const int my_q = i0 + wave * 32 + lrow;
@@ -179,133 +275,106 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   for (int kk = 0; kk < HD / 16; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_q < Sq) raw = *(const u32x4*)(qbase + (long)my_q * row_stride + 16 * kk + 8 * half);
-    raw ^= p.q_sign;
+    raw = (raw & p.q_and) ^ p.q_sign;
     qf[kk] = __builtin_bit_cast(bf16x8, raw);
   }
 
   f32x16 oacc[HD / 32];
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max, log2 units
-  float l_run = 0.f;        // this lane's share of the running row sum
+  float m_run = -INFINITY;  // maximum the exponentials are taken against (log2 units)
+  float l_run = 0.f;        // this lane's share of the row sum, against m_run
   const float c = p.scale_log2;
   float slope = 0.f;
   if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;  // bias in log2 units
+  // multiplier turning the stored scores into log2 units
+  const float cs = ALIBI ? 1.f : c;
 
-  TileRegs<HD> regs;
-  int buf = 0;
+  f32x16 s_cur[2];
+  u32x4 kreg[T::KU], vreg[T::KR];
+
   if (t_begin < t_end) {
-    load_tile<HD>(regs, kbase, vbase, row_stride, key_lo + t_begin * BC, key_hi, tid);
-    store_tile<HD>(regs, ks0, vt0, tid);
+    // prologue: K and V of the first tile, K of the second, then S of the first
+    kv.load_k(kreg, t_begin);
+    kv.load_v(vreg, t_begin);
+    store_k<HD>(kreg, ks0, tid);
+    store_vt<HD>(vreg, vt0, tid);
+    kv.load_k(kreg, t_begin + 1);  // zeros when past the last key: harmless
+    store_k<HD>(kreg, ks0 + T::KELEMS, tid);
     __syncthreads();
+    qk_tile<HD>(s_cur, ks0, qf, lrow, half);
+    mask_tile<ALIBI>(s_cur, tile_full(t_begin), key_lo + t_begin * BC, key_hi, my_pos, wl, wr, c, slope, half);
+    m_run = to_log2(tile_max(s_cur), cs);
+    __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int j0 = key_lo + t * BC;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) load_tile<HD>(regs, kbase, vbase, row_stride, j0 + BC, key_hi, tid);
+    const int par = (t - t_begin) & 1;
+    uint16_t* const k_next = ks0 + (par ^ 1) * T::KELEMS;  // K of tile t+1
+    uint16_t* const k_free = ks0 + par * T::KELEMS;        // receives K of tile t+2
+    uint16_t* const v_cur = vt0 + par * T::VELEMS;         // V of tile t
+    uint16_t* const v_free = vt0 + (par ^ 1) * T::VELEMS;  // receives V of tile t+1
 
-    const uint16_t* kt = ks0 + buf * T::KELEMS;
-    const uint16_t* vtile = vt0 + buf * T::VELEMS;
+    kv.load_k(kreg, t + 2);
+    kv.load_v(vreg, t + 1);
 
-    // S^T (64 keys x 32 queries per wave) as two 32x32 blocks.
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kt + (32 * kb + lrow) * T::KROW + 16 * kk + 8 * half);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-      }
-    }
+    // ---- stage A: S(t+1) = K(t+1) Q^T, and P(t) = exp2(S(t) - m) --------------
+    f32x16 s_nxt[2];
+    qk_tile<HD>(s_nxt, k_next, qf, lrow, half);
 
-    // Is every (row, key) of this tile visible to every valid row of the block?
-    const bool full = (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) &&
-                      (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
-
-    float tmax;
-    if (ALIBI || !full) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // key held by (lane, r): see k_lds_row for the row order
-          const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-          float tv = s[kb][r] * c;
-          if constexpr (ALIBI) tv -= slope * fabsf((float)(my_pos - key));
-          if (!full) {
-            const bool vis = key < key_hi && (wl < 0 || key >= my_pos - wl) && (wr < 0 || key <= my_pos + wr);
-            tv = vis ? tv : -INFINITY;
-          }
-          s[kb][r] = tv;
-          mx = fmaxf(mx, tv);
-        }
-      }
-      tmax = max_with_other_half(mx);
-    } else {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      tmax = max_with_other_half(mx) * c;
-    }
-
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // empty so far: keep exp args finite
-    const float alpha = fast_exp2(m_run - m_use);
-    float rsum = 0.f;
-    if (ALIBI || !full) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(s[kb][r] - m_use);
-          s[kb][r] = pv;
-          rsum += pv;
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = pv;
-          rsum += pv;
-        }
-    }
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < HD / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-    // P^T in bf16: chunk ci (16 keys) is the B operand of one 32x32x16 product.
+    const float negm = (m_run == -INFINITY) ? 0.f : -m_run;
     bf16x8 pf[4];
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int ci = 0; ci < 4; ++ci) {
-      const f32x16& src = s[ci >> 1];
-      const int r0 = 8 * (ci & 1);
-      u32x4 pk = {pack_bf16x2(src[r0 + 0], src[r0 + 1]), pack_bf16x2(src[r0 + 2], src[r0 + 3]),
-                  pack_bf16x2(src[r0 + 4], src[r0 + 5]), pack_bf16x2(src[r0 + 6], src[r0 + 7])};
-      pf[ci] = __builtin_bit_cast(bf16x8, pk);
+      const int kb = ci >> 1, r0 = 8 * (ci & 1);
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm));
+        const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm));
+        pk[e] = pack_bf16x2(p0, p1);
+        // the row sum stays in fp32: the lse needs it to ~1e-4 relative, which a sum
+        // of bf16-rounded terms (2^-9 each) cannot guarantee
+        lsum0 += p0;
+        lsum1 += p1;
+      }
+      pf[ci] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
     }
+    l_run += lsum0 + lsum1;
 
-    // O^T (HD x 32 queries) += V^T P^T
+    // ---- mask S(t+1) where tile t+1 crosses a mask boundary -------------------
+    const bool nxt_full = tile_full(t + 1);
+    mask_tile<ALIBI>(s_nxt, nxt_full, key_lo + (t + 1) * BC, key_hi, my_pos, wl, wr, c, slope, half);
+
+    // ---- stage B: O += V(t)^T P(t), row max of S(t+1), stage the next tiles ---
 #pragma unroll
-    for (int db = 0; db < HD / 32; ++db) {
+    for (int ci = 0; ci < 4; ++ci) {
 #pragma unroll
-      for (int ci = 0; ci < 4; ++ci) {
-        const bf16x8 a = *(const bf16x8*)(vtile + (32 * db + lrow) * T::VROW + 16 * ci + 8 * half);
+      for (int db = 0; db < HD / 32; ++db) {
+        const bf16x8 a = *(const bf16x8*)(v_cur + (32 * db + lrow) * T::VROW + 16 * ci + 8 * half);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], oacc[db], 0, 0, 0);
       }
     }
+    const float tmax = to_log2(tile_max(s_nxt), cs);
+    store_k<HD>(kreg, k_free, tid);
+    store_vt<HD>(vreg, v_free, tid);
 
-    if (has_next) store_tile<HD>(regs, ks0 + (buf ^ 1) * T::KELEMS, vt0 + (buf ^ 1) * T::VELEMS, tid);
+    // ---- move the reference maximum only when a row grew by more than 2^8 -----
+    const float m_new = fmaxf(m_run, tmax);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m_run + RESCALE_TH) != 0, 0)) {
+      // 0 when only m_run is -inf; 1 for a row that has seen no visible key yet
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
     __syncthreads();
-    buf ^= 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
   // ---- epilogue: one division per row, logsumexp ------------------------------
