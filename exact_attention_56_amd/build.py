@@ -18,7 +18,18 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["fa_fwd_kernel.hip", "fa_decode_kernel.hip", "fa_api.hip"]
+# (source, extra flags).  headdim 64/128 keep S and O in arch VGPRs (MFMA VGPR form):
+# the softmax reads S with plain VALU ops and the kernel fits two waves per SIMD.
+# headdim 256 needs the accumulation registers, so it keeps the compiler's choice.
+VGPR_FORM = ["-mllvm", "--amdgpu-mfma-vgpr-form"]
+SOURCES = [
+    ("fa_fwd_d64.hip", VGPR_FORM),
+    ("fa_fwd_d128.hip", VGPR_FORM),
+    ("fa_fwd_d256.hip", []),
+    ("fa_fwd_launch.hip", []),
+    ("fa_decode_kernel.hip", []),
+    ("fa_api.hip", []),
+]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 OFFLOAD_ARCH = "gfx950"
 
@@ -49,10 +60,10 @@ def build(verbose: bool = False) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     objs = []
     jobs = []
-    for src in SOURCES:
+    for src, extra in SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB_PATH + ".tmp"

@@ -1,0 +1,8 @@
+// fa_fwd_d64.hip - instantiates the forward kernels for headdim 64.
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+hipError_t launch_fwd_d64(const FwdParams& p, bool split, hipStream_t stream) {
+  return launch_fwd_hd<64>(p, split, stream);
+}
+}  // namespace fa

@@ -1,4 +1,5 @@
-// fa_fwd_kernel.hip - matrix-core (MFMA) attention forward for gfx950.
+// fa_fwd_kernel.h - matrix-core (MFMA) attention forward for gfx950 (kernel templates;
+// fa_fwd_d{64,128,256}.hip instantiate them, fa_fwd_launch.hip dispatches).
 //
 // What it computes: for each (batch, head) and query row i,
 //   out_i = sum_j softmax_j(scale * q_i.k_j + bias_ij) v_j   over the visible keys j,
@@ -38,6 +39,7 @@
 //  * K/V tiles are read with buffer loads whose range ends at the last valid key,
 //    so ragged tails read zeros without branches; only tiles crossing a mask
 //    boundary run the per-element visibility test.
+#pragma once
 #include "fa_common.h"
 
 namespace fa {
@@ -166,25 +168,29 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint16_t* kt, cons
   }
 }
 
-// Mask (and, with ALiBi, bias) the scores of one tile in place.  Without ALiBi the
-// scores stay raw (unscaled); with ALiBi they become scale*log2e*s + bias*log2e.
-template <bool ALIBI>
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], bool full, int j0, int key_hi, int my_pos, int wl,
-                                          int wr, float c, float slope, int half) {
-  if (!ALIBI && full) return;
+// ALiBi: turn the raw scores of one tile into log2 units with the bias added,
+// scale*log2e*s - slope*log2e*|pos - key|.  Without ALiBi the scores stay raw.
+__device__ __forceinline__ void bias_tile(f32x16 (&s)[2], int j0, int my_pos, float c, float slope, int half) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // key held by (lane, r): see k_lds_row for the row order
       const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-      float tv = s[kb][r];
-      if constexpr (ALIBI) tv = tv * c - slope * fabsf((float)(my_pos - key));
-      if (!full) {
-        const bool vis = key < key_hi && (wl < 0 || key >= my_pos - wl) && (wr < 0 || key <= my_pos + wr);
-        tv = vis ? tv : -INFINITY;
-      }
-      s[kb][r] = tv;
+      s[kb][r] = s[kb][r] * c - slope * fabsf((float)(my_pos - key));
+    }
+  }
+}
+
+// Set the scores of keys this row may not see to -inf (tiles crossing a mask boundary).
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int j0, int key_hi, int my_pos, int wl, int wr, int half) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
+      const bool vis = key < key_hi && (wl < 0 || key >= my_pos - wl) && (wr < 0 || key <= my_pos + wr);
+      s[kb][r] = vis ? s[kb][r] : -INFINITY;
     }
   }
 }
@@ -201,6 +207,119 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
     m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
   }
   return max_with_other_half(fmaxf(m0, m1));
+}
+
+// Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+
+// Per-wave state of the forward loop.
+template <int HD>
+struct FwdState {
+  bf16x8 qf[HD / 16];       // Q^T fragments (B operand of S^T = K Q^T)
+  f32x16 oacc[HD / 32];     // O^T accumulator, unscaled
+  float m_run;              // reference maximum of the exponentials (log2 units)
+  float l_run;              // this lane's share of the row sum against m_run
+};
+
+// One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), staging of
+// K(t+2) and V(t+1), reference-maximum update.  Ends with the tile barrier.
+template <int HD, bool ALIBI>
+__device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
+                                          int t_begin, const KVStream<HD>& kv, uint16_t* ks0, uint16_t* vt0,
+                                          u32x4 (&kreg)[Tile<HD>::KU], u32x4 (&vreg)[Tile<HD>::KR], int tid,
+                                          int lrow, int half, float c, float cs, float slope, int my_pos,
+                                          int wl, int wr, int i0, int i_last, int off) {
+  using T = Tile<HD>;
+  const int par = (t - t_begin) & 1;
+  const uint16_t* const k_next = ks0 + (par ^ 1) * T::KELEMS;  // K of tile t+1
+  uint16_t* const k_free = ks0 + par * T::KELEMS;              // receives K of tile t+2
+  const uint16_t* const v_cur = vt0 + par * T::VELEMS;         // V of tile t
+  uint16_t* const v_free = vt0 + (par ^ 1) * T::VELEMS;        // receives V of tile t+1
+
+  kv.load_k(kreg, t + 2);  // past the last tile these read zeros or unused keys: harmless
+  kv.load_v(vreg, t + 1);
+
+  // S(t+1) = K(t+1) Q^T
+  qk_tile<HD>(s_nxt, k_next, st.qf, lrow, half);
+
+  // P(t) = exp2(S(t) * cs - m), rounded to bf16 for the P V product
+  const float negm = (st.m_run == -INFINITY) ? 0.f : -st.m_run;
+  bf16x8 pf[4];
+  float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+  for (int ci = 0; ci < 4; ++ci) {
+    const int kb = ci >> 1, r0 = 8 * (ci & 1);
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm));
+      const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm));
+      pk[e] = pack_bf16x2(p0, p1);
+      // the row sum stays in fp32: the lse needs it to ~1e-4 relative, which a sum
+      // of bf16-rounded terms (2^-9 each) cannot guarantee
+      lsum0 += p0;
+      lsum1 += p1;
+    }
+    pf[ci] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  }
+  st.l_run += lsum0 + lsum1;
+
+  // O^T += V(t)^T P(t)^T
+#pragma unroll
+  for (int ci = 0; ci < 4; ++ci) {
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db) {
+      const bf16x8 a = *(const bf16x8*)(v_cur + (32 * db + lrow) * T::VROW + 16 * ci + 8 * half);
+      st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], st.oacc[db], 0, 0, 0);
+    }
+  }
+
+  // max of S(t+1) before masking: exact for tiles every row sees in full
+  const int j1 = kv.key_lo + (t + 1) * BC;
+  if constexpr (ALIBI) bias_tile(s_nxt, j1, my_pos, c, slope, half);
+  float mx = tile_max(s_nxt);
+
+  store_k<HD>(kreg, k_free, tid);
+  store_vt<HD>(vreg, v_free, tid);
+
+  // Issue order: loads first, then S(t+1) products spread through the exponentials,
+  // then the P V products spread through the max of S(t+1) and the LDS stores.
+  __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KU + Tile<HD>::KR, 0);
+#pragma unroll
+  for (int i = 0; i < HD / 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < HD / 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+  }
+
+  // tiles crossing a mask boundary: mask, then take the max again
+  const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
+                        (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
+  if (!nxt_full) {
+    mask_tile(s_nxt, j1, kv.key_hi, my_pos, wl, wr, half);
+    mx = tile_max(s_nxt);
+  }
+
+  // move the reference maximum only when a row grew by more than 2^8
+  const float m_new = fmaxf(st.m_run, to_log2(mx, cs));
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > st.m_run + RESCALE_TH) != 0, 0)) {
+    // 0 when only m_run is -inf; 1 for a row that has seen no visible key yet
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    st.m_run = m_new;
+  }
+  __syncthreads();
 }
 
 template <int HD, bool ALIBI, bool SPLIT>
@@ -261,36 +380,29 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
     t_begin = (lo - key_lo) / BC;
     t_end = (hi - key_lo) / BC + 1;
   }
-  // every (row, key) of tile t visible to every valid row of the block?
-  auto tile_full = [&](int t) {
-    const int j0 = key_lo + t * BC;
-    return (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
-  };
 
   // ---- Q fragments: B operand of S^T = K Q^T, held for the whole loop ----------
+  FwdState<HD> st;
   const int my_q = i0 + wave * 32 + lrow;
   const int my_pos = my_q + off;
-  bf16x8 qf[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_q < Sq) raw = *(const u32x4*)(qbase + (long)my_q * row_stride + 16 * kk + 8 * half);
     raw = (raw & p.q_and) ^ p.q_sign;
-    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    st.qf[kk] = __builtin_bit_cast(bf16x8, raw);
   }
-
-  f32x16 oacc[HD / 32];
 #pragma unroll
-  for (int db = 0; db < HD / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // maximum the exponentials are taken against (log2 units)
-  float l_run = 0.f;        // this lane's share of the row sum, against m_run
+  for (int db = 0; db < HD / 32; ++db) st.oacc[db] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
   const float c = p.scale_log2;
   float slope = 0.f;
   if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;  // bias in log2 units
   // multiplier turning the stored scores into log2 units
   const float cs = ALIBI ? 1.f : c;
 
-  f32x16 s_cur[2];
+  f32x16 s_a[2], s_b[2];
   u32x4 kreg[T::KU], vreg[T::KR];
 
   if (t_begin < t_end) {
@@ -302,80 +414,25 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
     kv.load_k(kreg, t_begin + 1);  // zeros when past the last key: harmless
     store_k<HD>(kreg, ks0 + T::KELEMS, tid);
     __syncthreads();
-    qk_tile<HD>(s_cur, ks0, qf, lrow, half);
-    mask_tile<ALIBI>(s_cur, tile_full(t_begin), key_lo + t_begin * BC, key_hi, my_pos, wl, wr, c, slope, half);
-    m_run = to_log2(tile_max(s_cur), cs);
+    qk_tile<HD>(s_a, ks0, st.qf, lrow, half);
+    const int j0 = key_lo + t_begin * BC;
+    if constexpr (ALIBI) bias_tile(s_a, j0, my_pos, c, slope, half);
+    mask_tile(s_a, j0, key_hi, my_pos, wl, wr, half);
+    st.m_run = to_log2(tile_max(s_a), cs);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int par = (t - t_begin) & 1;
-    uint16_t* const k_next = ks0 + (par ^ 1) * T::KELEMS;  // K of tile t+1
-    uint16_t* const k_free = ks0 + par * T::KELEMS;        // receives K of tile t+2
-    uint16_t* const v_cur = vt0 + par * T::VELEMS;         // V of tile t
-    uint16_t* const v_free = vt0 + (par ^ 1) * T::VELEMS;  // receives V of tile t+1
-
-    kv.load_k(kreg, t + 2);
-    kv.load_v(vreg, t + 1);
-
-    // ---- stage A: S(t+1) = K(t+1) Q^T, and P(t) = exp2(S(t) - m) --------------
-    f32x16 s_nxt[2];
-    qk_tile<HD>(s_nxt, k_next, qf, lrow, half);
-
-    const float negm = (m_run == -INFINITY) ? 0.f : -m_run;
-    bf16x8 pf[4];
-    float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-      const int kb = ci >> 1, r0 = 8 * (ci & 1);
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm));
-        const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm));
-        pk[e] = pack_bf16x2(p0, p1);
-        // the row sum stays in fp32: the lse needs it to ~1e-4 relative, which a sum
-        // of bf16-rounded terms (2^-9 each) cannot guarantee
-        lsum0 += p0;
-        lsum1 += p1;
-      }
-      pf[ci] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-    }
-    l_run += lsum0 + lsum1;
-
-    // ---- mask S(t+1) where tile t+1 crosses a mask boundary -------------------
-    const bool nxt_full = tile_full(t + 1);
-    mask_tile<ALIBI>(s_nxt, nxt_full, key_lo + (t + 1) * BC, key_hi, my_pos, wl, wr, c, slope, half);
-
-    // ---- stage B: O += V(t)^T P(t), row max of S(t+1), stage the next tiles ---
-#pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-#pragma unroll
-      for (int db = 0; db < HD / 32; ++db) {
-        const bf16x8 a = *(const bf16x8*)(v_cur + (32 * db + lrow) * T::VROW + 16 * ci + 8 * half);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], oacc[db], 0, 0, 0);
-      }
-    }
-    const float tmax = to_log2(tile_max(s_nxt), cs);
-    store_k<HD>(kreg, k_free, tid);
-    store_vt<HD>(vreg, v_free, tid);
-
-    // ---- move the reference maximum only when a row grew by more than 2^8 -----
-    const float m_new = fmaxf(m_run, tmax);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m_run + RESCALE_TH) != 0, 0)) {
-      // 0 when only m_run is -inf; 1 for a row that has seen no visible key yet
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < HD / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  // two tiles per trip so S(t) and S(t+1) swap roles without register copies
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile_step<HD, ALIBI>(st, s_a, s_b, t, t_begin, kv, ks0, vt0, kreg, vreg, tid, lrow, half, c, cs, slope,
+                         my_pos, wl, wr, i0, i_last, off);
+    if (t + 1 >= t_end) break;
+    tile_step<HD, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, ks0, vt0, kreg, vreg, tid, lrow, half, c, cs,
+                         slope, my_pos, wl, wr, i0, i_last, off);
   }
+  f32x16* const oacc = st.oacc;
+  const float m_run = st.m_run;
+  const float l_run = st.l_run;
 
   // ---- epilogue: one division per row, logsumexp ------------------------------
   const float l_tot = sum_with_other_half(l_run);
@@ -413,33 +470,25 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
 }
 
 template <int HD, bool ALIBI, bool SPLIT>
-static hipError_t launch(const FwdParams& p, long nblocks, hipStream_t stream) {
+hipError_t launch_fwd_instance(const FwdParams& p, long nblocks, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<HD, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool ALIBI, bool SPLIT>
-static hipError_t launch_hd(const FwdParams& p, int headdim, long nblocks, hipStream_t stream) {
-  switch (headdim) {
-    case 64: return launch<64, ALIBI, SPLIT>(p, nblocks, stream);
-    case 128: return launch<128, ALIBI, SPLIT>(p, nblocks, stream);
-    case 256: return launch<256, ALIBI, SPLIT>(p, nblocks, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// Host-side launcher used by the C ABI layer.  Arguments are already validated.
-hipError_t launch_fwd(const FwdParams& p, int headdim, bool split, hipStream_t stream) {
+// One translation unit per head dimension instantiates these (separate files let
+// each get its own register-allocation flags).
+template <int HD>
+hipError_t launch_fwd_hd(const FwdParams& p, bool split, hipStream_t stream) {
   const long nblocks = (long)p.batch * p.nheads * p.num_q_tiles * (split ? p.num_splits : 1);
   const bool alibi = p.alibi != nullptr;
-  if (split) return alibi ? launch_hd<true, true>(p, headdim, nblocks, stream)
-                          : launch_hd<false, true>(p, headdim, nblocks, stream);
-  return alibi ? launch_hd<true, false>(p, headdim, nblocks, stream)
-               : launch_hd<false, false>(p, headdim, nblocks, stream);
+  if (split) return alibi ? launch_fwd_instance<HD, true, true>(p, nblocks, stream)
+                          : launch_fwd_instance<HD, false, true>(p, nblocks, stream);
+  return alibi ? launch_fwd_instance<HD, true, false>(p, nblocks, stream)
+               : launch_fwd_instance<HD, false, false>(p, nblocks, stream);
 }
 
-long fwd_num_blocks(const FwdParams& p, bool split) {
-  return (long)p.batch * p.nheads * p.num_q_tiles * (split ? p.num_splits : 1);
-}
+hipError_t launch_fwd_d64(const FwdParams& p, bool split, hipStream_t stream);
+hipError_t launch_fwd_d128(const FwdParams& p, bool split, hipStream_t stream);
+hipError_t launch_fwd_d256(const FwdParams& p, bool split, hipStream_t stream);
 
 }  // namespace fa
