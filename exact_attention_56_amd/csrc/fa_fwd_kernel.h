@@ -24,8 +24,10 @@
 //  * K rows are stored in LDS with bits 2 and 3 of the row index swapped; with
 //    that order the fp32 S^T accumulator, rounded to bf16, is already laid out as
 //    the B operand of O^T += V^T P^T, so P never leaves the registers;
-//  * V is transposed once, in registers, on its way into LDS (V^T rows of 64 keys)
-//    so the A operand of O^T += V^T P^T is a plain 16-byte LDS read;
+//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//    destination, no staging registers); V stays in its natural [key][d] layout
+//    and the A operand of O^T += V^T P^T is assembled with two ds_read_b64_tr_b16
+//    transpose reads per product;
 //  * two-stage software pipeline per 64-key tile t: the products for S(t+1) are
 //    issued between the exponentials of tile t, and O += V(t) P(t) between the
 //    row maxima of S(t+1), so the matrix cores and the vector ALUs work together;
@@ -36,9 +38,9 @@
 //    result exact (O and l share it) and removes the rescale from almost every tile;
 //  * exponentials use exp2 with scale*log2(e) folded into one FMA; the row sum is
 //    accumulated from the fp32 exponentials (P is rounded to bf16 only for P V);
-//  * K/V tiles are read with buffer loads whose range ends at the last valid key,
-//    so ragged tails read zeros without branches; only tiles crossing a mask
-//    boundary run the per-element visibility test.
+//  * the buffer loads' range ends at the last valid key, so ragged tails land in
+//    LDS as zeros without branches; only tiles crossing a mask boundary run the
+//    per-element visibility test.
 #pragma once
 #include "fa_common.h"
 
@@ -47,21 +49,33 @@ namespace fa {
 constexpr int BR = 128;        // query rows per workgroup
 constexpr int BC = 64;         // keys per tile
 constexpr int NTHREADS = 256;  // 4 waves
-constexpr int PAD = 8;         // bf16 padding per LDS row (16 bytes) against bank conflicts
 constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
+constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: reads as zero
 
+// LDS tiles.  A K row keeps its HD/8 16-byte chunks plus one pad slot (16 lanes
+// reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); a V row
+// keeps two pad slots (the 4 rows one transpose read touches land on disjoint
+// 8-bank groups).  Pad slots are filled with zeros by out-of-range loads.
 template <int HD>
 struct Tile {
-  static constexpr int KROW = HD + PAD;   // K tile row pitch in LDS (elements)
-  static constexpr int VROW = BC + PAD;   // V^T tile row pitch in LDS (elements)
-  static constexpr int KELEMS = BC * KROW;
-  static constexpr int VELEMS = HD * VROW;
-  static constexpr int LDS_ELEMS = 2 * (KELEMS + VELEMS);  // two buffers each
-  static constexpr int CPR = HD / 8;      // 16-byte chunks per K/V row
-  static constexpr int KU = BC * CPR / NTHREADS;  // K chunks per thread (= HD/32)
-  static constexpr int KR = HD / 32;      // V rows per thread (one 8-wide column chunk)
-  static constexpr int KB = BC / KR;      // V key blocks across the tile
+  static constexpr int CPR = HD / 8;         // 16-byte chunks per K/V row in memory
+  static constexpr int KCH = CPR + 1;        // 16-byte slots per K row in LDS
+  static constexpr int VCH = CPR + 2;        // 16-byte slots per V row in LDS
+  static constexpr int KPITCH = KCH * 16;    // bytes
+  static constexpr int VPITCH = VCH * 16;
+  // 64-lane (1 KiB) direct loads per tile: the tile needs KCH (VCH) of them; the
+  // count is rounded up to a multiple of the 4 waves so every wave issues the same
+  // loads without a branch, and the buffer has room for the extra (all-zero) ones.
+  static constexpr int KPW = (KCH + 3) / 4;  // K loads per wave
+  static constexpr int VPW = (VCH + 3) / 4;  // V loads per wave
+  static constexpr int KBYTES = 4096 * KPW;  // one K buffer (>= BC * KPITCH)
+  static constexpr int VBYTES = 4096 * VPW;  // one V buffer (>= BC * VPITCH)
+  static constexpr int LDS_BYTES = 2 * (KBYTES + VBYTES);
 };
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // LDS row that holds key `row` of the tile: bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int k_lds_row(int row) {
@@ -75,86 +89,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
 }
 
-// Two bf16 halves (`half` 0 = low, 1 = high) of a and b, packed a-first.
-__device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, int half) {
-  return half == 0 ? ((a & 0xffffu) | (b << 16)) : ((a >> 16) | (b & 0xffff0000u));
-}
-
-template <int HD>
-__device__ __forceinline__ void store_k(const u32x4 (&kr)[Tile<HD>::KU], uint16_t* ks, int tid) {
-  using T = Tile<HD>;
-#pragma unroll
-  for (int u = 0; u < T::KU; ++u) {
-    const int id = tid + NTHREADS * u;
-    const int row = id / T::CPR, col = id % T::CPR;
-    *(u32x4*)(ks + k_lds_row(row) * T::KROW + col * 8) = kr[u];
-  }
-}
-
-// V^T: this thread holds KR consecutive keys x 8 consecutive columns; write each
-// column as KR consecutive keys of one V^T row.
-template <int HD>
-__device__ __forceinline__ void store_vt(const u32x4 (&vr)[Tile<HD>::KR], uint16_t* vt, int tid) {
-  using T = Tile<HD>;
-  const int kb = tid % T::KB, dc = tid / T::KB;
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    uint16_t* dst = vt + (dc * 8 + d) * T::VROW + kb * T::KR;
-    const int w = d >> 1, hf = d & 1;
-    if constexpr (T::KR == 2) {
-      *(uint32_t*)dst = pick_pair(vr[0][w], vr[1][w], hf);
-    } else if constexpr (T::KR == 4) {
-      u32x2 o = {pick_pair(vr[0][w], vr[1][w], hf), pick_pair(vr[2][w], vr[3][w], hf)};
-      *(u32x2*)dst = o;
-    } else {
-      u32x4 o = {pick_pair(vr[0][w], vr[1][w], hf), pick_pair(vr[2][w], vr[3][w], hf),
-                 pick_pair(vr[4][w], vr[5][w], hf), pick_pair(vr[6][w], vr[7][w], hf)};
-      *(u32x4*)dst = o;
-    }
-  }
-}
-
+// Streams K and V tiles from HBM into LDS.  Load u of a tile (wave u % 4 issues
+// it) fills LDS bytes [1024u, 1024u + 1024) of the buffer, lane l the 16-byte
+// slot 64u + l, i.e. row (64u + l) / KCH, slot (64u + l) % KCH; the lane fetches
+// the matching 16 bytes (K rows in the k_lds_row order) or, for a pad slot or a
+// slot past the last row, an out-of-range offset that writes zeros.
 template <int HD>
 struct KVStream {
   using T = Tile<HD>;
   const uint16_t* kbase;
   const uint16_t* vbase;
   int key_lo, key_hi, row_bytes;
-  int row_stride;          // elements between consecutive keys
-  uint32_t k_off[T::KU];   // byte offsets of this thread's K chunks inside a tile
-  uint32_t v_off[T::KR];   // byte offsets of this thread's V rows inside a tile
+  int row_stride;        // elements between consecutive keys
+  int wave;
+  uint32_t koff[T::KPW]; // this lane's byte offsets inside a K tile, per load it issues
+  uint32_t voff[T::VPW];
 
-  __device__ __forceinline__ void init(int tid) {
+  __device__ __forceinline__ void init(int wv, int lane) {
+    wave = wv;
 #pragma unroll
-    for (int u = 0; u < T::KU; ++u) {
-      const int id = tid + NTHREADS * u;
-      k_off[u] = (uint32_t)((id / T::CPR) * row_bytes + (id % T::CPR) * 16);
+    for (int i = 0; i < T::KPW; ++i) {
+      const int slot = 64 * (wave + 4 * i) + lane;
+      const int row = slot / T::KCH, ch = slot % T::KCH;
+      koff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(k_lds_row(row) * row_bytes + ch * 16) : OOB_OFFSET;
     }
-    const int kb = tid % T::KB, dc = tid / T::KB;
 #pragma unroll
-    for (int rr = 0; rr < T::KR; ++rr) v_off[rr] = (uint32_t)((kb * T::KR + rr) * row_bytes + dc * 16);
+    for (int i = 0; i < T::VPW; ++i) {
+      const int slot = 64 * (wave + 4 * i) + lane;
+      const int row = slot / T::VCH, ch = slot % T::VCH;
+      voff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
+    }
   }
-  // tile t starts at key key_lo + t*BC; keys at or past key_hi read as zeros
-  __device__ __forceinline__ void load_k(u32x4 (&kr)[T::KU], int t) const {
+  // tile t starts at key key_lo + t*BC; keys at or past key_hi land as zeros
+  __device__ __forceinline__ void load_k(lds_u8* dst, int t) const {
     const int j0 = key_lo + t * BC;
     const auto rs = tile_rsrc(kbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
-    for (int u = 0; u < T::KU; ++u)
-      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)k_off[u], 0, 0));
+    for (int i = 0; i < T::KPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (wave + 4 * i), 16, (int)koff[i], 0, 0, 0);
   }
-  __device__ __forceinline__ void load_v(u32x4 (&vr)[T::KR], int t) const {
+  __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
     const int j0 = key_lo + t * BC;
     const auto rs = tile_rsrc(vbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
-    for (int rr = 0; rr < T::KR; ++rr)
-      vr[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)v_off[rr], 0, 0));
+    for (int i = 0; i < T::VPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (wave + 4 * i), 16, (int)voff[i], 0, 0, 0);
   }
 };
 
+// Wait until this wave's direct-to-LDS loads have landed (vmcnt(0)).
+__device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // S^T (64 keys x 32 queries of this wave) = K_tile Q^T, two 32x32 blocks.
+// `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
 template <int HD>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint16_t* kt, const bf16x8 (&qf)[HD / 16],
-                                        int lrow, int half) {
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const bf16x8 (&qf)[HD / 16]) {
   using T = Tile<HD>;
   s[0] = f32x16{};
   s[1] = f32x16{};
@@ -162,10 +151,34 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint16_t* kt, cons
   for (int kk = 0; kk < HD / 16; ++kk) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *(const bf16x8*)(kt + (32 * kb + lrow) * T::KROW + 16 * kk + 8 * half);
+      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + 32 * kb * T::KPITCH + 32 * kk);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
     }
   }
+}
+
+// A operand of O^T += V^T P^T for column block db and key chunk ci: V^T[d][16ci + 8*(lane/32) + 0..7]
+// for d = 32db + lane%32.  `vt` is this lane's transpose-read address in a V buffer
+// (see vt_lane_offset); each read returns 4 consecutive keys of one column.
+template <int HD>
+__device__ __forceinline__ bf16x8 v_operand(const lds_u8* vt, int db, int ci) {
+  using T = Tile<HD>;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + 16 * ci * T::VPITCH + 64 * db));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (16 * ci + 4) * T::VPITCH + 64 * db));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Byte offset of this lane's transpose reads in a V buffer.  Within each group of
+// 16 lanes, lane 4e + q reads 4 columns of key row e: the transpose then hands lane
+// j of the group keys 0..3 of column j.  Groups: lanes 0-15 columns 0-15, 16-31
+// columns 16-31 (keys +0..7), 32-47 and 48-63 the same columns for keys +8..15.
+template <int HD>
+__device__ __forceinline__ int vt_lane_offset(int lane) {
+  using T = Tile<HD>;
+  const int g = lane >> 4, r = lane & 15;
+  return (8 * (g >> 1) + (r >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
 }
 
 // ALiBi: turn the raw scores of one tile into log2 units with the bias added,
@@ -198,19 +211,18 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int j0, int key_hi, in
 // Max of the scores in log2 units: the stored max times `cs` (> 0); -inf stays -inf.
 __device__ __forceinline__ float to_log2(float mx, float cs) { return mx == -INFINITY ? mx : mx * cs; }
 
+// Row max over the tile: this lane's 32 scores (v_maximum3 tree; no NaN reaches
+// here from finite inputs), then the other half-wave's 32.
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
-  float m0 = fmaxf(s[0][0], s[0][1]);
-  float m1 = fmaxf(s[1][0], s[1][1]);
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) {
-    m0 = fmaxf(m0, fmaxf(s[0][r], s[0][r + 1]));
-    m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
-  }
-  return max_with_other_half(fmaxf(m0, m1));
+  typedef float f32x32 __attribute__((ext_vector_type(32)));
+  const f32x32 all = __builtin_shufflevector(s[0], s[1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16,
+                                             17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
+  return max_with_other_half(__builtin_reduce_maximum(all));
 }
 
 // Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200,
+              SG_TRANS = 0x400;
 
 // Per-wave state of the forward loop.
 template <int HD>
@@ -221,26 +233,30 @@ struct FwdState {
   float l_run;              // this lane's share of the row sum against m_run
 };
 
-// One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), staging of
-// K(t+2) and V(t+1), reference-maximum update.  Ends with the tile barrier.
+// LDS buffers of the forward loop, as byte addresses.
+struct LdsBufs {
+  lds_u8* k[2];        // K tile buffers
+  lds_u8* v[2];        // V tile buffers
+  const lds_u8* kl[2]; // this lane's K operand address in each K buffer
+  const lds_u8* vl[2]; // this lane's transpose-read address in each V buffer
+};
+
+// One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), loads of
+// K(t+2) and V(t+1) into the free buffers, reference-maximum update.  Ends with
+// the tile barrier.
 template <int HD, bool ALIBI>
 __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
-                                          int t_begin, const KVStream<HD>& kv, uint16_t* ks0, uint16_t* vt0,
-                                          u32x4 (&kreg)[Tile<HD>::KU], u32x4 (&vreg)[Tile<HD>::KR], int tid,
-                                          int lrow, int half, float c, float cs, float slope, int my_pos,
-                                          int wl, int wr, int i0, int i_last, int off) {
-  using T = Tile<HD>;
+                                          int t_begin, const KVStream<HD>& kv, const LdsBufs& lb, int half,
+                                          float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
+                                          int i_last, int off) {
   const int par = (t - t_begin) & 1;
-  const uint16_t* const k_next = ks0 + (par ^ 1) * T::KELEMS;  // K of tile t+1
-  uint16_t* const k_free = ks0 + par * T::KELEMS;              // receives K of tile t+2
-  const uint16_t* const v_cur = vt0 + par * T::VELEMS;         // V of tile t
-  uint16_t* const v_free = vt0 + (par ^ 1) * T::VELEMS;        // receives V of tile t+1
-
-  kv.load_k(kreg, t + 2);  // past the last tile these read zeros or unused keys: harmless
-  kv.load_v(vreg, t + 1);
+  // K(t+1) is in k[par^1]; K(t+2) goes to k[par]; V(t) is in v[par]; V(t+1) goes to v[par^1].
+  // Past the last tile these loads read zeros or unused keys: harmless.
+  kv.load_k(lb.k[par], t + 2);
+  kv.load_v(lb.v[par ^ 1], t + 1);
 
   // S(t+1) = K(t+1) Q^T
-  qk_tile<HD>(s_nxt, k_next, st.qf, lrow, half);
+  qk_tile<HD>(s_nxt, lb.kl[par ^ 1], st.qf);
 
   // P(t) = exp2(S(t) * cs - m), rounded to bf16 for the P V product
   const float negm = (st.m_run == -INFINITY) ? 0.f : -st.m_run;
@@ -269,7 +285,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
   for (int ci = 0; ci < 4; ++ci) {
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      const bf16x8 a = *(const bf16x8*)(v_cur + (32 * db + lrow) * T::VROW + 16 * ci + 8 * half);
+      const bf16x8 a = v_operand<HD>(lb.vl[par], db, ci);
       st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], st.oacc[db], 0, 0, 0);
     }
   }
@@ -279,24 +295,55 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
   if constexpr (ALIBI) bias_tile(s_nxt, j1, my_pos, c, slope, half);
   float mx = tile_max(s_nxt);
 
-  store_k<HD>(kreg, k_free, tid);
-  store_vt<HD>(vreg, v_free, tid);
-
-  // Issue order: loads first, then S(t+1) products spread through the exponentials,
-  // then the P V products spread through the max of S(t+1) and the LDS stores.
-  __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KU + Tile<HD>::KR, 0);
+  // Issue order: the global loads; LDS operand reads running four products ahead;
+  // the S(t+1) products, each followed by two exponentials of tile t and their
+  // FMAs/conversions; then the P V products, each followed by row-sum adds, the
+  // max of S(t+1), the V transposition and the LDS stores.
+  constexpr int NQK = HD / 8;  // products per phase (S(t+1), then P V)
+#ifndef FA_SCHED
+#define FA_SCHED 1
+#endif
+  if constexpr (FA_SCHED == 2) {
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KPW + Tile<HD>::VPW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
-  for (int i = 0; i < HD / 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
-  }
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_TRANS, 32 / NQK, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < HD / 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+    }
+  } else if constexpr (FA_SCHED == 1) {
+#ifndef FA_V1
+#define FA_V1 3
+#endif
+#ifndef FA_V2
+#define FA_V2 5
+#endif
+#ifndef FA_PF
+#define FA_PF 2
+#endif
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KPW + Tile<HD>::VPW, 0);
+    if constexpr (FA_PF > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, FA_PF, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_V1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_V2, 0);
+    }
   }
 
   // tiles crossing a mask boundary: mask, then take the max again
@@ -319,19 +366,18 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
       for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
     st.m_run = m_new;
   }
+  wait_tile_loads();  // K(t+2) and V(t+1) are in LDS before anyone passes the barrier
   __syncthreads();
 }
 
 template <int HD, bool ALIBI, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   using T = Tile<HD>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[T::LDS_ELEMS];
-  uint16_t* const ks0 = smem;
-  uint16_t* const vt0 = smem + 2 * T::KELEMS;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lrow = lane & 31;  // query column / A-operand row owned by this lane
   const int half = lane >> 5;  // which 8-element k slice this lane feeds
 
@@ -364,7 +410,17 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   kv.key_hi = key_hi;
   kv.row_stride = (int)row_stride;
   kv.row_bytes = (int)row_stride * 2;
-  kv.init(tid);
+  kv.init(wave, lane);
+
+  LdsBufs lb;
+  lds_u8* const lds = (lds_u8*)smem;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lb.k[i] = lds + i * T::KBYTES;
+    lb.v[i] = lds + 2 * T::KBYTES + i * T::VBYTES;
+    lb.kl[i] = lb.k[i] + lrow * T::KPITCH + 16 * half;
+    lb.vl[i] = lb.v[i] + vt_lane_offset<HD>(lane);
+  }
 
   const int i0 = qt * BR;
   const int i_last = min(i0 + BR, Sq) - 1;
@@ -403,18 +459,15 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   const float cs = ALIBI ? 1.f : c;
 
   f32x16 s_a[2], s_b[2];
-  u32x4 kreg[T::KU], vreg[T::KR];
 
   if (t_begin < t_end) {
     // prologue: K and V of the first tile, K of the second, then S of the first
-    kv.load_k(kreg, t_begin);
-    kv.load_v(vreg, t_begin);
-    store_k<HD>(kreg, ks0, tid);
-    store_vt<HD>(vreg, vt0, tid);
-    kv.load_k(kreg, t_begin + 1);  // zeros when past the last key: harmless
-    store_k<HD>(kreg, ks0 + T::KELEMS, tid);
+    kv.load_k(lb.k[0], t_begin);
+    kv.load_v(lb.v[0], t_begin);
+    kv.load_k(lb.k[1], t_begin + 1);  // zeros when past the last key: harmless
+    wait_tile_loads();
     __syncthreads();
-    qk_tile<HD>(s_a, ks0, st.qf, lrow, half);
+    qk_tile<HD>(s_a, lb.kl[0], st.qf);
     const int j0 = key_lo + t_begin * BC;
     if constexpr (ALIBI) bias_tile(s_a, j0, my_pos, c, slope, half);
     mask_tile(s_a, j0, key_hi, my_pos, wl, wr, half);
@@ -424,11 +477,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
 
   // two tiles per trip so S(t) and S(t+1) swap roles without register copies
   for (int t = t_begin; t < t_end; t += 2) {
-    tile_step<HD, ALIBI>(st, s_a, s_b, t, t_begin, kv, ks0, vt0, kreg, vreg, tid, lrow, half, c, cs, slope,
-                         my_pos, wl, wr, i0, i_last, off);
+    tile_step<HD, ALIBI>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
     if (t + 1 >= t_end) break;
-    tile_step<HD, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, ks0, vt0, kreg, vreg, tid, lrow, half, c, cs,
-                         slope, my_pos, wl, wr, i0, i_last, off);
+    tile_step<HD, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+                         off);
   }
   f32x16* const oacc = st.oacc;
   const float m_run = st.m_run;
