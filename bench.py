@@ -20,8 +20,10 @@ Printed: ONE JSON line with the contract fields plus
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,6 +40,33 @@ METRIC = "attention fwd TFLOPS (bf16, 1 MI355X) at hd128 seqlen 2k-16k; % of MFM
 # MI355X published dense peaks: 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU, and HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_hd128_bench_s2048_hbm_traffic.txt")
+KERNEL_SOURCES = ["exact_attention_56_amd/csrc/fa_common.h", "exact_attention_56_amd/csrc/fa_fwd_kernel.h",
+                  "exact_attention_56_amd/csrc/fa_fwd_d128.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when that summary was taken on different kernel sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    hsh = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if not t or not hsh or hsh.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
 
 
 def visible_pairs(w: Workload) -> int:
@@ -172,8 +201,9 @@ def decode_bench(dev, reps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first (about 0.2 s: lets the GPU reach its steady clock)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the seqlen sweep and the decode workload")
@@ -257,7 +287,7 @@ def main():
                    "global_batch": base.batch, "seq_len": base.seqlen_q, "nheads": base.nheads,
                    "headdim": base.headdim, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "fa::fwd_kernel<128,false,false>", "per_launch": per_case},
     }
     if not args.no_extra:
