@@ -21,7 +21,8 @@ namespace {
 constexpr int kMaxSeqlen = 1 << 30;     // keeps every position/window sum inside int32
 constexpr long kMaxBlocks = 0x7fffffffL;  // grid x dimension
 constexpr int kDecodeMaxRows = 8;       // fa_fwd_splitkv: vector-ALU path up to this seqlen_q
-constexpr int kQTile = 128;             // query rows per matrix-core workgroup
+constexpr long long kMaxRowElems = 1 << 22;  // nheads * headdim
+constexpr int kQTile = fa::FWD_BLOCK_ROWS;  // query rows per matrix-core workgroup
 
 bool headdim_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
@@ -48,6 +49,9 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
   if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
   if (elems4(batch, seqlen_q, nheads, headdim) < 0 || elems4(batch, seqlen_k, nheads, headdim) < 0)
     return FA_ERR_INVALID_ARG;
+  // The kernels address at most 128 key rows (nheads*headdim bf16 apart) from one
+  // buffer base with 32-bit offsets.
+  if ((long long)nheads * headdim > kMaxRowElems) return FA_ERR_UNSUPPORTED;
 
   int wl = window_left;
   int wr = causal ? 0 : window_right;

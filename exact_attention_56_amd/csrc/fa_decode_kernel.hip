@@ -19,7 +19,14 @@
 namespace fa {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_UNROLL = 4;  // key rows per lane per step
+#ifndef FA_DEC_UNROLL
+#define FA_DEC_UNROLL 8
+#endif
+#ifndef FA_DEC_CPOL
+#define FA_DEC_CPOL 2
+#endif
+constexpr int DEC_UNROLL = FA_DEC_UNROLL;  // key rows per lane per step
+constexpr int DEC_CPOL = FA_DEC_CPOL;      // KV loads are non-temporal (read once, streamed)
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -32,7 +39,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   __shared__ float sm_m[4], sm_l[4];
   __shared__ float sm_acc[4][HD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane / LPR;   // row group inside the wave
   const int cidx = lane % LPR;  // 8-column chunk of the head dimension
 
@@ -46,8 +54,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   const int b = w / p.nheads;
 
   const long row_stride = (long)p.nheads * HD;
-  const uint16_t* __restrict__ kbase = p.k + (long)b * Sk * row_stride + (long)h * HD + cidx * 8;
-  const uint16_t* __restrict__ vbase = p.v + (long)b * Sk * row_stride + (long)h * HD + cidx * 8;
+  const int row_bytes = (int)row_stride * 2;
 
   // visible keys of row i inside this split: [lo, hi)
   const int pos = i + Sk - Sq;
@@ -55,6 +62,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   int hi = min(Sk, lo + p.split_len);
   if (p.window_left >= 0) lo = max(lo, pos - p.window_left);
   if (p.window_right >= 0) hi = min(hi, pos + p.window_right + 1);
+  const long kvb = (long)b * Sk * row_stride + (long)h * HD;  // key 0 of this (batch, head)
 
   // q chunk, pre-multiplied by softmax_scale * log2(e) (sign included)
   const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
@@ -76,13 +84,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
   for (int base = lo + wave * STEP; base < hi; base += 4 * STEP) {
+    // buffer resources over keys [base, min(hi, base + STEP)): later keys read as zeros
+    const int nrec = min(hi - base, STEP) * row_bytes;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvb + (long)base * row_stride), (short)0, nrec,
+                                                       0x00020000);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvb + (long)base * row_stride), (short)0, nrec,
+                                                       0x00020000);
     u32x4 kr[DEC_UNROLL], vr[DEC_UNROLL];
 #pragma unroll
     for (int u = 0; u < DEC_UNROLL; ++u) {
-      const int key = base + u * RPW + g;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      kr[u] = key < hi ? *(const u32x4*)(kbase + (long)key * row_stride) : zero;
-      vr[u] = key < hi ? *(const u32x4*)(vbase + (long)key * row_stride) : zero;
+      const int off = (u * RPW + g) * row_bytes + cidx * 16;
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, DEC_CPOL));
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, DEC_CPOL));
     }
     float s[DEC_UNROLL];
     float bmax = -INFINITY;

@@ -46,9 +46,11 @@
 
 namespace fa {
 
-constexpr int BR = 128;        // query rows per workgroup
-constexpr int BC = 64;         // keys per tile
-constexpr int NTHREADS = 256;  // 4 waves
+constexpr int NWAVES = FWD_WAVES;  // waves per workgroup (32 query rows each)
+constexpr int BR = FWD_BLOCK_ROWS;  // query rows per workgroup
+constexpr int BC = 64;              // keys per tile
+constexpr int NTHREADS = 64 * NWAVES;
+static_assert(BR == 32 * NWAVES, "one 32-row query block per wave");
 constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: reads as zero
 
@@ -66,8 +68,8 @@ struct Tile {
   // 64-lane (1 KiB) direct loads per tile: the tile needs KCH (VCH) of them; the
   // count is rounded up to a multiple of the 4 waves so every wave issues the same
   // loads without a branch, and the buffer has room for the extra (all-zero) ones.
-  static constexpr int KPW = (KCH + 3) / 4;  // K loads per wave
-  static constexpr int VPW = (VCH + 3) / 4;  // V loads per wave
+  static constexpr int KPW = (KCH + 3) / 4;  // K loads per loading wave (4 waves load K)
+  static constexpr int VPW = (VCH + 3) / 4;  // V loads per loading wave (4 waves load V)
   static constexpr int KBYTES = 4096 * KPW;  // one K buffer (>= BC * KPITCH)
   static constexpr int VBYTES = 4096 * VPW;  // one V buffer (>= BC * VPITCH)
   static constexpr int LDS_BYTES = 2 * (KBYTES + VBYTES);
@@ -101,39 +103,44 @@ struct KVStream {
   const uint16_t* vbase;
   int key_lo, key_hi, row_bytes;
   int row_stride;        // elements between consecutive keys
-  int wave;
+  int lw;                // this wave's index among the 4 waves loading a tensor
+  bool loads_k, loads_v; // with 8 waves, waves 0-3 load K and waves 4-7 load V
   uint32_t koff[T::KPW]; // this lane's byte offsets inside a K tile, per load it issues
   uint32_t voff[T::VPW];
 
-  __device__ __forceinline__ void init(int wv, int lane) {
-    wave = wv;
+  __device__ __forceinline__ void init(int wave, int lane) {
+    lw = wave & 3;
+    loads_k = NWAVES == 4 || wave < 4;
+    loads_v = NWAVES == 4 || wave >= 4;
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i) {
-      const int slot = 64 * (wave + 4 * i) + lane;
+      const int slot = 64 * (lw + 4 * i) + lane;
       const int row = slot / T::KCH, ch = slot % T::KCH;
       koff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(k_lds_row(row) * row_bytes + ch * 16) : OOB_OFFSET;
     }
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i) {
-      const int slot = 64 * (wave + 4 * i) + lane;
+      const int slot = 64 * (lw + 4 * i) + lane;
       const int row = slot / T::VCH, ch = slot % T::VCH;
       voff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
     }
   }
   // tile t starts at key key_lo + t*BC; keys at or past key_hi land as zeros
   __device__ __forceinline__ void load_k(lds_u8* dst, int t) const {
+    if (!loads_k) return;
     const int j0 = key_lo + t * BC;
     const auto rs = tile_rsrc(kbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (wave + 4 * i), 16, (int)koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)koff[i], 0, 0, 0);
   }
   __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
+    if (!loads_v) return;
     const int j0 = key_lo + t * BC;
     const auto rs = tile_rsrc(vbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (wave + 4 * i), 16, (int)voff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)voff[i], 0, 0, 0);
   }
 };
 
@@ -330,8 +337,13 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
 #ifndef FA_PF
 #define FA_PF 2
 #endif
+#ifndef FA_VI
+#define FA_VI 0
+#endif
     __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KPW + Tile<HD>::VPW, 0);
     if constexpr (FA_PF > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, FA_PF, 0);
+    // exponentials of tile t fill the first LDS latency after the barrier
+    if constexpr (FA_VI > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_VI, 0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);

@@ -49,7 +49,7 @@
  *   FA_ERR_INVALID_ARG (-1): a NULL required pointer, a size < 1, a window side < -1,
  *                            num_splits outside [1, seqlen_k], a non-finite softmax_scale,
  *                            or a problem whose element count overflows 64-bit indexing;
- *   FA_ERR_UNSUPPORTED (-2): headdim not in {64, 128, 256};
+ *   FA_ERR_UNSUPPORTED (-2): headdim not in {64, 128, 256}, or nheads * headdim > 2^22;
  *   FA_ERR_LAUNCH      (-3): the HIP runtime reported an error for the launch.
  *   No exception crosses the ABI and nothing is printed.
  */
