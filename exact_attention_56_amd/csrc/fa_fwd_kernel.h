@@ -72,7 +72,14 @@ struct Tile {
   static constexpr int VPW = (VCH + 3) / 4;  // V loads per loading wave (4 waves load V)
   static constexpr int KBYTES = 4096 * KPW;  // one K buffer (>= BC * KPITCH)
   static constexpr int VBYTES = 4096 * VPW;  // one V buffer (>= BC * VPITCH)
-  static constexpr int LDS_BYTES = 2 * (KBYTES + VBYTES);
+  // Ring of NBUF K and NBUF V buffers: K runs NBUF tiles ahead of the step that
+  // reads it and V NBUF-1, so a tile's loads have NBUF-1 steps to land.  Headdim 64
+  // measured slower with three buffers, so every headdim keeps two.
+  static constexpr int NBUF = 2;
+  static constexpr int LDS_BYTES = NBUF * (KBYTES + VBYTES);
+  // loads one wave issues per step (its vmcnt after a step's loads)
+  static constexpr int LOADS_PER_STEP = NWAVES == 4 ? KPW + VPW : KPW;
+  static_assert(NWAVES == 4 || KPW == VPW, "K- and V-loading waves issue equally many loads");
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -144,8 +151,13 @@ struct KVStream {
   }
 };
 
-// Wait until this wave's direct-to-LDS loads have landed (vmcnt(0)).
-__device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's direct-to-LDS loads are still in flight
+// (s_waitcnt vmcnt(N): low 4 bits of the count in [3:0], high 2 in [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_tile_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // S^T (64 keys x 32 queries of this wave) = K_tile Q^T, two 32x32 blocks.
 // `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
@@ -202,6 +214,20 @@ __device__ __forceinline__ void bias_tile(f32x16 (&s)[2], int j0, int my_pos, fl
   }
 }
 
+// ALiBi on a tile whose keys all lie on one side of every row's aligned position:
+// |pos - key| is then linear in the key, so the bias splits into slope*koff (the
+// key's offset inside the tile, the same for every lane) and a per-lane part that
+// the caller carries as the tile's log2 offset.  Stored scores become
+// scale*log2e*s + sgn*slope*log2e*koff, with sgn = +1 left of the rows, -1 right.
+__device__ __forceinline__ void bias_tile_linear(f32x16 (&s)[2], float c, float slope, bool right) {
+  if (right) slope = -slope;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, slope * (float)(32 * kb + 16 * (r >> 3) + (r & 7)));
+  }
+}
+
 // Set the scores of keys this row may not see to -inf (tiles crossing a mask boundary).
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int j0, int key_hi, int my_pos, int wl, int wr, int half) {
 #pragma unroll
@@ -218,14 +244,17 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int j0, int key_hi, in
 // Max of the scores in log2 units: the stored max times `cs` (> 0); -inf stays -inf.
 __device__ __forceinline__ float to_log2(float mx, float cs) { return mx == -INFINITY ? mx : mx * cs; }
 
-// Row max over the tile: this lane's 32 scores (v_maximum3 tree; no NaN reaches
-// here from finite inputs), then the other half-wave's 32.
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+// Max of this lane's 32 scores of the tile (v_maximum3 tree; no NaN reaches here
+// from finite inputs).
+__device__ __forceinline__ float lane_max(const f32x16 (&s)[2]) {
   typedef float f32x32 __attribute__((ext_vector_type(32)));
   const f32x32 all = __builtin_shufflevector(s[0], s[1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16,
                                              17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
-  return max_with_other_half(__builtin_reduce_maximum(all));
+  return __builtin_reduce_maximum(all);
 }
+
+// Row max over the tile: this lane's 32 scores, then the other half-wave's 32.
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) { return max_with_other_half(lane_max(s)); }
 
 // Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200,
@@ -238,14 +267,40 @@ struct FwdState {
   f32x16 oacc[HD / 32];     // O^T accumulator, unscaled
   float m_run;              // reference maximum of the exponentials (log2 units)
   float l_run;              // this lane's share of the row sum against m_run
+  float b_cur;              // log2 offset to add to the stored scores of the tile in s_cur (ALiBi)
 };
+
+// Turn the raw S^T of tile t (first key j0) into stored scores: mask where the tile
+// crosses a mask boundary, add the ALiBi bias (exactly, or split off as a per-lane
+// offset on tiles where it is linear).  Sets `b` to this lane's log2 offset (stored
+// score * cs + b is the score in log2 units) and returns the row max in log2 units.
+template <bool ALIBI>
+__device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, int key_hi, int my_pos, int wl, int wr,
+                                             int i0, int i_last, int off, float c, float cs, float slope, int half) {
+  const bool full = (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
+  b = 0.f;
+  if constexpr (ALIBI) {
+    const bool left = j0 + BC - 1 <= i0 + off;  // every key at or before every row's position
+    const bool right = j0 >= i_last + off;      // every key at or after every row's position
+    if (full && (left || right)) {
+      bias_tile_linear(s, c, slope, right);
+      const float d = slope * (float)(j0 + 8 * half - my_pos);
+      b = right ? -d : d;
+      // the two half-waves hold different keys, so each adds its own offset first
+      return max_with_other_half(lane_max(s) + b);
+    }
+    bias_tile(s, j0, my_pos, c, slope, half);
+  }
+  if (!full) mask_tile(s, j0, key_hi, my_pos, wl, wr, half);
+  return to_log2(tile_max(s), cs);
+}
 
 // LDS buffers of the forward loop, as byte addresses.
 struct LdsBufs {
-  lds_u8* k[2];        // K tile buffers
-  lds_u8* v[2];        // V tile buffers
-  const lds_u8* kl[2]; // this lane's K operand address in each K buffer
-  const lds_u8* vl[2]; // this lane's transpose-read address in each V buffer
+  lds_u8* k[3];        // K tile buffers (NBUF used)
+  lds_u8* v[3];        // V tile buffers
+  const lds_u8* kl[3]; // this lane's K operand address in each K buffer
+  const lds_u8* vl[3]; // this lane's transpose-read address in each V buffer
 };
 
 // One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), loads of
@@ -256,17 +311,20 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
                                           int t_begin, const KVStream<HD>& kv, const LdsBufs& lb, int half,
                                           float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
                                           int i_last, int off) {
-  const int par = (t - t_begin) & 1;
-  // K(t+1) is in k[par^1]; K(t+2) goes to k[par]; V(t) is in v[par]; V(t+1) goes to v[par^1].
-  // Past the last tile these loads read zeros or unused keys: harmless.
-  kv.load_k(lb.k[par], t + 2);
-  kv.load_v(lb.v[par ^ 1], t + 1);
+  constexpr int NB = Tile<HD>::NBUF;
+  // Tile j lives in buffer (j - t_begin) % NB.  This step reads K(t+1) and V(t) and
+  // loads K(t+NB) and V(t+NB-1) into the buffers K(t) and V(t-1) left (both read in
+  // the previous step).  Past the last tile these loads read zeros or unused keys.
+  const int rel = t - t_begin;
+  const int b0 = rel % NB, b1 = (rel + 1) % NB, bm1 = (rel + NB - 1) % NB;
+  kv.load_k(lb.k[b0], t + NB);
+  kv.load_v(lb.v[bm1], t + NB - 1);
 
   // S(t+1) = K(t+1) Q^T
-  qk_tile<HD>(s_nxt, lb.kl[par ^ 1], st.qf);
+  qk_tile<HD>(s_nxt, lb.kl[b1], st.qf);
 
   // P(t) = exp2(S(t) * cs - m), rounded to bf16 for the P V product
-  const float negm = (st.m_run == -INFINITY) ? 0.f : -st.m_run;
+  const float negm = (st.m_run == -INFINITY) ? 0.f : st.b_cur - st.m_run;
   bf16x8 pf[4];
   float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
@@ -292,15 +350,15 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
   for (int ci = 0; ci < 4; ++ci) {
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      const bf16x8 a = v_operand<HD>(lb.vl[par], db, ci);
+      const bf16x8 a = v_operand<HD>(lb.vl[b0], db, ci);
       st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], st.oacc[db], 0, 0, 0);
     }
   }
 
   // max of S(t+1) before masking: exact for tiles every row sees in full
   const int j1 = kv.key_lo + (t + 1) * BC;
-  if constexpr (ALIBI) bias_tile(s_nxt, j1, my_pos, c, slope, half);
-  float mx = tile_max(s_nxt);
+  float mx = 0.f;  // row max of S(t+1) in log2 units
+  if constexpr (!ALIBI) mx = to_log2(tile_max(s_nxt), cs);
 
   // Issue order: the global loads; LDS operand reads running four products ahead;
   // the S(t+1) products, each followed by two exponentials of tile t and their
@@ -358,16 +416,20 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
     }
   }
 
-  // tiles crossing a mask boundary: mask, then take the max again
-  const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
-                        (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
-  if (!nxt_full) {
-    mask_tile(s_nxt, j1, kv.key_hi, my_pos, wl, wr, half);
-    mx = tile_max(s_nxt);
+  // ALiBi tiles, and tiles crossing a mask boundary: bias / mask, then take the max again
+  float b_nxt = 0.f;
+  if constexpr (ALIBI) {
+    mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+  } else {
+    const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
+                          (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
+    if (!nxt_full)
+      mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
   }
+  st.b_cur = b_nxt;  // tile t's offset was used by P(t) above
 
   // move the reference maximum only when a row grew by more than 2^8
-  const float m_new = fmaxf(st.m_run, to_log2(mx, cs));
+  const float m_new = fmaxf(st.m_run, mx);
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > st.m_run + RESCALE_TH) != 0, 0)) {
     // 0 when only m_run is -inf; 1 for a row that has seen no visible key yet
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
@@ -378,15 +440,15 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
       for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
     st.m_run = m_new;
   }
-  wait_tile_loads();  // K(t+2) and V(t+1) are in LDS before anyone passes the barrier
+  // K(t+2) and V(t+1) (loaded NB-2 steps ago) are in LDS before anyone passes the barrier
+  wait_tile_loads<NB == 2 ? 0 : Tile<HD>::LOADS_PER_STEP>();
   __syncthreads();
 }
 
+// One work item: (batch, head, query tile[, key split]) number `item` of `items`.
 template <int HD, bool ALIBI, bool SPLIT>
-__global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int item, int items) {
   using T = Tile<HD>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -394,7 +456,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   const int half = lane >> 5;  // which 8-element k slice this lane feeds
 
   // ---- work item -------------------------------------------------------------
-  int w = xcd_remap(blockIdx.x, gridDim.x);
+  int w = xcd_remap(item, items);
   int qt = w % p.num_q_tiles;
   w /= p.num_q_tiles;
   int split = 0;
@@ -427,9 +489,9 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   LdsBufs lb;
   lds_u8* const lds = (lds_u8*)smem;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < T::NBUF; ++i) {
     lb.k[i] = lds + i * T::KBYTES;
-    lb.v[i] = lds + 2 * T::KBYTES + i * T::VBYTES;
+    lb.v[i] = lds + T::NBUF * T::KBYTES + i * T::VBYTES;
     lb.kl[i] = lb.k[i] + lrow * T::KPITCH + 16 * half;
     lb.vl[i] = lb.v[i] + vt_lane_offset<HD>(lane);
   }
@@ -464,6 +526,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   for (int db = 0; db < HD / 32; ++db) st.oacc[db] = f32x16{};
   st.m_run = -INFINITY;
   st.l_run = 0.f;
+  st.b_cur = 0.f;
   const float c = p.scale_log2;
   float slope = 0.f;
   if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;  // bias in log2 units
@@ -473,17 +536,17 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   f32x16 s_a[2], s_b[2];
 
   if (t_begin < t_end) {
-    // prologue: K and V of the first tile, K of the second, then S of the first
-    kv.load_k(lb.k[0], t_begin);
-    kv.load_v(lb.v[0], t_begin);
-    kv.load_k(lb.k[1], t_begin + 1);  // zeros when past the last key: harmless
-    wait_tile_loads();
+    // prologue: K of the first NBUF tiles and V of the first NBUF-1, then S of the
+    // first (tiles past the last key land as zeros: harmless)
+#pragma unroll
+    for (int j = 0; j < T::NBUF; ++j) kv.load_k(lb.k[j], t_begin + j);
+#pragma unroll
+    for (int j = 0; j + 1 < T::NBUF; ++j) kv.load_v(lb.v[j], t_begin + j);
+    wait_tile_loads<0>();
     __syncthreads();
     qk_tile<HD>(s_a, lb.kl[0], st.qf);
     const int j0 = key_lo + t_begin * BC;
-    if constexpr (ALIBI) bias_tile(s_a, j0, my_pos, c, slope, half);
-    mask_tile(s_a, j0, key_hi, my_pos, wl, wr, half);
-    st.m_run = to_log2(tile_max(s_a), cs);
+    st.m_run = prep_scores<ALIBI>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
 
@@ -502,7 +565,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   const float l_tot = sum_with_other_half(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
-  if (my_q >= Sq) return;
+  if (my_q >= Sq) return;  // this lane's row is past the end: nothing to write
 
   if constexpr (!SPLIT) {
     uint16_t* obase = (uint16_t*)p.out + ((long)b * Sq + my_q) * row_stride + (long)h * HD;
@@ -533,9 +596,19 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p) {
   }
 }
 
+// One workgroup per work item.  (A grid of only the resident workgroups looping
+// over items with a static stride was measured slower: the causal items' unequal
+// lengths then leave CUs idle.)
+template <int HD, bool ALIBI, bool SPLIT>
+__global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p, int items) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD>::LDS_BYTES];
+  fwd_item<HD, ALIBI, SPLIT>(p, smem, blockIdx.x, items);
+}
+
 template <int HD, bool ALIBI, bool SPLIT>
 hipError_t launch_fwd_instance(const FwdParams& p, long nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<HD, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<HD, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p,
+                     (int)nblocks);
   return hipGetLastError();
 }
 
