@@ -392,8 +392,10 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
 #ifndef FA_V2
 #define FA_V2 5
 #endif
+    // LDS operand reads issued ahead of the first product: at headdim 256 only one
+    // wave runs per SIMD, so a deeper queue hides more LDS latency.
 #ifndef FA_PF
-#define FA_PF 2
+    constexpr int FA_PF = HD == 256 ? 12 : 2;
 #endif
 #ifndef FA_VI
 #define FA_VI 0
