@@ -75,7 +75,10 @@ struct Tile {
   // Ring of NBUF K and NBUF V buffers: K runs NBUF tiles ahead of the step that
   // reads it and V NBUF-1, so a tile's loads have NBUF-1 steps to land.  Headdim 64
   // measured slower with three buffers, so every headdim keeps two.
-  static constexpr int NBUF = 2;
+#ifndef FA_NBUF
+#define FA_NBUF 2
+#endif
+  static constexpr int NBUF = HD == 256 ? 2 : FA_NBUF;
   static constexpr int LDS_BYTES = NBUF * (KBYTES + VBYTES);
   // loads one wave issues per step (its vmcnt after a step's loads)
   static constexpr int LOADS_PER_STEP = NWAVES == 4 ? KPW + VPW : KPW;
@@ -343,6 +346,11 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
     }
     pf[ci] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
+  // At headdim 256 (one wave per SIMD) keep the row-sum adds in this block, between
+  // the products; left alone they sink past the masking branch below.  With two
+  // waves per SIMD the sunk adds overlap the other wave's products, which measured
+  // faster at headdim 64 and 128.
+  if constexpr (HD == 256) asm volatile("" : "+v"(lsum0), "+v"(lsum1));
   st.l_run += lsum0 + lsum1;
 
   // O^T += V(t)^T P(t)^T
