@@ -231,14 +231,25 @@ __device__ __forceinline__ void bias_tile_linear(f32x16 (&s)[2], float c, float 
   }
 }
 
-// Set the scores of keys this row may not see to -inf (tiles crossing a mask boundary).
+// Set the scores of keys this row may not see to -inf (tiles crossing a mask
+// boundary).  The row sees the key interval [lo, hi]; element (kb, r) of this lane
+// holds key j0 + 8*half + c with c = 32kb + 16(r/8) + r%8, so visibility is one
+// unsigned compare of (j0 + 8*half - lo) + c against hi - lo.
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int j0, int key_hi, int my_pos, int wl, int wr, int half) {
+  const int lo = wl < 0 ? 0 : max(0, my_pos - wl);
+  const int hi = wr < 0 ? key_hi - 1 : min(key_hi - 1, my_pos + wr);
+  int d = j0 + 8 * half - lo;
+  int span = hi - lo;
+  if (span < 0) {  // nothing visible: every (d + c) must compare above span = 0
+    span = 0;
+    d = -(1 << 20);
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-      const bool vis = key < key_hi && (wl < 0 || key >= my_pos - wl) && (wr < 0 || key <= my_pos + wr);
+      const int cidx = 32 * kb + 16 * (r >> 3) + (r & 7);
+      const bool vis = (uint32_t)(d + cidx) <= (uint32_t)span;
       s[kb][r] = vis ? s[kb][r] : -INFINITY;
     }
   }
