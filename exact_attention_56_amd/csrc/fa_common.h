@@ -15,11 +15,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Matrix-core forward: waves per workgroup (32 query rows each).
-#ifndef FWD_WAVES
-#define FWD_WAVES 4
-#endif
-constexpr int FWD_BLOCK_ROWS = 32 * FWD_WAVES;  // query rows per workgroup
+// Matrix-core forward: query rows per workgroup of the default four-wave launch
+// (the eight-wave launch recounts its 256-row tiles itself).
+constexpr int FWD_BLOCK_ROWS = 128;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -46,11 +46,10 @@
 
 namespace fa {
 
-constexpr int NWAVES = FWD_WAVES;  // waves per workgroup (32 query rows each)
-constexpr int BR = FWD_BLOCK_ROWS;  // query rows per workgroup
-constexpr int BC = 64;              // keys per tile
-constexpr int NTHREADS = 64 * NWAVES;
-static_assert(BR == 32 * NWAVES, "one 32-row query block per wave");
+// A workgroup has NW = 4 or 8 waves of 32 query rows each.  Eight waves (256 rows)
+// halve the K/V traffic from L2 per flop and measured faster for headdim 128
+// without a mask at seqlen_q >= 4096; everything else uses four.
+constexpr int BC = 64;  // keys per tile
 constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: reads as zero
 
@@ -58,8 +57,9 @@ constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: re
 // reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); a V row
 // keeps two pad slots (the 4 rows one transpose read touches land on disjoint
 // 8-bank groups).  Pad slots are filled with zeros by out-of-range loads.
-template <int HD>
+template <int HD, int NW>
 struct Tile {
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static constexpr int CPR = HD / 8;         // 16-byte chunks per K/V row in memory
   static constexpr int KCH = CPR + 1;        // 16-byte slots per K row in LDS
   static constexpr int VCH = CPR + 2;        // 16-byte slots per V row in LDS
@@ -81,8 +81,8 @@ struct Tile {
   static constexpr int NBUF = HD == 256 ? 2 : FA_NBUF;
   static constexpr int LDS_BYTES = NBUF * (KBYTES + VBYTES);
   // loads one wave issues per step (its vmcnt after a step's loads)
-  static constexpr int LOADS_PER_STEP = NWAVES == 4 ? KPW + VPW : KPW;
-  static_assert(NWAVES == 4 || KPW == VPW, "K- and V-loading waves issue equally many loads");
+  static constexpr int LOADS_PER_STEP = NW == 4 ? KPW + VPW : KPW;
+  static_assert(NW == 4 || KPW == VPW, "K- and V-loading waves issue equally many loads");
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -106,9 +106,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
 // slot 64u + l, i.e. row (64u + l) / KCH, slot (64u + l) % KCH; the lane fetches
 // the matching 16 bytes (K rows in the k_lds_row order) or, for a pad slot or a
 // slot past the last row, an out-of-range offset that writes zeros.
-template <int HD>
+template <int HD, int NW>
 struct KVStream {
-  using T = Tile<HD>;
+  using T = Tile<HD, NW>;
   const uint16_t* kbase;
   const uint16_t* vbase;
   int key_lo, key_hi, row_bytes;
@@ -120,8 +120,8 @@ struct KVStream {
 
   __device__ __forceinline__ void init(int wave, int lane) {
     lw = wave & 3;
-    loads_k = NWAVES == 4 || wave < 4;
-    loads_v = NWAVES == 4 || wave >= 4;
+    loads_k = NW == 4 || wave < 4;
+    loads_v = NW == 4 || wave >= 4;
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i) {
       const int slot = 64 * (lw + 4 * i) + lane;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void wait_tile_loads() {
 // `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
 template <int HD>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const bf16x8 (&qf)[HD / 16]) {
-  using T = Tile<HD>;
+  using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   s[0] = f32x16{};
   s[1] = f32x16{};
 #pragma unroll
@@ -184,7 +184,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
 // (see vt_lane_offset); each read returns 4 consecutive keys of one column.
 template <int HD>
 __device__ __forceinline__ bf16x8 v_operand(const lds_u8* vt, int db, int ci) {
-  using T = Tile<HD>;
+  using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + 16 * ci * T::VPITCH + 64 * db));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (16 * ci + 4) * T::VPITCH + 64 * db));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -198,7 +198,7 @@ __device__ __forceinline__ bf16x8 v_operand(const lds_u8* vt, int db, int ci) {
 // columns 16-31 (keys +0..7), 32-47 and 48-63 the same columns for keys +8..15.
 template <int HD>
 __device__ __forceinline__ int vt_lane_offset(int lane) {
-  using T = Tile<HD>;
+  using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   const int g = lane >> 4, r = lane & 15;
   return (8 * (g >> 1) + (r >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
 }
@@ -320,12 +320,13 @@ struct LdsBufs {
 // One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), loads of
 // K(t+2) and V(t+1) into the free buffers, reference-maximum update.  Ends with
 // the tile barrier.
-template <int HD, bool ALIBI>
+template <int HD, int NW, bool ALIBI>
 __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
-                                          int t_begin, const KVStream<HD>& kv, const LdsBufs& lb, int half,
+                                          int t_begin, const KVStream<HD, NW>& kv, const LdsBufs& lb, int half,
                                           float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
                                           int i_last, int off) {
-  constexpr int NB = Tile<HD>::NBUF;
+  using T = Tile<HD, NW>;
+  constexpr int NB = T::NBUF;
   // Tile j lives in buffer (j - t_begin) % NB.  This step reads K(t+1) and V(t) and
   // loads K(t+NB) and V(t+NB-1) into the buffers K(t) and V(t-1) left (both read in
   // the previous step).  Past the last tile these loads read zeros or unused keys.
@@ -388,7 +389,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
 #define FA_SCHED 1
 #endif
   if constexpr (FA_SCHED == 2) {
-    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KPW + Tile<HD>::VPW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, T::LOADS_PER_STEP, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
@@ -419,7 +420,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
 #ifndef FA_VI
 #define FA_VI 0
 #endif
-    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, Tile<HD>::KPW + Tile<HD>::VPW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, T::LOADS_PER_STEP, 0);
     if constexpr (FA_PF > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, FA_PF, 0);
     // exponentials of tile t fill the first LDS latency after the barrier
     if constexpr (FA_VI > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_VI, 0);
@@ -462,14 +463,15 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
     st.m_run = m_new;
   }
   // K(t+2) and V(t+1) (loaded NB-2 steps ago) are in LDS before anyone passes the barrier
-  wait_tile_loads<NB == 2 ? 0 : Tile<HD>::LOADS_PER_STEP>();
+  wait_tile_loads<NB == 2 ? 0 : T::LOADS_PER_STEP>();
   __syncthreads();
 }
 
 // One work item: (batch, head, query tile[, key split]) number `item` of `items`.
-template <int HD, bool ALIBI, bool SPLIT>
+template <int HD, int NW, bool ALIBI, bool SPLIT>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int item, int items) {
-  using T = Tile<HD>;
+  using T = Tile<HD, NW>;
+  constexpr int BR = 32 * NW;  // query rows per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -498,7 +500,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const long row_stride = (long)p.nheads * HD;
   const uint16_t* __restrict__ qbase = p.q + (long)b * Sq * row_stride + (long)h * HD;
 
-  KVStream<HD> kv;
+  KVStream<HD, NW> kv;
   kv.kbase = p.k + (long)b * Sk * row_stride + (long)h * HD;
   kv.vbase = p.v + (long)b * Sk * row_stride + (long)h * HD;
   kv.key_lo = key_lo;
@@ -573,10 +575,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 
   // two tiles per trip so S(t) and S(t+1) swap roles without register copies
   for (int t = t_begin; t < t_end; t += 2) {
-    tile_step<HD, ALIBI>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
+    tile_step<HD, NW, ALIBI>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
     if (t + 1 >= t_end) break;
-    tile_step<HD, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
-                         off);
+    tile_step<HD, NW, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+                             i_last, off);
   }
   f32x16* const oacc = st.oacc;
   const float m_run = st.m_run;
@@ -620,29 +622,45 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 // One workgroup per work item.  (A grid of only the resident workgroups looping
 // over items with a static stride was measured slower: the causal items' unequal
 // lengths then leave CUs idle.)
-template <int HD, bool ALIBI, bool SPLIT>
-__global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdParams p, int items) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD>::LDS_BYTES];
-  fwd_item<HD, ALIBI, SPLIT>(p, smem, blockIdx.x, items);
+template <int HD, int NW, bool ALIBI, bool SPLIT>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p, int items) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD, NW>::LDS_BYTES];
+  fwd_item<HD, NW, ALIBI, SPLIT>(p, smem, blockIdx.x, items);
 }
 
-template <int HD, bool ALIBI, bool SPLIT>
+template <int HD, int NW, bool ALIBI, bool SPLIT>
 hipError_t launch_fwd_instance(const FwdParams& p, long nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<HD, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p,
+  hipLaunchKernelGGL((fwd_kernel<HD, NW, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, p,
                      (int)nblocks);
   return hipGetLastError();
 }
 
+// Eight waves per workgroup for headdim 128 with neither causal mask nor window and
+// at least 4096 query rows; four otherwise.
+inline int fwd_waves(const FwdParams& p, int hd, bool split) {
+  return (hd == 128 && !split && p.window_left < 0 && p.window_right < 0 && p.seqlen_q >= 4096) ? 8 : 4;
+}
+
 // One translation unit per head dimension instantiates these (separate files let
-// each get its own register-allocation flags).
+// each get its own register-allocation flags).  The caller sets num_q_tiles for
+// 128-row tiles; an eight-wave launch recounts them for 256 rows.
 template <int HD>
 hipError_t launch_fwd_hd(const FwdParams& p, bool split, hipStream_t stream) {
-  const long nblocks = (long)p.batch * p.nheads * p.num_q_tiles * (split ? p.num_splits : 1);
   const bool alibi = p.alibi != nullptr;
-  if (split) return alibi ? launch_fwd_instance<HD, true, true>(p, nblocks, stream)
-                          : launch_fwd_instance<HD, false, true>(p, nblocks, stream);
-  return alibi ? launch_fwd_instance<HD, true, false>(p, nblocks, stream)
-               : launch_fwd_instance<HD, false, false>(p, nblocks, stream);
+  if constexpr (HD == 128) {
+    if (fwd_waves(p, HD, split) == 8) {
+      FwdParams p8 = p;
+      p8.num_q_tiles = (p.seqlen_q + 255) / 256;
+      const long nblocks = (long)p8.batch * p8.nheads * p8.num_q_tiles;
+      return alibi ? launch_fwd_instance<HD, 8, true, false>(p8, nblocks, stream)
+                   : launch_fwd_instance<HD, 8, false, false>(p8, nblocks, stream);
+    }
+  }
+  const long nblocks = (long)p.batch * p.nheads * p.num_q_tiles * (split ? p.num_splits : 1);
+  if (split) return alibi ? launch_fwd_instance<HD, 4, true, true>(p, nblocks, stream)
+                          : launch_fwd_instance<HD, 4, false, true>(p, nblocks, stream);
+  return alibi ? launch_fwd_instance<HD, 4, true, false>(p, nblocks, stream)
+               : launch_fwd_instance<HD, 4, false, false>(p, nblocks, stream);
 }
 
 hipError_t launch_fwd_d64(const FwdParams& p, bool split, hipStream_t stream);

@@ -67,6 +67,10 @@ FWD_CASES = [
     (1, 2, 384, 768, 64, False, 100, -1, False, None),
     (1, 2, 96, 1200, 128, True, 700, 0, True, None),
     (1, 2, 1, 700, 128, True, -1, -1, True, None),
+    # headdim 128 without a mask from 4096 query rows on: eight-wave (256-row) workgroups
+    (1, 1, 4096 + 77, 3001, 128, False, -1, -1, False, None),
+    (1, 1, 4352, 4352, 128, False, -1, -1, True, None),
+    (1, 1, 4095, 333, 128, False, -1, -1, False, None),
 ]
 
 
