@@ -10,6 +10,9 @@ Functions
   flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
                   alibi_slopes=None) -> (out, lse)
   fwd(q, k, v, out, lse, ...)                      preallocated outputs
+  flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+                                                   packed sequences, grouped K/V heads
+  fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, ...)
   fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, ...)
   combine(out_partial, lse_partial, out, lse)
   decode(q, k_cache, v_cache, num_splits=16, ...) -> (out, lse)
@@ -48,6 +51,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_combine.restype = i
     lib.fa_status_str.argtypes = [i]
@@ -132,6 +137,50 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, 
     out = torch.empty_like(q)
     lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
     fwd(q, k, v, out, lse, softmax_scale, causal, window_size, alibi_slopes)
+    return out, lse
+
+
+def fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None) -> None:
+    """fa_fwd_varlen on preallocated out [total_q,H,D] bf16 and lse [H,total_q] fp32.
+
+    q [total_q, H, D], k/v [total_k, H_k, D] (H_k divides H), cu_seqlens_* int32 [batch+1]
+    on the same device.  The cumulative lengths are read by the kernel only: they must
+    lie inside the tensors (see fa_fwd_varlen in include/fa.h).
+    """
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k, "k", torch.bfloat16, 3, q.device)
+    _require(v, "v", torch.bfloat16, 3, q.device)
+    _require(out, "out", torch.bfloat16, 3, q.device)
+    _require(lse, "lse", torch.float32, 2, q.device)
+    _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
+    _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, q.device)
+    total_q, h, d = q.shape
+    hk = k.shape[1]
+    if k.shape != v.shape or k.shape[2] != d:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must be [total_k, H_k, {d}]")
+    if hk < 1 or h % hk != 0:
+        raise ValueError(f"K/V heads ({hk}) must divide query heads ({h})")
+    if out.shape != q.shape or tuple(lse.shape) != (h, total_q):
+        raise ValueError("out must match q and lse must be [nheads, total_q]")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [batch + 1]")
+    batch = cu_seqlens_q.shape[0] - 1
+    slopes = _alibi(alibi_slopes, h, q.device)
+    _check(load_library().fa_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), batch, int(max_seqlen_q), int(max_seqlen_k), total_q, h, hk, d,
+        _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes),
+        _stream_handle(q)))
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                           causal=False, window_size=(-1, -1), alibi_slopes=None):
+    """Packed-sequence forward; returns (out [total_q,H,D] bf16, lse [H,total_q] fp32)."""
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+               window_size, alibi_slopes)
     return out, lse
 
 

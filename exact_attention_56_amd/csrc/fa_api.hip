@@ -69,6 +69,10 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
   p->seqlen_q = seqlen_q;
   p->seqlen_k = seqlen_k;
   p->nheads = nheads;
+  p->nheads_k = nheads;
+  p->cu_q = nullptr;
+  p->cu_k = nullptr;
+  p->lse_head_stride = 0;
   // The kernels fold the scale into Q's sign and a positive multiplier: a negative
   // scale negates Q, a zero scale zeroes Q (every score is then exactly 0).
   if (softmax_scale == 0.f) {
@@ -134,6 +138,32 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_parti
     e = fa::launch_fwd(p, headdim, true, stream);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int nheads,
+                  int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
+                  const float* alibi_slopes, hipStream_t stream) {
+  if (!out || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1) return FA_ERR_INVALID_ARG;
+  // The per-sequence lengths live on the device; the maxima size the grid and the
+  // window normalisation.  One padded "batch" of max_seqlen rows is validated in
+  // their place (every sequence is at most that long).
+  fa::FwdParams p;
+  const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, &p);
+  if (st != FA_OK) return st;
+  if (batch < 1 || elems4(total_q, nheads, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
+  p.batch = batch;
+  p.nheads_k = nheads_k;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.lse_head_stride = total_q;
+  p.out = out;
+  p.lse = lse;
+  if (fa::fwd_num_blocks(p, false) > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return fa::launch_fwd(p, headdim, false, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,

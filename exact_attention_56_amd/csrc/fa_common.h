@@ -30,7 +30,11 @@ struct FwdParams {
   void* out;              // bf16 [B, Sq, H, D]  or fp32 [S, B, H, Sq, D] (split mode)
   float* lse;             // fp32 [B, H, Sq]     or fp32 [S, B, H, Sq]    (split mode)
   const float* alibi;     // fp32 [H] ALiBi slopes, or nullptr
-  int batch, seqlen_q, seqlen_k, nheads;
+  int batch, seqlen_q, seqlen_k, nheads;  // varlen: seqlen_q/k are the maximum lengths
+  int nheads_k;           // K/V heads; query head h reads K/V head h / (nheads / nheads_k)
+  const int* cu_q;        // varlen: [batch + 1] first q/out row of each sequence, or nullptr
+  const int* cu_k;        // varlen: [batch + 1] first k/v row of each sequence, or nullptr
+  long lse_head_stride;   // varlen: total_q, lse being [nheads, total_q]
   float scale_log2;       // |softmax_scale| * log2(e), or 1 when softmax_scale == 0
   uint32_t q_and;         // 0 when softmax_scale == 0 (Q is zeroed on load), else all ones
   uint32_t q_sign;        // 0x80008000 when softmax_scale < 0 (Q is negated on load), else 0

@@ -491,22 +491,39 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const int b = w / p.nheads;
   if (p.reverse_q) qt = p.num_q_tiles - 1 - qt;
 
-  const int Sq = p.seqlen_q, Sk = p.seqlen_k;
+  // This sequence's rows: a padded batch has them at b * seqlen; a packed (varlen)
+  // batch lists each sequence's first row in cu_q / cu_k.
+  long q_start, k_start;
+  int Sq, Sk;
+  if (p.cu_q != nullptr) {
+    q_start = p.cu_q[b];
+    Sq = p.cu_q[b + 1] - q_start;
+    k_start = p.cu_k[b];
+    Sk = p.cu_k[b + 1] - k_start;
+    if (qt * BR >= Sq) return;  // the whole workgroup: no row of this tile exists
+  } else {
+    Sq = p.seqlen_q;
+    Sk = p.seqlen_k;
+    q_start = (long)b * Sq;
+    k_start = (long)b * Sk;
+  }
   int key_lo = 0, key_hi = Sk;
   if constexpr (SPLIT) {
     key_lo = min(Sk, split * p.split_len);
     key_hi = min(Sk, key_lo + p.split_len);
   }
-  const long row_stride = (long)p.nheads * HD;
-  const uint16_t* __restrict__ qbase = p.q + (long)b * Sq * row_stride + (long)h * HD;
+  const long row_stride = (long)p.nheads * HD;     // q and out
+  const long kv_stride = (long)p.nheads_k * HD;    // k and v
+  const int hk = h / (p.nheads / p.nheads_k);
+  const uint16_t* __restrict__ qbase = p.q + q_start * row_stride + (long)h * HD;
 
   KVStream<HD, NW> kv;
-  kv.kbase = p.k + (long)b * Sk * row_stride + (long)h * HD;
-  kv.vbase = p.v + (long)b * Sk * row_stride + (long)h * HD;
+  kv.kbase = p.k + k_start * kv_stride + (long)hk * HD;
+  kv.vbase = p.v + k_start * kv_stride + (long)hk * HD;
   kv.key_lo = key_lo;
   kv.key_hi = key_hi;
-  kv.row_stride = (int)row_stride;
-  kv.row_bytes = (int)row_stride * 2;
+  kv.row_stride = (int)kv_stride;
+  kv.row_bytes = (int)kv_stride * 2;
   kv.init(wave, lane);
 
   LdsBufs lb;
@@ -591,7 +608,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   if (my_q >= Sq) return;  // this lane's row is past the end: nothing to write
 
   if constexpr (!SPLIT) {
-    uint16_t* obase = (uint16_t*)p.out + ((long)b * Sq + my_q) * row_stride + (long)h * HD;
+    uint16_t* obase = (uint16_t*)p.out + (q_start + my_q) * row_stride + (long)h * HD;
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
@@ -602,7 +619,11 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
                    pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
         *(u32x2*)(obase + d0) = o;
       }
-    if (half == 0) p.lse[((long)b * p.nheads + h) * Sq + my_q] = lse_v;
+    if (half == 0) {
+      const long li = p.cu_q != nullptr ? (long)h * p.lse_head_stride + q_start + my_q
+                                        : ((long)b * p.nheads + h) * Sq + my_q;
+      p.lse[li] = lse_v;
+    }
   } else {
     const long rowid = (((long)split * p.batch + b) * p.nheads + h) * Sq + my_q;
     float* obase = (float*)p.out + rowid * HD;

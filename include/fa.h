@@ -103,6 +103,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v,
                    const float* alibi_slopes, int num_splits, hipStream_t stream);
 
 /*
+ * fa_fwd_varlen - attention forward over a packed batch of sequences of different
+ * lengths, with grouped K/V heads [FA-overview, "函数重命名" (the variable-length
+ * interface), "代码解读：FlashSelfAttention" (packed rows indexed by cu_seqlens),
+ * "代码解读博客：FlashCrossAttention" (separate cu_seqlens_k / max_seqlen_k, K/V
+ * with their own head count H_k)].
+ *   cu_seqlens_q [batch + 1] int32 (device, read): sequence b owns q/out rows
+ *                [cu_seqlens_q[b], cu_seqlens_q[b+1]); cu_seqlens_q[0] = 0 and the
+ *                array is non-decreasing;
+ *   cu_seqlens_k [batch + 1] int32 (device, read): the same for k/v rows;
+ *   q, out [total_q, nheads, headdim]   bf16 (device), total_q = cu_seqlens_q[batch]
+ *   k, v   [total_k, nheads_k, headdim] bf16 (device), total_k = cu_seqlens_k[batch]
+ *   lse    [nheads, total_q]            fp32 (device, written)
+ *   max_seqlen_q, max_seqlen_k: at least every sequence's length (they size the grid;
+ *                rows of a longer sequence past max_seqlen_q are left unwritten);
+ *   nheads_k: divides nheads; query head h reads K/V head h / (nheads / nheads_k)
+ *             (nheads_k = nheads: ordinary multi-head, 1: a single shared K/V head).
+ * Each sequence is its own attention problem: causal alignment, windows and ALiBi
+ * use that sequence's lengths (query i of sequence b sits at key position
+ * i + Sk_b - Sq_b).  alibi_slopes is indexed by query head.  The cu_seqlens arrays
+ * are read on the device only, so the host cannot check them: they must describe
+ * rows inside q/k/v/out (an invalid array makes the kernel read or write outside
+ * the buffers).  Errors as for fa_fwd, plus FA_ERR_INVALID_ARG for a NULL cu_seqlens
+ * pointer, total_q < 1, nheads_k < 1 or nheads_k not dividing nheads.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int max_seqlen_q,
+                  int max_seqlen_k, int total_q, int nheads, int nheads_k, int headdim,
+                  float softmax_scale, int causal, int window_left, int window_right,
+                  const float* alibi_slopes, hipStream_t stream);
+
+/*
  * fa_combine - second half of the split-KV forward [FA-overview, "2.2"].
  * Per row: L = ln sum_s exp(lse_partial[s]); out = sum_s exp(lse_partial[s] - L) *
  * out_partial[s]; lse = L.  A row where every split is empty gets out = 0, lse = -inf.

@@ -6,5 +6,5 @@ passages of the pages they follow.
 """
 
 from .attention import (alibi_bias, aligned_key_position, as_f64, attention_forward,  # noqa: F401
-                        attention_sampled, brute_force, combine, head_rows, softmax_rows,
+                        attention_sampled, attention_varlen, brute_force, combine, head_rows, softmax_rows,
                         split_bounds, splitkv_partials, visible_mask)

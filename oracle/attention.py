@@ -161,6 +161,41 @@ def attention_forward(q, k, v, softmax_scale: float, causal: bool = False, windo
     return out, lse
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale: float, causal: bool = False,
+                     window_left: int = -1, window_right: int = -1, alibi_slopes=None,
+                     row_chunk: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+    """Packed batch of sequences with grouped K/V heads, fp64.
+
+    [FA-overview §代码解读：FlashSelfAttention, §代码解读博客：FlashCrossAttention,
+    §函数重命名]: sequence b is rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and
+    rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v, and is an attention
+    problem of its own (its own lengths for the causal alignment, windows and ALiBi).
+    K/V carry H_k heads (H_k divides H); query head h reads K/V head h // (H // H_k).
+    q [total_q, H, D], k/v [total_k, H_k, D] -> out [total_q, H, D], lse [H, total_q].
+    """
+    qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
+    total_q, nheads, headdim = qd.shape
+    group = nheads // kd.shape[1]
+    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    out = np.zeros((total_q, nheads, headdim))
+    lse = np.full((nheads, total_q), -np.inf)
+    for b in range(len(cq) - 1):
+        q0, sq = cq[b], cq[b + 1] - cq[b]
+        k0, sk = ck[b], ck[b + 1] - ck[b]
+        for h in range(nheads):
+            kh, vh = kd[k0:k0 + sk, h // group, :], vd[k0:k0 + sk, h // group, :]
+            slope = None if slopes is None else float(slopes[h])
+            for r0 in range(0, sq, row_chunk):
+                rows = np.arange(r0, min(sq, r0 + row_chunk))
+                o, l = head_rows(qd[q0 + rows, h, :], kh, vh, rows, sq, softmax_scale, causal, window_left,
+                                 window_right, slope)
+                out[q0 + rows, h, :] = o
+                lse[h, q0 + rows] = l
+    return out, lse
+
+
 def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_scale: float,
                       causal: bool = False, window_left: int = -1, window_right: int = -1,
                       alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:

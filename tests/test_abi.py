@@ -29,7 +29,7 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_status_str"]
+    assert declared_functions() == ["fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -74,6 +74,24 @@ def test_splitkv_rejects_invalid(lib, over, ns, code):
     a = fwd_args(**over)
     a.insert(15, ns)  # num_splits comes just before the stream
     assert lib.fa_fwd_splitkv(*a) == code
+
+
+def varlen_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, batch=2, max_sq=8, max_sk=8,
+             total_q=10, nheads=4, nheads_k=2, headdim=128, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu_q=None), -1), (dict(cu_k=None), -1), (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(nheads_k=0), -1), (dict(nheads_k=3), -1), (dict(nheads=2, nheads_k=4), -1), (dict(total_q=0), -1),
+    (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(max_sk=-1), -1), (dict(wl=-3), -1),
+    (dict(scale=math.inf), -1), (dict(headdim=80), -2), (dict(nheads=1 << 16, nheads_k=1 << 16), -2),
+])
+def test_varlen_rejects_invalid(lib, over, code):
+    assert lib.fa_fwd_varlen(*varlen_args(**over)) == code
 
 
 @pytest.mark.parametrize("args,code", [

@@ -92,6 +92,47 @@ def test_fwd_matches_oracle(case):
     check_empty_rows_zero(out, ref_lse)
 
 
+VARLEN_CASES = [
+    # lengths of q sequences, lengths of k sequences, H, H_k, d, causal, wl, wr, alibi
+    ((100, 0, 257, 3), (130, 5, 200, 64), 4, 2, 128, True, -1, -1, False),
+    ((1, 129, 64), (300, 129, 0), 2, 1, 64, False, -1, -1, True),
+    ((300, 77), (77, 300), 8, 2, 128, False, 40, 10, True),
+    ((200, 200), (200, 333), 4, 4, 256, True, -1, -1, False),
+    ((520, 1), (700, 1000), 6, 3, 64, True, 100, 0, True),
+    # a sequence of at least 4096 rows without a mask: the eight-wave launch, grouped heads
+    ((4100, 50), (4100, 3000), 2, 1, 128, False, -1, -1, False),
+]
+
+
+def varlen_id(c):
+    lq, lk, h, hk, d, causal, wl, wr, alibi = c
+    return (f"q{'-'.join(map(str, lq))}_k{'-'.join(map(str, lk))}_h{h}kv{hk}_d{d}"
+            f"{'_causal' if causal else ''}_w{wl},{wr}{'_alibi' if alibi else ''}")
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[varlen_id(c) for c in VARLEN_CASES])
+def test_varlen_gqa_matches_oracle(case):
+    lq, lk, h, hk, d, causal, wl, wr, alibi = case
+    announce("varlen " + varlen_id(case))
+    cq = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32)
+    ck = torch.tensor([0] + list(np.cumsum(lk)), dtype=torch.int32)
+    total_q, total_k = int(cq[-1]), int(ck[-1])
+    q, k, v = make_qkv(1, total_q, max(total_k, 1), h, d, seed=total_q * 3 + total_k, nheads_k=hk)
+    q, k, v = q[0], k[0, :total_k], v[0, :total_k]
+    slopes = make_alibi_slopes(h) if alibi else None
+    scale = f32(1.0 / math.sqrt(d))
+    qd, kd, vd = q.to(DEV), k.contiguous().to(DEV), v.contiguous().to(DEV)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((h, total_q), float("nan"), dtype=torch.float32, device=DEV)
+    fa.fwd_varlen(qd, kd, vd, out, lse, cq.to(DEV), ck.to(DEV), max(lq), max(lk), scale, causal, (wl, wr),
+                  None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention_varlen(q, k, v, cq.numpy(), ck.numpy(), scale, causal, wl, wr, slopes)
+    check_lse(lse.cpu(), ref_lse)
+    check_out(out.cpu(), ref_out)
+    check_empty_rows_zero(out.cpu()[None], ref_lse[None])
+
+
 def test_fwd_deterministic():
     announce("determinism b2h4 sq300 sk700 d128 causal alibi")
     q, k, v, slopes = inputs(2, 4, 300, 700, 128, True, seed=11)

@@ -266,6 +266,33 @@ def pin_sampled_rows():
         assert np.allclose(o[n], full[b, i, h], atol=1e-14) and abs(l[n] - full_lse[b, h, i]) < 1e-14
 
 
+def pin_varlen_gqa():
+    """A packed batch with grouped K/V heads equals, sequence by sequence, the scalar
+    brute force on that sequence alone with each K/V head repeated for the query heads
+    of its group (contiguous groups of H / H_k query heads share a K/V head)."""
+    nheads, nheads_k, headdim = 4, 2, 5
+    lens_q, lens_k = [3, 0, 6, 1, 2], [5, 2, 4, 1, 0]  # an empty query and an empty key sequence
+    cq, ck = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    q = rand((cq[-1], nheads, headdim), 40)
+    k, v = rand((ck[-1], nheads_k, headdim), 41), rand((ck[-1], nheads_k, headdim), 42)
+    heads = [0, 0, 1, 1]  # K/V head of each query head
+    slopes = np.array([0.3, 0.1, 0.0, 0.2])
+    for causal, wl, wr, al in [(False, -1, -1, None), (True, -1, -1, None), (True, 2, 0, slopes),
+                               (False, 1, 2, slopes)]:
+        out, lse = oracle.attention_varlen(q, k, v, cq, ck, 0.7, causal, wl, wr, al)
+        assert out.shape == q.shape and lse.shape == (nheads, cq[-1])
+        for b in range(len(lens_q)):
+            if lens_q[b] == 0:
+                continue
+            rq, rk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+            ob, lb = oracle.brute_force(q[None, rq], k[rk][:, heads][None], v[rk][:, heads][None], 0.7, causal,
+                                        wl, wr, al)
+            assert np.allclose(out[rq], ob[0], atol=1e-12)
+            assert np.array_equal(np.isneginf(lse[:, rq]), np.isneginf(lb[0]))
+            fin = np.isfinite(lb[0])
+            assert np.allclose(lse[:, rq][fin], lb[0][fin], atol=1e-12)
+
+
 def pin_bf16_widening():
     """bf16 inputs widen exactly: the oracle sees the very values the GPU gets."""
     t = torch.tensor([1.0, -2.5, 3.140625, 1e-3, 65280.0]).to(torch.bfloat16)
@@ -330,6 +357,10 @@ def test_sampled_rows():
     pin_sampled_rows()
 
 
+def test_varlen_gqa():
+    pin_varlen_gqa()
+
+
 def test_bf16_widening():
     pin_bf16_widening()
 
@@ -350,6 +381,7 @@ def _all_pins():
         pin_brute_force(case)
     pin_invariants()
     pin_split_combine()
+    pin_varlen_gqa()
 
 
 def _top_left(i, seqlen_q, seqlen_k):
@@ -413,7 +445,40 @@ def _head_rows_k_for_v(q_rows, k_head, v_head, *args, **kwargs):
     return _ORIG_HEAD_ROWS(q_rows, k_head, k_head, *args, **kwargs)
 
 
+def _varlen_heads_modulo(q, k, v, cu_q, cu_k, *args, **kwargs):
+    # query head h paired with K/V head h % H_k instead of h // (H / H_k)
+    nheads, nheads_k = q.shape[1], k.shape[1]
+    idx = [h % nheads_k for h in range(nheads)]
+    return _ORIG_VARLEN(q, oa.as_f64(k)[:, idx], oa.as_f64(v)[:, idx], cu_q, cu_k, *args, **kwargs)
+
+
+def _varlen_global_alignment(q, k, v, cu_q, cu_k, softmax_scale, causal=False, window_left=-1, window_right=-1,
+                             alibi_slopes=None, row_chunk=512):
+    # bottom-right alignment taken from the longest sequences instead of each sequence's own lengths
+    cq, ck = np.asarray(cu_q), np.asarray(cu_k)
+    sq_max, sk_max = int(np.diff(cq).max()), int(np.diff(ck).max())
+    qd, kd, vd = oa.as_f64(q), oa.as_f64(k), oa.as_f64(v)
+    out = np.zeros(qd.shape)
+    lse = np.full((qd.shape[1], qd.shape[0]), -np.inf)
+    group = qd.shape[1] // kd.shape[1]
+    for b in range(len(cq) - 1):
+        sq, sk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        for h in range(qd.shape[1]):
+            slope = None if alibi_slopes is None else float(alibi_slopes[h])
+            rows = np.arange(sq) + (sq_max - sq)
+            kh = np.concatenate([np.zeros((sk_max - sk, qd.shape[2])), kd[ck[b]:ck[b + 1], h // group]])
+            vh = np.concatenate([np.zeros((sk_max - sk, qd.shape[2])), vd[ck[b]:ck[b + 1], h // group]])
+            if sq == 0:
+                continue
+            o, l = oa.head_rows(qd[cq[b]:cq[b + 1], h], kh, vh, rows, sq_max, softmax_scale, causal, window_left,
+                                window_right, slope)
+            out[cq[b]:cq[b + 1], h] = o
+            lse[h, cq[b]:cq[b + 1]] = l
+    return out, lse
+
+
 _ORIG_HEAD_ROWS = oa.head_rows
+_ORIG_VARLEN = oa.attention_varlen
 _ORIG_ALIBI = oa.alibi_bias
 _ORIG_SOFTMAX = oa.softmax_rows
 _ORIG_VISIBLE = oa.visible_mask
@@ -429,6 +494,8 @@ _ORIG_COMBINE = oa.combine
     ("combine", _combine_no_weights),
     ("head_rows", _head_rows_bias_scaled),
     ("head_rows", _head_rows_k_for_v),
+    ("attention_varlen", _varlen_heads_modulo),
+    ("attention_varlen", _varlen_global_alignment),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, replacement):
     """Each planted oracle mistake must make at least one pin fail."""
