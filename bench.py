@@ -13,8 +13,9 @@ Printed: ONE JSON line with the contract fields plus
   roofline      the forward kernel: algorithmic FLOPs per launch / mean launch time
                 (HIP events on the launch stream), against the bf16 MFMA peak;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the workload;
-  extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k) and the
-                split-KV decode workload in HBM GB/s.
+  extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k), the
+                split-KV decode workload in HBM GB/s, and a packed batch of causal
+                sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen).
 """
 
 from __future__ import annotations
@@ -34,7 +35,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import exact_attention_56_amd as fa  # noqa: E402
-from exact_attention_56_amd.inputs import WORKLOADS, Workload, make_qkv, sweep_workload  # noqa: E402
+from exact_attention_56_amd.inputs import (VARLEN_GQA, WORKLOADS, Workload, make_qkv,  # noqa: E402
+                                           make_varlen_qkv, sweep_workload)
 
 METRIC = "attention fwd TFLOPS (bf16, 1 MI355X) at hd128 seqlen 2k-16k; % of MFMA peak"
 # MI355X published dense peaks: 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU, and HBM3E 8 TB/s.
@@ -198,6 +200,29 @@ def decode_bench(dev, reps: int, warmup: int):
             "bytes_per_splitkv_launch": partial_bytes}
 
 
+def varlen_bench(dev, reps: int, warmup: int):
+    w = VARLEN_GQA
+    q, k, v, cu = make_varlen_qkv(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.nheads, q.shape[0], dtype=torch.float32, device=dev)
+    mx = max(w.lengths)
+
+    def launch():
+        fa.fwd_varlen(q, k, v, out, lse, cu, cu, mx, mx, w.softmax_scale, w.causal)
+
+    for _ in range(warmup):
+        launch()
+    mean_ms, min_ms = time_events(launch, reps)
+    # causal square sequences: S (S + 1) / 2 visible pairs, 4 * headdim flop per pair and head
+    flops = sum(s * (s + 1) // 2 for s in w.lengths) * w.nheads * 4 * w.headdim
+    tf = flops / (mean_ms * 1e-3) / 1e12
+    return {"workload": f"{w.name}: {len(w.lengths)} sequences ({sum(w.lengths)} tokens, lengths "
+                        f"{min(w.lengths)}..{mx}), {w.nheads} query heads over {w.nheads_k} K/V heads x "
+                        f"{w.headdim}, causal",
+            "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4), "algorithmic_gflop": round(flops / 1e9, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,11 +313,12 @@ def main():
                    "headdim": base.headdim, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "fa::fwd_kernel<128,false,false>", "per_launch": per_case},
+                     "kernel": "fa::fwd_kernel<128,4,false,false>", "per_launch": per_case},
     }
     if not args.no_extra:
         result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
-                           "decode": decode_bench(dev, reps=20, warmup=3)}
+                           "decode": decode_bench(dev, reps=20, warmup=3),
+                           "varlen_gqa": varlen_bench(dev, reps=10, warmup=3)}
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

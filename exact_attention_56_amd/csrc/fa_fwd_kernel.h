@@ -479,6 +479,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const int half = lane >> 5;  // which 8-element k slice this lane feeds
 
   // ---- work item -------------------------------------------------------------
+  // Items run query tile fastest, then key split, batch, and head slowest.  Each XCD
+  // takes a contiguous range of items (xcd_remap), i.e. a slice of the heads over
+  // every sequence of the batch: the XCDs then get equal work even when sequences
+  // differ in length, and the query heads that share a K/V head stay on one XCD.
   int w = xcd_remap(item, items);
   int qt = w % p.num_q_tiles;
   w /= p.num_q_tiles;
@@ -487,8 +491,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     split = w % p.num_splits;
     w /= p.num_splits;
   }
-  const int h = w % p.nheads;
-  const int b = w / p.nheads;
+  const int b = w % p.batch;
+  const int h = w / p.batch;
   if (p.reverse_q) qt = p.num_q_tiles - 1 - qt;
 
   // This sequence's rows: a padded batch has them at b * seqlen; a packed (varlen)

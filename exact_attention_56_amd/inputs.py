@@ -94,3 +94,47 @@ def workload_inputs(w: Workload):
     q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed)
     slopes = make_alibi_slopes(w.nheads) if w.alibi else None
     return q, k, v, slopes
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of sequences (self-attention, q and k share the lengths) with
+    grouped K/V heads."""
+
+    name: str
+    lengths: tuple
+    nheads: int
+    nheads_k: int
+    headdim: int
+    causal: bool = True
+    seed: int = 6
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.headdim), dtype=torch.float32))
+
+
+def varlen_lengths(count: int, lo: int, hi: int, seed: int) -> tuple:
+    """`count` sequence lengths drawn uniformly from [lo, hi] by a seeded generator."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (count,), generator=g))
+
+
+# 16 sequences of 256..4096 tokens, 32 query heads sharing 8 K/V heads, headdim 128, causal.
+VARLEN_GQA = VarlenWorkload("varlen_gqa_causal", varlen_lengths(16, 256, 4096, seed=6), 32, 8, 128)
+
+
+def make_varlen_qkv(w: VarlenWorkload, device: str = "cpu"):
+    """q [total, H, D], k and v [total, H_k, D] bf16 (same recipe as make_qkv, drawn
+    as one long sequence) and cu_seqlens int32 [len(lengths) + 1]."""
+    total = sum(w.lengths)
+    q, k, v = make_qkv(1, total, total, w.nheads, w.headdim, w.seed, nheads_k=w.nheads_k, device=device)
+    cu = torch.tensor([0] + list(_cumsum(w.lengths)), dtype=torch.int32, device=device)
+    return q[0], k[0], v[0], cu
+
+
+def _cumsum(xs):
+    s = 0
+    for x in xs:
+        s += x
+        yield s
