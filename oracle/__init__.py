@@ -1,10 +1,10 @@
-"""fp64 CPU oracle for the attention forward pass: TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for attention (forward and backward): TEST INFRASTRUCTURE ONLY.
 
 Imported by the tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the GPU library.  See oracle/attention.py for the definitions and the
 passages of the pages they follow.
 """
 
-from .attention import (alibi_bias, aligned_key_position, as_f64, attention_forward,  # noqa: F401
-                        attention_sampled, attention_varlen, brute_force, combine, head_rows, softmax_rows,
-                        split_bounds, splitkv_partials, visible_mask)
+from .attention import (alibi_bias, aligned_key_position, as_f64, attention_backward,  # noqa: F401
+                        attention_forward, attention_sampled, attention_varlen, brute_force, combine,
+                        head_rows, softmax_rows, split_bounds, splitkv_partials, visible_mask)

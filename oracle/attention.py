@@ -16,6 +16,7 @@ Sources (the pages are web articles; each is cited by title and section):
       -slope * |i - j| to the score of query i and key j.
     - section "算法 / 前向传播": the forward also writes the row-wise
       logsumexp L, which the backward uses.
+    - section "算法 / 反向传播": the backward recomputes P from L alone.
     - section "2.1：更改causal标志的行为": when seqlen_q != seqlen_k the causal
       mask is aligned to the bottom-right corner of the score matrix (2x5 example).
       A mask row with no kept entry gives a zero output row.
@@ -194,6 +195,41 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale: float, 
                 out[q0 + rows, h, :] = o
                 lse[h, q0 + rows] = l
     return out, lse
+
+
+def attention_backward(q, k, v, dout, softmax_scale: float, causal: bool = False, window_left: int = -1,
+                       window_right: int = -1, alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Exact gradients of out = attention(q, k, v) for an upstream gradient dout, fp64.
+
+    [FA-overview §算法 / 反向传播]: the backward needs only the row-wise logsumexp L of
+    the forward; P is recomputed as exp(S - L).  Per (batch, head), with S the scaled
+    and biased scores and P = exp(S - L) on the visible pairs (0 elsewhere):
+      dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij (= dO_i . O_i),
+      dS = P o (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+    The bias (mask, ALiBi) is a constant: it has no gradient here.
+    q [B,Sq,H,D], k/v [B,Sk,H,D], dout [B,Sq,H,D] -> dq, dk, dv with the shapes of q, k, v.
+    """
+    qd, kd, vd, gd = as_f64(q), as_f64(k), as_f64(v), as_f64(dout)
+    batch, seqlen_q, nheads, headdim = qd.shape
+    seqlen_k = kd.shape[1]
+    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    dq, dk, dv = np.zeros(qd.shape), np.zeros(kd.shape), np.zeros(vd.shape)
+    rows = np.arange(seqlen_q)
+    keep = visible_mask(seqlen_q, seqlen_k, causal, window_left, window_right, rows)
+    for b in range(batch):
+        for h in range(nheads):
+            qh, kh, vh, gh = qd[b, :, h], kd[b, :, h], vd[b, :, h], gd[b, :, h]
+            scores = softmax_scale * (qh @ kh.T)
+            if slopes is not None:
+                scores = scores + alibi_bias(float(slopes[h]), seqlen_q, seqlen_k, rows)
+            p, _ = softmax_rows(scores, keep)
+            dv[b, :, h] = p.T @ gh
+            dp = gh @ vh.T
+            d_row = np.sum(p * dp, axis=1)
+            ds = p * (dp - d_row[:, None])
+            dq[b, :, h] = softmax_scale * (ds @ kh)
+            dk[b, :, h] = softmax_scale * (ds.T @ qh)
+    return dq, dk, dv
 
 
 def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_scale: float,

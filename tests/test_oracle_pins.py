@@ -293,6 +293,74 @@ def pin_varlen_gqa():
             assert np.allclose(lse[:, rq][fin], lb[0][fin], atol=1e-12)
 
 
+BWD_MODES = [(False, -1, -1, None), (True, -1, -1, None), (True, 2, 0, [0.3, 0.05]), (False, 1, 2, [0.2, 0.7]),
+             (False, -1, -1, [0.4, 0.0])]
+
+
+def _loss(q, k, v, dout, scale, causal, wl, wr, al):
+    out, _ = oracle.attention_forward(q, k, v, scale, causal, wl, wr, None if al is None else np.array(al))
+    return float(np.sum(out * dout))
+
+
+def pin_backward_finite_differences():
+    """Every element of dq, dk, dv equals the central difference of sum(dout * out) with
+    out from the (separately pinned) forward, in every mask mode; Sq > Sk leaves rows
+    with no visible key under the causal mask."""
+    eps = 1e-6
+    for shape_q, shape_k in [((1, 4, 2, 3), (1, 6, 2, 3)), ((1, 5, 2, 3), (1, 3, 2, 3))]:
+        q, k, v = rand(shape_q, 50), rand(shape_k, 51), rand(shape_k, 52)
+        dout = rand(shape_q, 53)
+        for causal, wl, wr, al in BWD_MODES:
+            dq, dk, dv = oracle.attention_backward(q, k, v, dout, 0.6, causal, wl, wr,
+                                                   None if al is None else np.array(al))
+            for x, g in ((q, dq), (k, dk), (v, dv)):
+                for idx in np.ndindex(*x.shape):
+                    old = x[idx]
+                    x[idx] = old + eps
+                    up = _loss(q, k, v, dout, 0.6, causal, wl, wr, al)
+                    x[idx] = old - eps
+                    dn = _loss(q, k, v, dout, 0.6, causal, wl, wr, al)
+                    x[idx] = old
+                    fd = (up - dn) / (2 * eps)
+                    assert abs(fd - g[idx]) <= 1e-7 * (1 + abs(fd)), (idx, fd, g[idx])
+
+
+def pin_backward_autograd():
+    """Square problems without window or ALiBi: torch autograd through
+    scaled_dot_product_attention in fp64 on the CPU."""
+    for causal in (False, True):
+        q, k, v = (torch.tensor(rand((2, 3, 7, 5), s), requires_grad=True) for s in (54, 55, 56))
+        dout = torch.tensor(rand((2, 3, 7, 5), 57))
+        out = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=0.45)
+        out.backward(dout)
+        tr = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)  # [B,H,S,D] -> [B,S,H,D]
+        dq, dk, dv = oracle.attention_backward(tr(q), tr(k), tr(v), tr(dout), 0.45, causal)
+        assert np.allclose(dq, tr(q.grad), atol=1e-12)
+        assert np.allclose(dk, tr(k.grad), atol=1e-12)
+        assert np.allclose(dv, tr(v.grad), atol=1e-12)
+
+
+def pin_backward_closed_forms():
+    """Rows of dS sum to zero, so the key gradients of every (batch, head) sum to zero;
+    rows of P sum to one, so dV sums to the upstream gradient of the non-empty rows;
+    scale 0 gives dq = dk = 0 and dv_j = sum over rows seeing j of dout_i / |visible_i|;
+    rows with no visible key get dq = 0."""
+    q, k, v, dout = rand((2, 6, 2, 4), 58), rand((2, 4, 2, 4), 59), rand((2, 4, 2, 4), 60), rand((2, 6, 2, 4), 61)
+    for causal, wl, wr, al in BWD_MODES:
+        al = None if al is None else np.array(al)
+        dq, dk, dv = oracle.attention_backward(q, k, v, dout, 0.9, causal, wl, wr, al)
+        keep = oracle.visible_mask(6, 4, causal, wl, wr)
+        nonempty = keep.any(axis=1)
+        assert np.allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+        assert np.allclose(dv.sum(axis=1), dout[:, nonempty].sum(axis=1), atol=1e-12)
+        assert np.all(dq[:, ~nonempty] == 0)
+        dq0, dk0, dv0 = oracle.attention_backward(q, k, v, dout, 0.0, causal, wl, wr)
+        assert np.all(dq0 == 0) and np.all(dk0 == 0)
+        cnt = np.maximum(keep.sum(axis=1), 1)
+        expect = np.einsum("ij,bihd->bjhd", keep / cnt[:, None], dout)
+        assert np.allclose(dv0, expect, atol=1e-13)
+
+
 def pin_bf16_widening():
     """bf16 inputs widen exactly: the oracle sees the very values the GPU gets."""
     t = torch.tensor([1.0, -2.5, 3.140625, 1e-3, 65280.0]).to(torch.bfloat16)
@@ -361,6 +429,18 @@ def test_varlen_gqa():
     pin_varlen_gqa()
 
 
+def test_backward_finite_differences():
+    pin_backward_finite_differences()
+
+
+def test_backward_autograd():
+    pin_backward_autograd()
+
+
+def test_backward_closed_forms():
+    pin_backward_closed_forms()
+
+
 def test_bf16_widening():
     pin_bf16_widening()
 
@@ -382,6 +462,8 @@ def _all_pins():
     pin_invariants()
     pin_split_combine()
     pin_varlen_gqa()
+    pin_backward_autograd()
+    pin_backward_closed_forms()
 
 
 def _top_left(i, seqlen_q, seqlen_k):
@@ -477,6 +559,27 @@ def _varlen_global_alignment(q, k, v, cu_q, cu_k, softmax_scale, causal=False, w
     return out, lse
 
 
+def _bwd_variant(drop_delta=False, unscaled_dk=False, dv_from_dp=False):
+    def bwd(q, k, v, dout, softmax_scale, causal=False, window_left=-1, window_right=-1, alibi_slopes=None):
+        qd, kd, vd, gd = oa.as_f64(q), oa.as_f64(k), oa.as_f64(v), oa.as_f64(dout)
+        dq, dk, dv = np.zeros(qd.shape), np.zeros(kd.shape), np.zeros(vd.shape)
+        sq, sk = qd.shape[1], kd.shape[1]
+        keep = oa.visible_mask(sq, sk, causal, window_left, window_right)
+        for b in range(qd.shape[0]):
+            for h in range(qd.shape[2]):
+                sc = softmax_scale * (qd[b, :, h] @ kd[b, :, h].T)
+                if alibi_slopes is not None:
+                    sc = sc + oa.alibi_bias(float(alibi_slopes[h]), sq, sk)
+                p, _ = oa.softmax_rows(sc, keep)
+                dp = gd[b, :, h] @ vd[b, :, h].T
+                dv[b, :, h] = (dp if dv_from_dp else p).T @ gd[b, :, h]
+                ds = p * dp if drop_delta else p * (dp - np.sum(p * dp, axis=1)[:, None])
+                dq[b, :, h] = softmax_scale * (ds @ kd[b, :, h])
+                dk[b, :, h] = (1.0 if unscaled_dk else softmax_scale) * (ds.T @ qd[b, :, h])
+        return dq, dk, dv
+    return bwd
+
+
 _ORIG_HEAD_ROWS = oa.head_rows
 _ORIG_VARLEN = oa.attention_varlen
 _ORIG_ALIBI = oa.alibi_bias
@@ -496,6 +599,9 @@ _ORIG_COMBINE = oa.combine
     ("head_rows", _head_rows_k_for_v),
     ("attention_varlen", _varlen_heads_modulo),
     ("attention_varlen", _varlen_global_alignment),
+    ("attention_backward", _bwd_variant(drop_delta=True)),
+    ("attention_backward", _bwd_variant(unscaled_dk=True)),
+    ("attention_backward", _bwd_variant(dv_from_dp=True)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, replacement):
     """Each planted oracle mistake must make at least one pin fail."""
