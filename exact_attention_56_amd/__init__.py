@@ -16,6 +16,8 @@ Functions
   fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, ...)
   combine(out_partial, lse_partial, out, lse)
   decode(q, k_cache, v_cache, num_splits=16, ...) -> (out, lse)
+  bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, ...)   gradients into preallocated tensors
+  attention_backward(q, k, v, out, lse, dout, ...) -> (dq, dk, dv)
 """
 
 from __future__ import annotations
@@ -53,6 +55,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
+    lib.fa_bwd.restype = i
     lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_combine.restype = i
     lib.fa_status_str.argtypes = [i]
@@ -223,3 +227,32 @@ def decode(q, k_cache, v_cache, num_splits=16, softmax_scale=None, causal=False,
     lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
     combine(op, lp, out, lse)
     return out, lse
+
+
+def bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, softmax_scale=None, causal=False, window_size=(-1, -1),
+        alibi_slopes=None) -> None:
+    """fa_bwd: gradients into preallocated dq/dk/dv (bf16, shapes of q/k/v); delta [B,H,Sq]
+    fp32 is scratch.  out and lse must be the forward's outputs for the same arguments."""
+    b, sq, sk, h, d = _check_qkv(q, k, v)
+    for t, name, like in ((out, "out", q), (dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, name, torch.bfloat16, 4, q.device)
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+    _require(lse, "lse", torch.float32, 3, q.device)
+    _require(delta, "delta", torch.float32, 3, q.device)
+    if tuple(lse.shape) != (b, h, sq) or tuple(delta.shape) != (b, h, sq):
+        raise ValueError("lse and delta must be [batch, nheads, seqlen_q]")
+    slopes = _alibi(alibi_slopes, h, q.device)
+    _check(load_library().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), b, sq, sk, h, d, _scale(softmax_scale, d),
+        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), _stream_handle(q)))
+
+
+def attention_backward(q, k, v, out, lse, dout, softmax_scale=None, causal=False, window_size=(-1, -1),
+                       alibi_slopes=None):
+    """Gradients (dq, dk, dv) of flash_attn_func's out for the upstream gradient dout."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device)
+    bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, softmax_scale, causal, window_size, alibi_slopes)
+    return dq, dk, dv

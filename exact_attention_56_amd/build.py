@@ -27,6 +27,10 @@ SOURCES = [
     ("fa_fwd_d128.hip", VGPR_FORM),
     ("fa_fwd_d256.hip", []),
     ("fa_fwd_launch.hip", []),
+    # backward: the dQ pass keeps its accumulators in arch VGPRs (two waves per SIMD);
+    # the dK/dV pass holds two accumulators per wave and uses the accumulation registers
+    ("fa_bwd_dq.hip", VGPR_FORM),
+    ("fa_bwd.hip", []),
     ("fa_decode_kernel.hip", []),
     ("fa_api.hip", []),
 ]

@@ -7,7 +7,7 @@
 #include <stdint.h>
 
 #include "fa.h"
-#include "fa_common.h"
+#include "fa_bwd_kernel.h"
 
 namespace fa {
 hipError_t launch_fwd(const FwdParams& p, int headdim, bool split, hipStream_t stream);
@@ -164,6 +164,48 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
   if (fa::fwd_num_blocks(p, false) > kMaxBlocks) return FA_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return fa::launch_fwd(p, headdim, false, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int batch, int seqlen_q, int seqlen_k, int nheads,
+           int headdim, float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, hipStream_t stream) {
+  if (!out || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+  fa::FwdParams f;  // the forward's validation and window normalisation
+  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, &f);
+  if (st != FA_OK) return st;
+  if (headdim != 64 && headdim != 128) return FA_ERR_UNSUPPORTED;
+  fa::BwdParams p;
+  p.q = f.q;
+  p.k = f.k;
+  p.v = f.v;
+  p.out = (const uint16_t*)out;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.alibi = alibi_slopes;
+  p.batch = batch;
+  p.seqlen_q = seqlen_q;
+  p.seqlen_k = seqlen_k;
+  p.nheads = nheads;
+  p.scale = softmax_scale;
+  p.scale_log2 = f.scale_log2;
+  p.q_and = f.q_and;
+  p.q_sign = f.q_sign;
+  p.window_left = f.window_left;
+  p.window_right = f.window_right;
+  p.num_q_tiles = (seqlen_q + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
+  p.num_k_tiles = (seqlen_k + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
+  const long rows = (long)batch * seqlen_q * nheads;
+  if ((long)batch * nheads * p.num_q_tiles > kMaxBlocks || (long)batch * nheads * p.num_k_tiles > kMaxBlocks ||
+      rows / 16 + 1 > kMaxBlocks)
+    return FA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return fa::launch_bwd(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,

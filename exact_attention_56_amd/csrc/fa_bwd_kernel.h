@@ -1,0 +1,516 @@
+// fa_bwd_kernel.h - matrix-core (MFMA) attention backward for gfx950 (kernel templates;
+// fa_bwd.hip instantiates them).
+//
+// What it computes, per (batch, head), for the visible (query i, key j) pairs:
+//   P_ij = exp(scale * q_i.k_j + bias_ij - L_i)       (L = the forward's logsumexp)
+//   dV_j = sum_i P_ij dO_i,          dP_ij = dO_i . v_j,
+//   D_i  = dO_i . O_i,               dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i = scale * sum_j dS_ij k_j,  dK_j  = scale * sum_i dS_ij q_i,
+// following the page "FlashAttention：快速且内存高效的准确注意力机制"
+// (cloud.tencent.com.cn/developer/article/2433927), sections "算法 / 反向传播" (P is
+// recomputed from the row-wise logsumexp alone, same tiling as the forward) and
+// "并行性 / 反向传播" (one block per column block of K and V).
+//
+// Design for CDNA4:
+//  * three kernels: delta_kernel (D = rowsum(dO o O), fp32), dkdv_kernel (one
+//    workgroup per 128 keys of a (batch, head): K and V of its keys stay in registers
+//    while 32-query tiles of Q, dO, L, D stream through LDS) and dq_kernel (one
+//    workgroup per 128 queries: Q and dO stay in registers while 64-key tiles of K and
+//    V stream through LDS).  dQ gets its own pass instead of atomic adds from the
+//    key-block workgroups: every output element is written once, so the results are
+//    deterministic, and no fp32 accumulation buffer is needed;
+//  * all products are v_mfma_f32_32x32x16_bf16 with transposed outputs where that
+//    keeps row statistics lane-local: the dq kernel holds S^T, dP^T (lane = query),
+//    the dkdv kernel S, dP (lane = key);
+//  * an accumulator whose rows are the contraction index of the next product is
+//    used directly as that product's B operand (rounded to bf16): the A operand of
+//    the first product reads LDS rows with bits 2 and 3 of the row index swapped,
+//    which puts 8 consecutive rows in each lane's registers;
+//  * the streamed tiles stay in their natural row order in LDS: the same tile
+//    serves the row reads (ds_read_b128, permuted rows) and the transposed reads
+//    (ds_read_b64_tr_b16) of the second product.
+#pragma once
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+
+// Backward problem description, filled on the host.  Sizes are in elements.
+struct BwdParams {
+  const uint16_t* q;      // bf16 [B, Sq, H, D]
+  const uint16_t* k;      // bf16 [B, Sk, H, D]
+  const uint16_t* v;      // bf16 [B, Sk, H, D]
+  const uint16_t* out;    // bf16 [B, Sq, H, D]  forward output
+  const uint16_t* dout;   // bf16 [B, Sq, H, D]  upstream gradient
+  const float* lse;       // fp32 [B, H, Sq]     forward logsumexp (natural log)
+  float* delta;           // fp32 [B, H, Sq]     D, written by delta_kernel
+  uint16_t* dq;           // bf16 [B, Sq, H, D]
+  uint16_t* dk;           // bf16 [B, Sk, H, D]
+  uint16_t* dv;           // bf16 [B, Sk, H, D]
+  const float* alibi;     // fp32 [H] or nullptr
+  int batch, seqlen_q, seqlen_k, nheads;
+  float scale;            // softmax_scale as given
+  float scale_log2;       // |scale| * log2(e), or 1 when scale == 0
+  uint32_t q_and;         // 0 when scale == 0 (the scores are then the bias alone)
+  uint32_t q_sign;        // 0x80008000 when scale < 0, else 0
+  int window_left, window_right;  // -1 = unbounded; window_right already 0 when causal
+  int num_q_tiles;        // ceil(Sq / 128): dq workgroups per (batch, head)
+  int num_k_tiles;        // ceil(Sk / 128): dkdv workgroups per (batch, head)
+};
+
+constexpr int BWD_NW = 4;        // waves per workgroup
+constexpr int BWD_ROWS = 128;    // rows (queries or keys) a workgroup owns: 32 per wave
+constexpr int DQ_TILE = 64;      // keys per streamed tile (dq kernel)
+constexpr int DKV_TILE = 32;     // queries per streamed tile (dkdv kernel)
+
+// Two bf16 [rows][row_stride] tensors streamed tile by tile (ROWS rows) into LDS in
+// natural row order, rows SA (SB) 16-byte slots apart; direct-to-LDS buffer loads,
+// rows past `hi` and pad slots land as zeros.  Load u of a tile (wave u % NW issues
+// it) fills LDS bytes [1024u, 1024u + 1024).
+template <int HD, int ROWS, int SA, int SB>
+struct PairStream {
+  static constexpr int CPR = HD / 8;
+  static constexpr int LA = (ROWS * SA + 63) / 64, LB = (ROWS * SB + 63) / 64;
+  static constexpr int PWA = (LA + BWD_NW - 1) / BWD_NW, PWB = (LB + BWD_NW - 1) / BWD_NW;
+  static constexpr int ABYTES = 1024 * BWD_NW * PWA, BBYTES = 1024 * BWD_NW * PWB;
+  static_assert(SA >= CPR && SB >= CPR, "a row holds its chunks");
+  const uint16_t* abase;
+  const uint16_t* bbase;
+  int lo, hi, row_stride, row_bytes, lw;
+  uint32_t aoff[PWA], boff[PWB];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    lw = wave;
+#pragma unroll
+    for (int i = 0; i < PWA; ++i) {
+      const int slot = 64 * (lw + BWD_NW * i) + lane;
+      const int row = slot / SA, ch = slot % SA;
+      aoff[i] = (row < ROWS && ch < CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
+    }
+#pragma unroll
+    for (int i = 0; i < PWB; ++i) {
+      const int slot = 64 * (lw + BWD_NW * i) + lane;
+      const int row = slot / SB, ch = slot % SB;
+      boff[i] = (row < ROWS && ch < CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
+    }
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* base, int t) const {
+    const int j0 = lo + t * ROWS;
+    const int rows = hi - j0;
+    const int n = rows > 0 ? min(rows, ROWS) * row_bytes : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)j0 * row_stride), (short)0, n, 0x00020000);
+  }
+  __device__ __forceinline__ void load(lds_u8* dsta, lds_u8* dstb, int t) const {
+    const auto ra = rsrc(abase, t);
+#pragma unroll
+    for (int i = 0; i < PWA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dsta + 1024 * (lw + BWD_NW * i), 16, (int)aoff[i], 0, 0, 0);
+    const auto rb = rsrc(bbase, t);
+#pragma unroll
+    for (int i = 0; i < PWB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dstb + 1024 * (lw + BWD_NW * i), 16, (int)boff[i], 0, 0, 0);
+  }
+};
+
+// A operand (32 rows x 16 columns) read from a row-major LDS tile: lane l takes row
+// k_lds_row(l % 32) + 32 blk, 16 bytes at column 16 kk + 8 (l / 32).
+template <int PITCH>
+__device__ __forceinline__ bf16x8 row_operand(const lds_u8* tile, int lrow, int half, int blk, int kk) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(tile + (k_lds_row(lrow) + 32 * blk) * PITCH +
+                                                             32 * kk + 16 * half);
+}
+
+// A operand of a transposed product: X^T[d][rows 16 ci + 8 (l / 32) + 0..7] for
+// d = 32 db + l % 32, from a row-major LDS tile (two transpose reads; see
+// vt_lane_offset for the lane pattern, here with any row pitch).
+template <int PITCH>
+__device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, int lane, int db, int ci) {
+  const int g = lane >> 4, r = lane & 15;
+  const lds_u8* p = tile + (8 * (g >> 1) + (r >> 2)) * PITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * ci * PITCH + 64 * db));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (16 * ci + 4) * PITCH + 64 * db));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 16 bytes of row `row` of a [rows][row_stride] bf16 tensor as a B operand (8
+// consecutive columns starting at 16 kk + 8 half), zero past the last row.
+__device__ __forceinline__ bf16x8 row_fragment(const uint16_t* base, long row_stride, int row, int nrows, int kk,
+                                               int half, uint32_t and_mask, uint32_t xor_mask) {
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (row < nrows) raw = *(const u32x4*)(base + (long)row * row_stride + 16 * kk + 8 * half);
+  raw = (raw & and_mask) ^ xor_mask;
+  return __builtin_bit_cast(bf16x8, raw);
+}
+
+// Pack register pairs (2e, 2e+1) of 8 consecutive accumulator rows r0..r0+7 into the
+// bf16 B operand of the next product.
+__device__ __forceinline__ bf16x8 pack_rows(const f32x16& x, int r0) {
+  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[r0], x[r0 + 1]), pack_bf16x2(x[r0 + 2], x[r0 + 3]),
+                                          pack_bf16x2(x[r0 + 4], x[r0 + 5]), pack_bf16x2(x[r0 + 6], x[r0 + 7])});
+}
+
+// Store a transposed accumulator X^T [HD rows (d) x 32 columns] of this wave as bf16
+// row `row` (the lane's column) of a [rows][row_stride] tensor, times `mul`.
+template <int HD>
+__device__ __forceinline__ void store_rows_bf16(uint16_t* base, long row_stride, int row, const f32x16 (&x)[HD / 32],
+                                                float mul, int half) {
+  uint16_t* o = base + (long)row * row_stride;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // accumulator rows 4g..4g+3 of block db hold columns 32db + 8g + 4*half + 0..3
+      const int d0 = 32 * db + 8 * g + 4 * half;
+      u32x2 w = {pack_bf16x2(x[db][4 * g] * mul, x[db][4 * g + 1] * mul),
+                 pack_bf16x2(x[db][4 * g + 2] * mul, x[db][4 * g + 3] * mul)};
+      *(u32x2*)(o + d0) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// delta_kernel: D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32.  One
+// wave per 8 rows; HD/8 lanes per row, 16 bytes each, then a lane-group sum.
+template <int HD>
+__global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
+  constexpr int LPR = HD / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;     // rows per wave
+  const int lane = threadIdx.x & 63;
+  const long row = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;  // row = (b*Sq + i)*H + h
+  const int c = lane % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *(const u32x4*)(p.out + row * HD + 8 * c);
+    const u32x4 g = *(const u32x4*)(p.dout + row * HD + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += __uint_as_float(o[e] << 16) * __uint_as_float(g[e] << 16);
+      acc += __uint_as_float(o[e] & 0xffff0000u) * __uint_as_float(g[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s, 64);
+  if (row < rows && c == 0) {
+    const int h = (int)(row % p.nheads);
+    const long bi = row / p.nheads;  // b * Sq + i
+    const int i = (int)(bi % p.seqlen_q);
+    const int b = (int)(bi / p.seqlen_q);
+    p.delta[((long)b * p.nheads + h) * p.seqlen_q + i] = acc;
+  }
+#endif
+}
+
+// Bias in log2 units of query i and key j (ALiBi), or 0.
+__device__ __forceinline__ float alibi_log2(float slope_log2, int pos_i, int key) {
+  return -slope_log2 * fabsf((float)(pos_i - key));
+}
+
+// ---------------------------------------------------------------------------------
+// dq_kernel: one workgroup per (batch, head, 128 queries); wave w owns queries
+// i0 + 32 w + 0..31.  Per 64-key tile t:
+//   S^T = K Q^T, dP^T = V dO^T   (lane = query; K, V rows from LDS, Q, dO in registers)
+//   P^T = exp2(S^T c + bias - L'), dS^T = P^T (dP^T - D)
+//   dQ^T += K^T dS^T              (K^T by transpose reads, dS^T as the B operand)
+template <int HD, bool ALIBI>
+__global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
+  constexpr int KS = HD / 8 + 2;  // K rows: transpose reads dominate (V-style pitch)
+  constexpr int VS = HD / 8 + 1;  // V rows: row reads only (K-style pitch)
+  using Stream = PairStream<HD, DQ_TILE, KS, VS>;
+  constexpr int KP = KS * 16, VP = VS * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (Stream::ABYTES + Stream::BBYTES)];
+  lds_u8* const lds = (lds_u8*)smem;
+  // buffer i: K at lds + i * ABYTES, V at lds + 2 * ABYTES + i * BBYTES
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, half = lane >> 5;
+
+  int w = xcd_remap(blockIdx.x, items);
+  int qt = w % p.num_q_tiles;
+  w /= p.num_q_tiles;
+  const int b = w % p.batch;
+  const int h = w / p.batch;
+  if (p.window_right >= 0) qt = p.num_q_tiles - 1 - qt;  // longest rows first
+
+  const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
+  const int wl = p.window_left, wr = p.window_right;
+  const long rs = (long)p.nheads * HD;
+  const long qoff = (long)b * Sq * rs + (long)h * HD, koff = (long)b * Sk * rs + (long)h * HD;
+
+  const int i0 = qt * BWD_ROWS;
+  const int i_last = min(i0 + BWD_ROWS, Sq) - 1;
+  const int my_q = i0 + 32 * wave + lrow;
+  const int my_pos = my_q + off;
+
+  // key tiles any row of this block sees
+  int lo = 0, hi = Sk - 1;
+  if (wl >= 0) lo = max(lo, i0 + off - wl);
+  if (wr >= 0) hi = min(hi, i_last + off + wr);
+  const int t_begin = hi >= lo ? lo / DQ_TILE : 0;
+  const int t_end = hi >= lo ? hi / DQ_TILE + 1 : 0;
+
+  bf16x8 qf[HD / 16], gf[HD / 16];
+#pragma unroll
+  for (int kk = 0; kk < HD / 16; ++kk) {
+    qf[kk] = row_fragment(p.q + qoff, rs, my_q, Sq, kk, half, p.q_and, p.q_sign);
+    gf[kk] = row_fragment(p.dout + qoff, rs, my_q, Sq, kk, half, 0xffffffffu, 0u);
+  }
+  // L in log2 units (an empty row gets +inf, so that every P of it is 0) and D
+  float lrow2 = INFINITY, drow = 0.f;
+  if (my_q < Sq) {
+    const long li = ((long)b * p.nheads + h) * Sq + my_q;
+    const float l = p.lse[li];
+    lrow2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    drow = p.delta[li];
+  }
+  const float c = p.scale_log2;
+  float slope2 = 0.f;
+  if constexpr (ALIBI) slope2 = p.alibi[h] * kLog2e;
+
+  f32x16 dq[HD / 32];
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db) dq[db] = f32x16{};
+
+  Stream st;
+  st.abase = p.k + koff;
+  st.bbase = p.v + koff;
+  st.lo = 0;
+  st.hi = Sk;
+  st.row_stride = (int)rs;
+  st.row_bytes = (int)rs * 2;
+  st.init(wave, lane);
+
+  if (t_begin < t_end) st.load(lds, lds + 2 * Stream::ABYTES, t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int cur = (t - t_begin) & 1;
+    wait_tile_loads<0>();
+    __syncthreads();  // tile t is in LDS; everyone is done with the other buffer
+    if (t + 1 < t_end)
+      st.load(lds + (cur ^ 1) * Stream::ABYTES, lds + 2 * Stream::ABYTES + (cur ^ 1) * Stream::BBYTES, t + 1);
+    const lds_u8* kt = lds + cur * Stream::ABYTES;
+    const lds_u8* vt = lds + 2 * Stream::ABYTES + cur * Stream::BBYTES;
+
+    f32x16 s[2], dp[2];
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<KP>(kt, lrow, half, kb, kk), qf[kk], s[kb], 0,
+                                                        0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<VP>(vt, lrow, half, kb, kk), gf[kk], dp[kb], 0,
+                                                         0, 0);
+      }
+
+    // P^T and dS^T.  Register r of block kb holds key j0 + 32 kb + 16 (r / 8) + 8 half + r % 8.
+    const int j0 = t * DQ_TILE;
+    const bool full = (j0 + DQ_TILE <= Sk) && (wl < 0 || j0 >= i_last + off - wl) &&
+                      (wr < 0 || j0 + DQ_TILE - 1 <= i0 + off + wr);
+    int vlo = 0, vspan = -1;  // visible keys of this row: [vlo, vlo + vspan]
+    if (!full) {
+      const int klo = wl < 0 ? 0 : max(0, my_pos - wl);
+      const int khi = wr < 0 ? Sk - 1 : min(Sk - 1, my_pos + wr);
+      vlo = klo;
+      vspan = khi - klo;
+    }
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+      const int kb = ci >> 1, r0 = 8 * (ci & 1);
+      f32x16 tmp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = j0 + 32 * kb + 16 * (r0 / 8) + 8 * half + e;
+        float x = fmaf(s[kb][r0 + e], c, -lrow2);
+        if constexpr (ALIBI) x += alibi_log2(slope2, my_pos, key);
+        float pv = fast_exp2(x);
+        if (!full) {
+          const bool vis = vspan >= 0 && (uint32_t)(key - vlo) <= (uint32_t)vspan && my_q < Sq;
+          pv = vis ? pv : 0.f;
+        }
+        tmp[e] = pv * (dp[kb][r0 + e] - drow);
+      }
+      dsf[ci] = pack_rows(tmp, 0);
+    }
+
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci)
+#pragma unroll
+      for (int db = 0; db < HD / 32; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<KP>(kt, lane, db, ci), dsf[ci], dq[db], 0, 0, 0);
+  }
+  if (my_q < Sq) store_rows_bf16<HD>(p.dq + qoff, rs, my_q, dq, p.scale, half);
+#endif
+}
+
+// ---------------------------------------------------------------------------------
+// dkdv_kernel: one workgroup per (batch, head, 128 keys); wave w owns keys
+// j0 + 32 w + 0..31.  Per 32-query tile t:
+//   S = Q K^T, dP = dO V^T        (lane = key; Q, dO rows from LDS, K, V in registers)
+//   P = exp2(S c + bias - L'), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by transpose reads; P, dS as B operands)
+template <int HD, bool ALIBI>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
+  constexpr int QS = HD / 8 + 2;  // Q and dO rows: both read both ways
+  using Stream = PairStream<HD, DKV_TILE, QS, QS>;
+  constexpr int QP = QS * 16;
+  constexpr int LDBYTES = 256;    // L' and D of one tile (fp32, 64 lanes x 4 bytes each)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (Stream::ABYTES + Stream::BBYTES + 2 * LDBYTES)];
+  lds_u8* const lds = (lds_u8*)smem;
+  // buffer i at lds + i * BUF: Q tile, dO tile, then L and D
+  constexpr int BUF = Stream::ABYTES + Stream::BBYTES + 2 * LDBYTES;
+  constexpr int GOFF = Stream::ABYTES, LOFF = Stream::ABYTES + Stream::BBYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, half = lane >> 5;
+
+  int w = xcd_remap(blockIdx.x, items);
+  const int kt_idx = w % p.num_k_tiles;
+  w /= p.num_k_tiles;
+  const int b = w % p.batch;
+  const int h = w / p.batch;
+
+  const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
+  const int wl = p.window_left, wr = p.window_right;
+  const long rs = (long)p.nheads * HD;
+  const long qoff = (long)b * Sq * rs + (long)h * HD, koff = (long)b * Sk * rs + (long)h * HD;
+  const long loff = ((long)b * p.nheads + h) * Sq;
+
+  const int j0 = kt_idx * BWD_ROWS;
+  const int j_last = min(j0 + BWD_ROWS, Sk) - 1;
+  const int my_k = j0 + 32 * wave + lrow;
+
+  // query tiles that see any key of this block: c_i = i + off in [j0 - wr, j_last + wl]
+  int lo = 0, hi = Sq - 1;
+  if (wr >= 0) lo = max(lo, j0 - wr - off);
+  if (wl >= 0) hi = min(hi, j_last + wl - off);
+  const int t_begin = hi >= lo ? lo / DKV_TILE : 0;
+  const int t_end = hi >= lo ? hi / DKV_TILE + 1 : 0;
+
+  bf16x8 kf[HD / 16], vf[HD / 16];
+#pragma unroll
+  for (int kk = 0; kk < HD / 16; ++kk) {
+    kf[kk] = row_fragment(p.k + koff, rs, my_k, Sk, kk, half, p.q_and, p.q_sign);
+    vf[kk] = row_fragment(p.v + koff, rs, my_k, Sk, kk, half, 0xffffffffu, 0u);
+  }
+  const float c = p.scale_log2;
+  float slope2 = 0.f;
+  if constexpr (ALIBI) slope2 = p.alibi[h] * kLog2e;
+  // visible queries of this key: c_i in [my_k - wr, my_k + wl]
+  const int qlo = wr < 0 ? 0 : max(0, my_k - wr - off);
+  const int qhi = wl < 0 ? Sq - 1 : min(Sq - 1, my_k + wl - off);
+
+  f32x16 dk[HD / 32], dv[HD / 32];
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db) dk[db] = dv[db] = f32x16{};
+
+  Stream st;
+  st.abase = p.q + qoff;
+  st.bbase = p.dout + qoff;
+  st.lo = 0;
+  st.hi = Sq;
+  st.row_stride = (int)rs;
+  st.row_bytes = (int)rs * 2;
+  st.init(wave, lane);
+  // L and D of a tile: wave 0 loads L, wave 1 loads D (4 bytes per lane, rows past
+  // the end read as zeros; L is scaled and -inf handled when read)
+  auto load_ld = [&](lds_u8* dst, int t) {
+    if (wave < 2) {
+      const int r0 = t * DKV_TILE;
+      const float* src = (wave == 0 ? p.lse : p.delta) + loff + r0;
+      const int n = max(0, min(DKV_TILE, Sq - r0)) * 4;
+      const auto rsr = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, dst + LDBYTES * wave, 4, 4 * lane, 0, 0, 0);
+    }
+  };
+
+  if (t_begin < t_end) {
+    st.load(lds, lds + GOFF, t_begin);
+    load_ld(lds + LOFF, t_begin);
+  }
+  for (int t = t_begin; t < t_end; ++t) {
+    const int cur = (t - t_begin) & 1;
+    wait_tile_loads<0>();
+    __syncthreads();
+    if (t + 1 < t_end) {
+      lds_u8* nb = lds + (cur ^ 1) * BUF;
+      st.load(nb, nb + GOFF, t + 1);
+      load_ld(nb + LOFF, t + 1);
+    }
+    const lds_u8* qt = lds + cur * BUF;
+    const lds_u8* gt = qt + GOFF;
+    const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
+
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(qt, lrow, half, 0, kk), kf[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(gt, lrow, half, 0, kk), vf[kk], dp, 0, 0, 0);
+    }
+
+    // register r holds query i0 + 16 (r / 8) + 8 half + r % 8 of the tile
+    const int i0 = t * DKV_TILE;
+    // every (query of the tile, key of the block) pair visible, no query past the end
+    const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
+                      (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+      const int qrow = 16 * ci + 8 * half;  // first tile row of this chunk
+      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+      const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+      const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+      const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+      const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+      f32x16 pt, dt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float l = e < 4 ? l_a[e] : l_b[e - 4];
+        const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+        const int qi = i0 + qrow + e;
+        float x = fmaf(s[8 * ci + e], c, -l * kLog2e);
+        if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+        float pv = (l == -INFINITY) ? 0.f : fast_exp2(x);
+        if (!full) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+        pt[e] = pv;
+        dt[e] = pv * (dp[8 * ci + e] - dd);
+      }
+      pf[ci] = pack_rows(pt, 0);
+      dsf[ci] = pack_rows(dt, 0);
+    }
+
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+      for (int db = 0; db < HD / 32; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(gt, lane, db, ci), pf[ci], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(qt, lane, db, ci), dsf[ci], dk[db], 0, 0, 0);
+      }
+  }
+  if (my_k < Sk) {
+    store_rows_bf16<HD>(p.dk + koff, rs, my_k, dk, p.scale, half);
+    store_rows_bf16<HD>(p.dv + koff, rs, my_k, dv, 1.f, half);
+  }
+#endif
+}
+
+hipError_t launch_bwd(const BwdParams& p, int headdim, hipStream_t stream);
+// dq_kernel launches (fa_bwd_dq.hip: its own register-allocation flags)
+hipError_t launch_dq_d64(const BwdParams& p, hipStream_t stream);
+hipError_t launch_dq_d128(const BwdParams& p, hipStream_t stream);
+
+template <int HD>
+hipError_t launch_dq_hd(const BwdParams& p, hipStream_t stream) {
+  const int items = p.batch * p.nheads * p.num_q_tiles;
+  if (p.alibi != nullptr)
+    hipLaunchKernelGGL((dq_kernel<HD, true>), dim3(items), dim3(256), 0, stream, p, items);
+  else
+    hipLaunchKernelGGL((dq_kernel<HD, false>), dim3(items), dim3(256), 0, stream, p, items);
+  return hipGetLastError();
+}
+
+}  // namespace fa

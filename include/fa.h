@@ -146,6 +146,31 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
                int batch, int seqlen_q, int nheads, int headdim, int num_splits,
                hipStream_t stream);
 
+/*
+ * fa_bwd - gradients of the attention forward [FA-overview, "算法 / 反向传播": P is
+ * recomputed from the row-wise logsumexp L alone; "并行性 / 反向传播": one block per
+ * K/V column block].  With S = softmax_scale * Q K^T + bias on the visible pairs and
+ * P = exp(S - L):
+ *   dV = P^T dO,  D = rowsum(dO o O),  dS = P o (dO V^T - D),
+ *   dQ = softmax_scale * dS K,  dK = softmax_scale * dS^T Q.
+ *   q, k, v, out   as for fa_fwd; out and lse are the forward's outputs (device, read)
+ *   dout [batch, seqlen_q, nheads, headdim] bf16 (device, read): gradient of out
+ *   dq   [batch, seqlen_q, nheads, headdim] bf16 (device, written)
+ *   dk, dv [batch, seqlen_k, nheads, headdim] bf16 (device, written)
+ *   delta [batch, nheads, seqlen_q] fp32 (device): caller-owned scratch, written with D
+ *   The other arguments mean what they mean for fa_fwd and must be the forward's.
+ * Rows with no visible key (lse = -inf) get dq = 0 and add nothing to dk, dv.  Keys no
+ * query sees get dk = dv = 0.  Every output element is written exactly once (no
+ * atomics): results are bitwise reproducible.  The ALiBi slopes are constants here
+ * (no gradient).  headdim must be 64 or 128 (256: FA_ERR_UNSUPPORTED).  Errors as for
+ * fa_fwd, plus FA_ERR_INVALID_ARG for a NULL out, lse, dout, dq, dk, dv or delta.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
+           float softmax_scale, int causal, int window_left, int window_right,
+           const float* alibi_slopes, hipStream_t stream);
+
 /* fa_status_str - static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

@@ -29,7 +29,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_varlen",
+                                    "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -92,6 +93,23 @@ def varlen_args(**over):
 ])
 def test_varlen_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_varlen(*varlen_args(**over)) == code
+
+
+def bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, batch=1,
+             seqlen_q=4, seqlen_k=4, nheads=2, headdim=128, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), -1), (dict(lse=None), -1), (dict(dout=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
+    (dict(dv=None), -1), (dict(delta=None), -1), (dict(q=None), -1), (dict(batch=0), -1), (dict(seqlen_k=0), -1),
+    (dict(wl=-2), -1), (dict(scale=math.nan), -1), (dict(headdim=256), -2), (dict(headdim=96), -2),
+])
+def test_bwd_rejects_invalid(lib, over, code):
+    assert lib.fa_bwd(*bwd_args(**over)) == code
 
 
 @pytest.mark.parametrize("args,code", [
