@@ -14,8 +14,9 @@ Printed: ONE JSON line with the contract fields plus
                 (HIP events on the launch stream), against the bf16 MFMA peak;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the workload;
   extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k), the
-                split-KV decode workload in HBM GB/s, and a packed batch of causal
-                sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen).
+                split-KV decode workload in HBM GB/s, a packed batch of causal
+                sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), and
+                the backward (fa_bwd) on the benchmark shape.
 """
 
 from __future__ import annotations
@@ -223,6 +224,34 @@ def varlen_bench(dev, reps: int, warmup: int):
             "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4), "algorithmic_gflop": round(flops / 1e9, 2)}
 
 
+def backward_bench(dev, reps: int, warmup: int):
+    """fa_bwd on the benchmark shape, non-causal and causal.  Algorithmic FLOPs: the five
+    products of the backward (S, dP, dV, dQ, dK) are 10 * headdim per visible pair, 2.5x
+    the forward's count."""
+    res = {}
+    for name in ("bench_s2048", "bench_s2048_causal"):
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
+        dout = torch.randn_like(q)
+        out, lse = fa.flash_attn_func(q, k, v, w.softmax_scale, w.causal)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(w.batch, w.nheads, w.seqlen_q, dtype=torch.float32, device=dev)
+
+        def launch():
+            fa.bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, w.softmax_scale, w.causal)
+
+        for _ in range(warmup):
+            launch()
+        mean_ms, min_ms = time_events(launch, reps)
+        flops = 2.5 * algorithmic_flops(w)
+        tf = flops / (mean_ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4),
+                     "algorithmic_gflop": round(flops / 1e9, 2)}
+        del q, k, v, dout, out, lse, dq, dk, dv, delta
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,7 +347,8 @@ def main():
     if not args.no_extra:
         result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
                            "decode": decode_bench(dev, reps=20, warmup=3),
-                           "varlen_gqa": varlen_bench(dev, reps=10, warmup=3)}
+                           "varlen_gqa": varlen_bench(dev, reps=10, warmup=3),
+                           "backward": backward_bench(dev, reps=10, warmup=5)}
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

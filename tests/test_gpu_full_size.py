@@ -68,3 +68,33 @@ def test_full_size_sampled(name):
     got_lse = lse_c[idx_b, idx_h, idx_i]
     check_lse(got_lse, ref_lse)
     check_out(got_out, ref_out)
+
+
+@pytest.mark.parametrize("name", ["bench_s2048", "bench_s2048_causal", "local_alibi_s8192"])
+def test_full_size_backward_heads(name):
+    """fa_bwd at the full workload size; two whole (batch, head) slices are compared with
+    the exact oracle gradient of that head alone (heads are independent problems)."""
+    from tests.test_gpu_backward import GRAD_REL
+    w = WORKLOADS[name]
+    print(f"[case] full-size backward {name}: {w}", file=sys.stderr, flush=True)
+    q, k, v, slopes = workload_inputs(w)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed + 100)).to(torch.bfloat16)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV)
+    sd = None if slopes is None else slopes.to(DEV)
+    window = (w.window_left, w.window_right)
+    out, lse = fa.flash_attn_func(qd, kd, vd, w.softmax_scale, w.causal, window, sd)
+    dq, dk, dv = fa.attention_backward(qd, kd, vd, out, lse, gd, w.softmax_scale, w.causal, window, sd)
+    torch.cuda.synchronize()
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert bool(torch.isfinite(t).all()), f"{nm}: non-finite or unwritten values"
+    for b, h in [(0, 0), (w.batch - 1, w.nheads - 1)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        hs = None if slopes is None else slopes[h:h + 1]
+        rq, rk, rv = oracle.attention_backward(q[sl], k[sl], v[sl], dout[sl], w.softmax_scale, w.causal,
+                                               w.window_left, w.window_right, hs)
+        for got, ref, nm in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+            g = got[sl].cpu().double().numpy()
+            err = float(np.abs(g - ref).max())
+            bound = GRAD_REL * float(np.abs(ref).max())
+            print(f"[case]   head ({b},{h}) {nm}: max err {err:.3e}, bound {bound:.3e}", file=sys.stderr, flush=True)
+            assert err <= bound, f"{nm} of head ({b},{h}): max err {err:.3e} > {bound:.3e}"
