@@ -60,7 +60,14 @@ struct BwdParams {
 constexpr int BWD_NW = 4;        // waves per workgroup
 constexpr int BWD_ROWS = 128;    // rows (queries or keys) a workgroup owns: 32 per wave
 constexpr int DQ_TILE = 64;      // keys per streamed tile (dq kernel)
-constexpr int DKV_TILE = 32;     // queries per streamed tile (dkdv kernel)
+// Queries per streamed tile (dkdv kernel).  Headdim 128 takes 64 (two independent
+// 32-query blocks per wave: the kernel runs one wave per SIMD there, so it has the
+// registers); headdim 64 takes 32, which keeps it at two waves per SIMD.
+#ifndef FA_DKV_TILE128
+#define FA_DKV_TILE128 64
+#endif
+template <int HD>
+constexpr int dkv_tile() { return HD == 128 ? FA_DKV_TILE128 : 32; }
 
 // Two bf16 [rows][row_stride] tensors streamed tile by tile (ROWS rows) into LDS in
 // natural row order, rows SA (SB) 16-byte slots apart; direct-to-LDS buffer loads,
@@ -353,6 +360,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 //   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by transpose reads; P, dS as B operands)
 template <int HD, bool ALIBI>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
+  constexpr int DKV_TILE = dkv_tile<HD>(), DKV_QB = DKV_TILE / 32;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
   constexpr int QS = HD / 8 + 2;  // Q and dO rows: both read both ways
   using Stream = PairStream<HD, DKV_TILE, QS, QS>;
@@ -445,22 +453,29 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     const lds_u8* gt = qt + GOFF;
     const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
 
-    f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 s[DKV_QB], dp[DKV_QB];
 #pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(qt, lrow, half, 0, kk), kf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(gt, lrow, half, 0, kk), vf[kk], dp, 0, 0, 0);
-    }
+    for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < DKV_QB; ++qb) {
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(qt, lrow, half, qb, kk), kf[kk], s[qb], 0, 0,
+                                                        0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(gt, lrow, half, qb, kk), vf[kk], dp[qb], 0,
+                                                         0, 0);
+      }
 
-    // register r holds query i0 + 16 (r / 8) + 8 half + r % 8 of the tile
+    // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
     const int i0 = t * DKV_TILE;
     // every (query of the tile, key of the block) pair visible, no query past the end
     const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
                       (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
-    bf16x8 pf[2], dsf[2];
+    bf16x8 pf[2 * DKV_QB], dsf[2 * DKV_QB];
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
-      const int qrow = 16 * ci + 8 * half;  // first tile row of this chunk
+    for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+      const int qb = cc >> 1, ci = cc & 1;
+      const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
       typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
       const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
       const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
@@ -472,23 +487,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
         const float l = e < 4 ? l_a[e] : l_b[e - 4];
         const float dd = e < 4 ? d_a[e] : d_b[e - 4];
         const int qi = i0 + qrow + e;
-        float x = fmaf(s[8 * ci + e], c, -l * kLog2e);
+        float x = fmaf(s[qb][8 * ci + e], c, -l * kLog2e);
         if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
         float pv = (l == -INFINITY) ? 0.f : fast_exp2(x);
         if (!full) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
         pt[e] = pv;
-        dt[e] = pv * (dp[8 * ci + e] - dd);
+        dt[e] = pv * (dp[qb][8 * ci + e] - dd);
       }
-      pf[ci] = pack_rows(pt, 0);
-      dsf[ci] = pack_rows(dt, 0);
+      pf[cc] = pack_rows(pt, 0);
+      dsf[cc] = pack_rows(dt, 0);
     }
 
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci)
+    for (int cc = 0; cc < 2 * DKV_QB; ++cc)
 #pragma unroll
       for (int db = 0; db < HD / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(gt, lane, db, ci), pf[ci], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(qt, lane, db, ci), dsf[ci], dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(gt, lane, db, cc), pf[cc], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(qt, lane, db, cc), dsf[cc], dk[db], 0, 0, 0);
       }
   }
   if (my_k < Sk) {
