@@ -23,6 +23,9 @@ Sources (the pages are web articles; each is cited by title and section):
     - section "2.2：针对推理进行优化": for very short queries the keys are split
       across thread blocks and a separate kernel merges the partial results.
     - section "2.3：局部（即滑动窗口）注意力": sliding-window local attention.
+    - section "2.5：分页KV缓存": the KV cache may be paged (a block table maps each
+      sequence's logical blocks to physical ones); section "2.2" also names the
+      KV-cache entry that rotates q and the new keys and appends to the cache in place.
 
 Readings where the pages are silent (each one is a documented convention,
 shared with the GPU library by specification only):
@@ -230,6 +233,85 @@ def attention_backward(q, k, v, dout, softmax_scale: float, causal: bool = False
             dq[b, :, h] = softmax_scale * (ds @ kh)
             dk[b, :, h] = softmax_scale * (ds.T @ qh)
     return dq, dk, dv
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (round to nearest, ties to even), returned as fp64:
+    the precision of the cache and of the operands the kernels multiply."""
+    import torch  # local import: rounding through torch's own RNE conversion
+
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def rotary(x: np.ndarray, positions: np.ndarray, cos: np.ndarray, sin: np.ndarray, rotary_dim: int) -> np.ndarray:
+    """Rotary position embedding, half-split layout, fp64: for d < rotary_dim / 2 the pair
+    (x_d, x_{d + rotary_dim/2}) of the row at position p is rotated by the angle whose
+    cosine and sine are cos[p, d], sin[p, d]; columns from rotary_dim on are unchanged.
+    x [..., S, H, D] with positions [S]."""
+    half = rotary_dim // 2
+    c = cos[positions][:, None, :]  # [S, 1, half]
+    s = sin[positions][:, None, :]
+    y = np.array(x, dtype=np.float64, copy=True)
+    x1, x2 = x[..., :half], x[..., half:rotary_dim]
+    y[..., :half] = x1 * c - x2 * s
+    y[..., half:rotary_dim] = x2 * c + x1 * s
+    return y
+
+
+def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, block_table=None, k_new=None,
+                      v_new=None, rotary_cos=None, rotary_sin=None, rotary_dim: int = 0, causal: bool = False,
+                      window_left: int = -1, window_right: int = -1, alibi_slopes=None):
+    """Decode against a KV cache, fp64 [FA-overview §2.2 (KV-cache decoding: rotary embedding,
+    in-place cache update), §2.5 (paged KV cache)].
+
+    q [B, Sq, H, D]; k_cache, v_cache [num_blocks, page, H_k, D] with block_table [B, blocks]
+    (logical block n of sequence b is physical block block_table[b, n]), or [B, capacity, H_k, D]
+    with block_table None.  Sequence b holds cache_seqlens[b] keys; the new rows k_new, v_new
+    [B, S_new, H_k, D] are appended at positions cache_seqlens[b] .. + S_new - 1.  With rotary
+    tables, q row i and new key row i are rotated at position cache_seqlens[b] + i and rounded
+    to bf16 (the cache stores bf16 and the kernels multiply bf16 operands).  Query head h reads
+    K/V head h // (H / H_k).  Returns out [B, Sq, H, D], lse [B, H, Sq], and the appended key
+    and value rows as stored [B, S_new, H_k, D] (None without new rows).
+    """
+    qd, kc, vc = as_f64(q), as_f64(k_cache), as_f64(v_cache)
+    lens = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
+    batch, seqlen_q, nheads, headdim = qd.shape
+    nheads_k = kc.shape[2]
+    group = nheads // nheads_k
+    page = kc.shape[1]
+    kn = None if k_new is None else as_f64(k_new)
+    vn = None if v_new is None else as_f64(v_new)
+    snew = 0 if kn is None else kn.shape[1]
+    use_rot = rotary_cos is not None
+    if use_rot:
+        cos, sin = as_f64(rotary_cos), as_f64(rotary_sin)
+    out = np.zeros(qd.shape)
+    lse = np.zeros((batch, nheads, seqlen_q))
+    k_app = None if kn is None else np.zeros(kn.shape)
+    v_app = None if vn is None else np.zeros(vn.shape)
+    heads = [h // group for h in range(nheads)]
+    for b in range(batch):
+        rows = []
+        for j in range(lens[b]):  # the cached keys, through the block table
+            if block_table is None:
+                rows.append((b, j))
+            else:
+                rows.append((int(block_table[b][j // page]), j % page))
+        kb = np.array([kc[blk, r] for blk, r in rows]).reshape(lens[b], nheads_k, headdim)
+        vb = np.array([vc[blk, r] for blk, r in rows]).reshape(lens[b], nheads_k, headdim)
+        if snew:
+            knb, vnb = kn[b], vn[b]
+            if use_rot:
+                knb = round_bf16(rotary(knb, lens[b] + np.arange(snew), cos, sin, rotary_dim))
+            k_app[b], v_app[b] = knb, vnb
+            kb, vb = np.concatenate([kb, knb]), np.concatenate([vb, vnb])
+        qb = qd[b]
+        if use_rot:
+            qb = round_bf16(rotary(qb, lens[b] + np.arange(seqlen_q), cos, sin, rotary_dim))
+        o, l = attention_forward(qb[None], kb[:, heads][None], vb[:, heads][None], softmax_scale, causal,
+                                 window_left, window_right, alibi_slopes)
+        out[b], lse[b] = o[0], l[0]
+    return out, lse, k_app, v_app
 
 
 def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_scale: float,

@@ -361,6 +361,68 @@ def pin_backward_closed_forms():
         assert np.allclose(dv0, expect, atol=1e-13)
 
 
+def _rot_complex(x, pos, cos, sin, rd):
+    """Rotary as complex multiplication: (x_d + i x_{d+rd/2}) * (cos + i sin)."""
+    half = rd // 2
+    z = (x[..., :half] + 1j * x[..., half:rd]) * (cos[pos] + 1j * sin[pos])[:, None, :]
+    y = np.array(x, dtype=np.float64, copy=True)
+    y[..., :half], y[..., half:rd] = z.real, z.imag
+    return y
+
+
+def pin_kvcache():
+    """KV-cache decode: rotary equals complex multiplication by e^{i theta}; a paged cache
+    with a shuffled block table equals the contiguous cache; the result equals the scalar
+    brute force on the explicitly gathered keys, with the new rows appended (rotated and
+    rounded to bf16 when rotary tables are given); the appended rows are returned as stored."""
+    rng = np.random.default_rng(70)
+    batch, sq, nh, nhk, d, page, rd = 3, 2, 4, 2, 8, 4, 6
+    theta = rng.uniform(0, 2 * np.pi, (40, rd // 2))
+    cos, sin = np.cos(theta), np.sin(theta)
+    x = rand((5, 2, d), 71)
+    assert np.allclose(oracle.rotary(x, np.arange(7, 12), cos, sin, rd), _rot_complex(x, np.arange(7, 12), cos, sin, rd),
+                       atol=1e-14)
+    lens = [5, 0, 9]
+    cap = 12
+    kc, vc = rand((batch, cap, nhk, d), 72), rand((batch, cap, nhk, d), 73)
+    q = rand((batch, sq, nh, d), 74)
+    knew, vnew = rand((batch, 2, nhk, d), 75), rand((batch, 2, nhk, d), 76)
+    # the same cache, paged with 4-row blocks in shuffled physical order
+    nblk = cap // page
+    perm = rng.permutation(batch * nblk)
+    kp, vp = np.zeros((batch * nblk, page, nhk, d)), np.zeros((batch * nblk, page, nhk, d))
+    table = np.zeros((batch, nblk), dtype=np.int64)
+    for b in range(batch):
+        for n in range(nblk):
+            table[b, n] = perm[b * nblk + n]
+            kp[table[b, n]], vp[table[b, n]] = kc[b, n * page:(n + 1) * page], vc[b, n * page:(n + 1) * page]
+    heads = [0, 0, 1, 1]
+    for causal, wl, al, use_new, use_rot in [(True, -1, None, False, False), (True, 3, np.array([0.3, 0.1, 0.2, 0.05]),
+                                                                              True, False),
+                                             (False, -1, None, True, True), (True, -1, None, True, True)]:
+        kw = dict(k_new=knew if use_new else None, v_new=vnew if use_new else None,
+                  rotary_cos=cos if use_rot else None, rotary_sin=sin if use_rot else None, rotary_dim=rd,
+                  causal=causal, window_left=wl, alibi_slopes=al)
+        o1, l1, ka1, va1 = oracle.attention_kvcache(q, kc, vc, lens, 0.4, **kw)
+        o2, l2, ka2, va2 = oracle.attention_kvcache(q, kp, vp, lens, 0.4, block_table=table, **kw)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        for b in range(batch):
+            kb, vb, qb = kc[b, :lens[b]], vc[b, :lens[b]], q[b]
+            if use_new:
+                kn = knew[b]
+                if use_rot:
+                    kn = oracle.round_bf16(_rot_complex(kn, lens[b] + np.arange(2), cos, sin, rd))
+                assert np.array_equal(ka1[b], kn) and np.array_equal(va1[b], vnew[b])
+                kb, vb = np.concatenate([kb, kn]), np.concatenate([vb, vnew[b]])
+            if use_rot:
+                qb = oracle.round_bf16(_rot_complex(qb, lens[b] + np.arange(sq), cos, sin, rd))
+            ob, lb = oracle.brute_force(qb[None], kb[:, heads][None], vb[:, heads][None], 0.4, causal, wl, -1, al)
+            assert np.allclose(o1[b], ob[0], atol=1e-12)
+            assert np.array_equal(np.isneginf(l1[b]), np.isneginf(lb[0]))
+            fin = np.isfinite(lb[0])
+            assert np.allclose(l1[b][fin], lb[0][fin], atol=1e-12)
+
+
 def pin_bf16_widening():
     """bf16 inputs widen exactly: the oracle sees the very values the GPU gets."""
     t = torch.tensor([1.0, -2.5, 3.140625, 1e-3, 65280.0]).to(torch.bfloat16)
@@ -441,6 +503,10 @@ def test_backward_closed_forms():
     pin_backward_closed_forms()
 
 
+def test_kvcache():
+    pin_kvcache()
+
+
 def test_bf16_widening():
     pin_bf16_widening()
 
@@ -464,6 +530,7 @@ def _all_pins():
     pin_varlen_gqa()
     pin_backward_autograd()
     pin_backward_closed_forms()
+    pin_kvcache()
 
 
 def _top_left(i, seqlen_q, seqlen_k):
@@ -580,7 +647,12 @@ def _bwd_variant(drop_delta=False, unscaled_dk=False, dv_from_dp=False):
     return bwd
 
 
+def _rotary_wrong_sign(x, positions, cos, sin, rotary_dim):
+    return _ORIG_ROTARY(x, positions, cos, -sin, rotary_dim)
+
+
 _ORIG_HEAD_ROWS = oa.head_rows
+_ORIG_ROTARY = oa.rotary
 _ORIG_VARLEN = oa.attention_varlen
 _ORIG_ALIBI = oa.alibi_bias
 _ORIG_SOFTMAX = oa.softmax_rows
@@ -602,6 +674,7 @@ _ORIG_COMBINE = oa.combine
     ("attention_backward", _bwd_variant(drop_delta=True)),
     ("attention_backward", _bwd_variant(unscaled_dk=True)),
     ("attention_backward", _bwd_variant(dv_from_dp=True)),
+    ("rotary", _rotary_wrong_sign),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, replacement):
     """Each planted oracle mistake must make at least one pin fail."""
