@@ -16,6 +16,7 @@ Functions
   fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, ...)
   combine(out_partial, lse_partial, out, lse)
   decode(q, k_cache, v_cache, num_splits=16, ...) -> (out, lse)
+  kvcache_decode(q, k_cache, v_cache, cache_seqlens, ...) -> (out, lse)   KV-cache decode step
   bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, ...)   gradients into preallocated tensors
   attention_backward(q, k, v, out, lse, dout, ...) -> (dq, dk, dv)
 """
@@ -55,6 +56,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, i, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i,
+                                   i, f, i, i, i, vp, i, vp]
+    lib.fa_fwd_kvcache.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
     lib.fa_bwd.restype = i
     lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -256,3 +260,53 @@ def attention_backward(q, k, v, out, lse, dout, softmax_scale=None, causal=False
     delta = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device)
     bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, softmax_scale, causal, window_size, alibi_slopes)
     return dq, dk, dv
+
+
+def kvcache_decode(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None, v_new=None, rotary_cos=None,
+                   rotary_sin=None, softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None,
+                   num_splits=0, max_splits=64):
+    """fa_fwd_kvcache: appends k_new/v_new (rotated with the rotary tables if given) to the
+    cache in place, then attends.  q [B,Sq,H,D]; k_cache/v_cache [num_blocks, page, H_k, D]
+    with block_table [B, max_blocks] int32, or [B, capacity, H_k, D] without; cache_seqlens
+    [B] int32.  Returns (out [B,Sq,H,D] bf16, lse [B,H,Sq] fp32)."""
+    _require(q, "q", torch.bfloat16, 4)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, q.device)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, q.device)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, 1, q.device)
+    b, sq, h, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must match and end in headdim")
+    hk, page = k_cache.shape[2], k_cache.shape[1]
+    if cache_seqlens.shape[0] != b:
+        raise ValueError("cache_seqlens must be [batch]")
+    max_blocks = 1
+    if block_table is not None:
+        _require(block_table, "block_table", torch.int32, 2, q.device)
+        if block_table.shape[0] != b:
+            raise ValueError("block_table must be [batch, max_blocks]")
+        max_blocks = block_table.shape[1]
+    elif k_cache.shape[0] != b:
+        raise ValueError("a contiguous cache must be [batch, capacity, H_k, D]")
+    snew = 0
+    if k_new is not None:
+        _require(k_new, "k_new", torch.bfloat16, 4, q.device)
+        _require(v_new, "v_new", torch.bfloat16, 4, q.device)
+        if k_new.shape != v_new.shape or k_new.shape[0] != b or k_new.shape[2] != hk or k_new.shape[3] != d:
+            raise ValueError("k_new and v_new must be [batch, seqlen_new, H_k, D]")
+        snew = k_new.shape[1]
+    rd = 0
+    if rotary_cos is not None:
+        _require(rotary_cos, "rotary_cos", torch.float32, 2, q.device)
+        _require(rotary_sin, "rotary_sin", torch.float32, 2, q.device)
+        rd = 2 * rotary_cos.shape[1]
+    slopes = _alibi(alibi_slopes, h, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
+    op = torch.empty(max_splits, b, h, sq, d, dtype=torch.float32, device=q.device)
+    lp = torch.empty(max_splits, b, h, sq, dtype=torch.float32, device=q.device)
+    _check(load_library().fa_fwd_kvcache(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(), _ptr(block_table), page,
+        max_blocks, _ptr(k_new), _ptr(v_new), snew, _ptr(rotary_cos), _ptr(rotary_sin), rd, out.data_ptr(),
+        lse.data_ptr(), op.data_ptr(), lp.data_ptr(), int(max_splits), b, sq, h, hk, d, _scale(softmax_scale, d),
+        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), int(num_splits), _stream_handle(q)))
+    return out, lse

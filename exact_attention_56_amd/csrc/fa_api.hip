@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fa.h"
 #include "fa_bwd_kernel.h"
 
@@ -14,6 +16,10 @@ hipError_t launch_fwd(const FwdParams& p, int headdim, bool split, hipStream_t s
 long fwd_num_blocks(const FwdParams& p, bool split);
 hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream);
+hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new, const uint16_t* v_new,
+                          uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
+                          uint16_t* qrot, hipStream_t stream);
+int decode_step_keys(int headdim);
 }  // namespace fa
 
 namespace {
@@ -73,6 +79,12 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
   p->cu_q = nullptr;
   p->cu_k = nullptr;
   p->lse_head_stride = 0;
+  p->cache_seqlens = nullptr;
+  p->block_table = nullptr;
+  p->page_size = 0;
+  p->page_shift = 0;
+  p->max_blocks = 0;
+  p->seqlen_new = 0;
   // The kernels fold the scale into Q's sign and a positive multiplier: a negative
   // scale negates Q, a zero scale zeroes Q (every score is then exactly 0).
   if (softmax_scale == 0.f) {
@@ -206,6 +218,72 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
     return FA_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return fa::launch_bwd(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens, const int* block_table,
+                   int page_size, int max_blocks_per_seq, const void* k_new, const void* v_new, int seqlen_new,
+                   const float* rotary_cos, const float* rotary_sin, int rotary_dim, void* out, float* lse,
+                   float* out_partial, float* lse_partial, int max_splits, int batch, int seqlen_q, int nheads,
+                   int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
+                   const float* alibi_slopes, int num_splits, hipStream_t stream) {
+  if (!cache_seqlens || !out || !lse || !out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
+  if (seqlen_q < 1 || seqlen_q > kDecodeMaxRows || seqlen_new < 0 || page_size < 1 || max_splits < 1)
+    return FA_ERR_INVALID_ARG;
+  if (nheads < 1 || nheads_k < 1 || nheads % nheads_k != 0) return FA_ERR_INVALID_ARG;
+  if (seqlen_new > 0 && (!k_new || !v_new)) return FA_ERR_INVALID_ARG;
+  if ((rotary_cos == nullptr) != (rotary_sin == nullptr)) return FA_ERR_INVALID_ARG;
+  if (rotary_cos && (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > headdim)) return FA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > max_splits) return FA_ERR_INVALID_ARG;
+  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
+  int shift = 0;
+  long long capacity = page_size;
+  if (block_table) {
+    // a decode step never crosses a block: blocks are a power of two of at least 64 rows
+    if ((page_size & (page_size - 1)) != 0 || page_size < 64 || page_size % fa::decode_step_keys(headdim) != 0 ||
+        max_blocks_per_seq < 1)
+      return FA_ERR_INVALID_ARG;
+    while ((1 << shift) < page_size) ++shift;
+    capacity = (long long)page_size * max_blocks_per_seq;
+  }
+  if (capacity > kMaxSeqlen) return FA_ERR_INVALID_ARG;
+  fa::FwdParams p;
+  const int st = prepare(q, k_cache, v_cache, batch, seqlen_q, (int)capacity, nheads, headdim, softmax_scale,
+                         causal, window_left, window_right, alibi_slopes, &p);
+  if (st != FA_OK) return st;
+  // automatic split count: about 2048 workgroups (eight per CU), at least 256 keys each
+  int ns = num_splits;
+  if (ns == 0) {
+    const long rows = (long)batch * nheads * seqlen_q;
+    ns = (int)std::min<long>(max_splits, std::max<long>(1, (2048 + rows - 1) / rows));
+    ns = (int)std::min<long long>(ns, std::max<long long>(1, capacity / 256));
+  }
+  if (elems4(ns, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
+  if ((long)batch * nheads * ns * seqlen_q > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  p.nheads_k = nheads_k;
+  p.cache_seqlens = cache_seqlens;
+  p.block_table = block_table;
+  p.page_size = page_size;
+  p.page_shift = shift;
+  p.max_blocks = block_table ? max_blocks_per_seq : 1;
+  p.seqlen_new = seqlen_new;
+  p.out = out_partial;
+  p.lse = lse_partial;
+  p.num_splits = ns;
+  p.split_len = (int)((capacity + ns - 1) / ns);
+  (void)hipGetLastError();
+  if (fa::launch_kvcache(p, headdim, (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
+                         (uint16_t*)v_cache, rotary_cos, rotary_sin, rotary_dim, (uint16_t*)out, stream) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  fa::CombineParams c;
+  c.out_partial = out_partial;
+  c.lse_partial = lse_partial;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  c.batch = batch;
+  c.seqlen_q = seqlen_q;
+  c.nheads = nheads;
+  c.num_splits = ns;
+  return fa::launch_combine(c, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,

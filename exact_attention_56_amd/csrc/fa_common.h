@@ -44,6 +44,14 @@ struct FwdParams {
   int num_splits;         // 1 for the plain forward
   int split_len;          // keys per split (ceil(Sk / num_splits))
   int reverse_q;          // 1: visit the heaviest query tiles first (causal)
+  // KV-cache decode (fa_fwd_kvcache); cache_seqlens is nullptr otherwise
+  const int* cache_seqlens;  // [batch] rows already in the cache
+  const int* block_table;    // [batch, max_blocks] physical block of each logical block, or
+                             // nullptr: contiguous cache, block b holds sequence b
+  int page_size;             // rows per block (the per-sequence capacity when contiguous)
+  int page_shift;            // log2(page_size) when paged
+  int max_blocks;            // row length of block_table
+  int seqlen_new;            // rows appended to every sequence before the attention
 };
 
 // Combine description.

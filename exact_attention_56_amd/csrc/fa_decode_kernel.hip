@@ -31,7 +31,10 @@ constexpr int DEC_CPOL = FA_DEC_CPOL;      // KV loads are non-temporal (read on
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-template <int HD, bool ALIBI>
+// KVC: the keys come from a KV cache (fa_fwd_kvcache): sequence b has
+// cache_seqlens[b] + seqlen_new keys, block n of it lives in block block_table[b, n]
+// (or block b of a contiguous cache), and K/V may have fewer heads than Q.
+template <int HD, bool ALIBI, bool KVC>
 __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) {
   constexpr int LPR = HD / 8;    // lanes per key row
   constexpr int RPW = 64 / LPR;  // key rows per wave per load
@@ -45,16 +48,19 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   const int cidx = lane % LPR;  // 8-column chunk of the head dimension
 
   int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int Sq = p.seqlen_q, Sk = p.seqlen_k;
+  const int Sq = p.seqlen_q;
   const int i = w % Sq;
   w /= Sq;
   const int split = w % p.num_splits;
   w /= p.num_splits;
   const int h = w % p.nheads;
   const int b = w / p.nheads;
+  const int Sk = KVC ? p.cache_seqlens[b] + p.seqlen_new : p.seqlen_k;
 
-  const long row_stride = (long)p.nheads * HD;
-  const int row_bytes = (int)row_stride * 2;
+  const long row_stride = (long)p.nheads * HD;       // q
+  const long kv_stride = (long)p.nheads_k * HD;      // k, v
+  const int row_bytes = (int)kv_stride * 2;
+  const int hk = h / (p.nheads / p.nheads_k);
 
   // visible keys of row i inside this split: [lo, hi)
   const int pos = i + Sk - Sq;
@@ -62,7 +68,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   int hi = min(Sk, lo + p.split_len);
   if (p.window_left >= 0) lo = max(lo, pos - p.window_left);
   if (p.window_right >= 0) hi = min(hi, pos + p.window_right + 1);
-  const long kvb = (long)b * Sk * row_stride + (long)h * HD;  // key 0 of this (batch, head)
+  const long kvb = KVC ? (long)hk * HD : (long)b * Sk * kv_stride + (long)hk * HD;  // key 0 / head offset
+  // KV-cache steps start on multiples of STEP so that none crosses a block; keys
+  // below lo are then masked
+  const int first = KVC ? (lo & ~(STEP - 1)) : lo;
 
   // q chunk, pre-multiplied by softmax_scale * log2(e) (sign included)
   const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
@@ -83,12 +92,20 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-  for (int base = lo + wave * STEP; base < hi; base += 4 * STEP) {
+  for (int base = first + wave * STEP; base < hi; base += 4 * STEP) {
     // buffer resources over keys [base, min(hi, base + STEP)): later keys read as zeros
     const int nrec = min(hi - base, STEP) * row_bytes;
-    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvb + (long)base * row_stride), (short)0, nrec,
+    long row0 = base;  // physical row of key `base`
+    if constexpr (KVC) {
+      if (p.block_table != nullptr)
+        row0 = (long)p.block_table[(long)b * p.max_blocks + (base >> p.page_shift)] * p.page_size +
+               (base & (p.page_size - 1));
+      else
+        row0 = (long)b * p.page_size + base;
+    }
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvb + row0 * kv_stride), (short)0, nrec,
                                                        0x00020000);
-    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvb + (long)base * row_stride), (short)0, nrec,
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvb + row0 * kv_stride), (short)0, nrec,
                                                        0x00020000);
     u32x4 kr[DEC_UNROLL], vr[DEC_UNROLL];
 #pragma unroll
@@ -111,7 +128,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
       for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
       const int key = base + u * RPW + g;
       if constexpr (ALIBI) part -= slope * fabsf((float)(pos - key));
-      s[u] = key < hi ? part : -INFINITY;
+      s[u] = (key < hi && (!KVC || key >= lo)) ? part : -INFINITY;
       bmax = fmaxf(bmax, s[u]);
     }
 #pragma unroll
@@ -218,15 +235,110 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   if (lane == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
+// Element e of a bf16 row x rotated at position `pos` (half-split rotary layout:
+// the pair (x_d, x_{d + rd/2}) turns by the angle of cos[pos, d], sin[pos, d];
+// columns from rd on are unchanged), rounded to bf16.
+__device__ __forceinline__ uint16_t rotated(const uint16_t* x, int e, long pos, const float* cos, const float* sin,
+                                            int rd) {
+  const int half = rd >> 1;
+  const float xe = __uint_as_float((uint32_t)x[e] << 16);
+  float y = xe;
+  if (e < half) {
+    const float c = cos[pos * half + e], s = sin[pos * half + e];
+    y = xe * c - __uint_as_float((uint32_t)x[e + half] << 16) * s;
+  } else if (e < rd) {
+    const float c = cos[pos * half + e - half], s = sin[pos * half + e - half];
+    y = xe * c + __uint_as_float((uint32_t)x[e - half] << 16) * s;
+  }
+  return (uint16_t)(pack_bf16x2(y, 0.f) & 0xffffu);
+}
+
+// KV-cache preparation, one wave per row: rows [0, n_kv) append k_new / v_new row
+// (b, i, hk) at position cache_seqlens[b] + i of the cache (keys rotated when cos is
+// given); rows [n_kv, n_kv + n_q) write query row (b, i, h) rotated at position
+// cache_seqlens[b] + i into qrot.
 template <int HD>
-static hipError_t launch_decode_hd(const FwdParams& p, hipStream_t stream) {
+__global__ __launch_bounds__(256) void kvcache_prep_kernel(FwdParams p, const uint16_t* k_new, const uint16_t* v_new,
+                                                           uint16_t* k_cache, uint16_t* v_cache, const float* cos,
+                                                           const float* sin, int rd, uint16_t* qrot, long n_kv,
+                                                           long n_q) {
+  const int lane = threadIdx.x & 63;
+  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task < n_kv) {
+    const int hk = (int)(task % p.nheads_k);
+    const long bi = task / p.nheads_k;
+    const int i = (int)(bi % p.seqlen_new);
+    const int b = (int)(bi / p.seqlen_new);
+    const int j = p.cache_seqlens[b] + i;
+    const long row = p.block_table != nullptr
+                         ? (long)p.block_table[(long)b * p.max_blocks + (j >> p.page_shift)] * p.page_size +
+                               (j & (p.page_size - 1))
+                         : (long)b * p.page_size + j;
+    const long src = bi * p.nheads_k * HD + (long)hk * HD;
+    const long dst = (row * p.nheads_k + hk) * HD;
+    for (int e = lane; e < HD; e += 64) {
+      k_cache[dst + e] = cos != nullptr ? rotated(k_new + src, e, j, cos, sin, rd) : k_new[src + e];
+      v_cache[dst + e] = v_new[src + e];
+    }
+  } else if (task < n_kv + n_q) {
+    const long t = task - n_kv;  // ((b * Sq) + i) * H + h
+    const long bi = t / p.nheads;
+    const int i = (int)(bi % p.seqlen_q);
+    const int b = (int)(bi / p.seqlen_q);
+    const long pos = (long)p.cache_seqlens[b] + i;
+    for (int e = lane; e < HD; e += 64) qrot[t * HD + e] = rotated(p.q + t * HD, e, pos, cos, sin, rd);
+  }
+}
+
+template <int HD, bool KVC>
+static hipError_t launch_decode_kvc(const FwdParams& p, hipStream_t stream) {
   const long nblocks = (long)p.batch * p.nheads * p.num_splits * p.seqlen_q;
   if (p.alibi)
-    hipLaunchKernelGGL((decode_split_kernel<HD, true>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<HD, true, KVC>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<HD, false>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<HD, false, KVC>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream,
+                       p);
   return hipGetLastError();
 }
+
+template <int HD>
+static hipError_t launch_decode_hd(const FwdParams& p, hipStream_t stream) {
+  return launch_decode_kvc<HD, false>(p, stream);
+}
+
+template <int HD>
+static hipError_t launch_kvcache_hd(const FwdParams& p, const uint16_t* k_new, const uint16_t* v_new,
+                                    uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
+                                    uint16_t* qrot, hipStream_t stream) {
+  const long n_kv = (long)p.batch * p.seqlen_new * p.nheads_k;
+  const long n_q = cos != nullptr ? (long)p.batch * p.seqlen_q * p.nheads : 0;
+  if (n_kv + n_q > 0)
+    hipLaunchKernelGGL(kvcache_prep_kernel<HD>, dim3((unsigned)((n_kv + n_q + 3) / 4)), dim3(256), 0, stream, p,
+                       k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, n_kv, n_q);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FwdParams d = p;
+  if (cos != nullptr) d.q = qrot;  // the decode kernel reads the rotated queries
+  return launch_decode_kvc<HD, true>(d, stream);
+}
+
+// KV-cache decode: append (and rotate), then the split partials.  The caller runs
+// the combine afterwards.
+hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new, const uint16_t* v_new,
+                          uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
+                          uint16_t* qrot, hipStream_t stream) {
+  switch (headdim) {
+    case 64: return launch_kvcache_hd<64>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    case 128: return launch_kvcache_hd<128>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    case 256: return launch_kvcache_hd<256>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Key rows one decode step covers per wave (blocks of a paged cache must hold a whole
+// number of them): DEC_UNROLL * 64 / (headdim / 8).
+int decode_step_keys(int headdim) { return DEC_UNROLL * 64 / (headdim / 8); }
 
 hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream) {
   switch (headdim) {

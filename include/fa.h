@@ -147,6 +147,46 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
                hipStream_t stream);
 
 /*
+ * fa_fwd_kvcache - decode step against a KV cache [FA-overview, "2.2" (short queries:
+ * the keys are split across workgroups and merged by a second kernel; the KV-cache
+ * entry rotates q and the new keys and appends them to the cache in place), "2.5"
+ * (paged KV cache)].
+ *   q [batch, seqlen_q, nheads, headdim] bf16 (device, read), 1 <= seqlen_q <= 8
+ *   k_cache, v_cache (device, read and written): block_table != NULL: paged,
+ *       [num_blocks, page_size, nheads_k, headdim] bf16, logical block n of sequence b
+ *       is physical block block_table[b * max_blocks_per_seq + n]; page_size a power of
+ *       two, at least 64;  block_table == NULL: contiguous [batch, page_size, nheads_k,
+ *       headdim], page_size being the capacity per sequence.
+ *   cache_seqlens [batch] int32 (device, read): rows already in the cache.
+ *   k_new, v_new [batch, seqlen_new, nheads_k, headdim] bf16 (device, read) or NULL when
+ *       seqlen_new = 0: appended at rows cache_seqlens[b] .. + seqlen_new - 1 (written into
+ *       the cache before the attention reads it).
+ *   rotary_cos, rotary_sin [positions, rotary_dim / 2] fp32 (device, read) or both NULL:
+ *       query row i and new key row i are rotated at position cache_seqlens[b] + i, pairs
+ *       (x_d, x_{d + rotary_dim/2}) for d < rotary_dim / 2 (rotary_dim even, <= headdim);
+ *       the rotated keys are stored in the cache.
+ *   out [batch, seqlen_q, nheads, headdim] bf16, lse [batch, nheads, seqlen_q] fp32
+ *       (device, written; out also holds the rotated queries between the two passes).
+ *   out_partial, lse_partial: caller-owned scratch of at least max_splits splits in the
+ *       fa_fwd_splitkv layout.  num_splits = 0 picks the split count (about 2048
+ *       workgroups, at least 256 keys per split), else 1..max_splits.
+ * Sequence b attends to its cache_seqlens[b] + seqlen_new keys; the causal/window
+ * alignment is bottom-right within them.  Query head h reads K/V head
+ * h / (nheads / nheads_k).  Device-side values (cache_seqlens, block_table, rotary
+ * positions) cannot be checked on the host: they must stay inside the buffers.
+ * Errors as for fa_fwd, plus FA_ERR_INVALID_ARG for NULL required pointers, seqlen_q
+ * outside [1, 8], an invalid page_size, rotary_dim, num_splits or head grouping.
+ */
+int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
+                   const int* block_table, int page_size, int max_blocks_per_seq,
+                   const void* k_new, const void* v_new, int seqlen_new,
+                   const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                   void* out, float* lse, float* out_partial, float* lse_partial, int max_splits,
+                   int batch, int seqlen_q, int nheads, int nheads_k, int headdim,
+                   float softmax_scale, int causal, int window_left, int window_right,
+                   const float* alibi_slopes, int num_splits, hipStream_t stream);
+
+/*
  * fa_bwd - gradients of the attention forward [FA-overview, "算法 / 反向传播": P is
  * recomputed from the row-wise logsumexp L alone; "并行性 / 反向传播": one block per
  * K/V column block].  With S = softmax_scale * Q K^T + bias on the visible pairs and

@@ -29,8 +29,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_combine", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_varlen",
-                                    "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_combine", "fa_fwd", "fa_fwd_kvcache", "fa_fwd_splitkv",
+                                    "fa_fwd_varlen", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -93,6 +93,25 @@ def varlen_args(**over):
 ])
 def test_varlen_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_varlen(*varlen_args(**over)) == code
+
+
+def kvc_args(**over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, table=FAKE, page=256, max_blocks=4, knew=None, vnew=None, snew=0,
+             cos=None, sin=None, rd=0, out=FAKE, lse=FAKE, op=FAKE, lp=FAKE, max_splits=16, batch=2, sq=1, nheads=8,
+             nheads_k=2, headdim=128, scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, num_splits=0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lens=None), -1), (dict(out=None), -1), (dict(op=None), -1), (dict(q=None), -1), (dict(sq=0), -1),
+    (dict(sq=9), -1), (dict(snew=2), -1), (dict(snew=-1), -1), (dict(page=100), -1), (dict(page=32), -1),
+    (dict(max_blocks=0), -1), (dict(nheads_k=3), -1), (dict(cos=FAKE), -1), (dict(cos=FAKE, sin=FAKE, rd=3), -1),
+    (dict(cos=FAKE, sin=FAKE, rd=256), -1), (dict(num_splits=17), -1), (dict(num_splits=-1), -1),
+    (dict(max_splits=0), -1), (dict(headdim=80), -2), (dict(table=None, page=0), -1),
+])
+def test_kvcache_rejects_invalid(lib, over, code):
+    assert lib.fa_fwd_kvcache(*kvc_args(**over)) == code
 
 
 def bwd_args(**over):

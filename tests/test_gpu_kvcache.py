@@ -1,0 +1,96 @@
+"""GPU parity of the KV-cache decode (fa_fwd_kvcache through the C ABI) against the
+fp64 oracle: paged caches with shuffled block tables and contiguous caches, in-place
+append of new rows, rotary embeddings, grouped K/V heads, masks, and split counts.
+
+Besides out and lse (the forward tolerances), the cache itself is checked: appended
+value rows are bit-exact, appended key rows (rotated in fp32 on the GPU, in fp64 then
+rounded in the oracle) are within one bf16 step, and every other cache row is unchanged.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_56_amd as fa
+import oracle
+from exact_attention_56_amd.inputs import make_alibi_slopes
+from tests.parity import check_empty_rows_zero, check_lse, check_out
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+KVC_CASES = [
+    # batch, Sq, H, H_k, D, page (None: contiguous), max_blocks / capacity, cache lengths, S_new, rotary_dim,
+    # causal, window_left, alibi, num_splits
+    (3, 1, 8, 2, 128, 64, 8, (100, 0, 447), 1, 0, True, -1, False, 0),
+    (2, 4, 4, 1, 128, 64, 6, (130, 63), 4, 128, True, -1, False, 0),
+    (2, 2, 4, 4, 64, 128, 4, (200, 5), 2, 32, True, 50, True, 3),
+    (2, 1, 6, 3, 256, 64, 5, (190, 257), 0, 0, True, -1, False, 16),
+    (2, 3, 4, 2, 128, None, 300, (0, 250), 3, 64, False, -1, False, 0),
+    (1, 8, 2, 2, 64, None, 1000, (900,), 8, 64, True, 100, True, 7),
+    (4, 1, 16, 16, 128, 256, 4, (1023, 1, 500, 768), 1, 128, True, -1, False, 0),
+]
+
+
+def case_id(c):
+    b, sq, h, hk, d, page, cap, lens, snew, rd, causal, wl, alibi, ns = c
+    return (f"b{b}_sq{sq}_h{h}kv{hk}_d{d}_{'paged' + str(page) if page else 'contig'}_lens{'-'.join(map(str, lens))}"
+            f"_new{snew}_rot{rd}{'_causal' if causal else ''}_wl{wl}{'_alibi' if alibi else ''}_ns{ns}")
+
+
+def bf16(shape, g):
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", KVC_CASES, ids=[case_id(c) for c in KVC_CASES])
+def test_kvcache_matches_oracle(case):
+    b, sq, h, hk, d, page, cap, lens, snew, rd, causal, wl, alibi, ns = case
+    print(f"[case] kvcache {case_id(case)}", file=sys.stderr, flush=True)
+    g = torch.Generator().manual_seed(sum(lens) + 31 * d + snew)
+    q = bf16((b, sq, h, d), g)
+    if page is None:
+        kc, vc = bf16((b, cap, hk, d), g), bf16((b, cap, hk, d), g)
+        table = None
+    else:
+        nblk = b * cap
+        kc, vc = bf16((nblk, page, hk, d), g), bf16((nblk, page, hk, d), g)
+        perm = torch.randperm(nblk, generator=g).to(torch.int32)
+        table = perm.view(b, cap).contiguous()
+    knew = bf16((b, snew, hk, d), g) if snew else None
+    vnew = bf16((b, snew, hk, d), g) if snew else None
+    cos = sin = None
+    if rd:
+        theta = torch.rand(4096, rd // 2, generator=g) * 2 * math.pi
+        cos, sin = torch.cos(theta), torch.sin(theta)
+    slopes = make_alibi_slopes(h) if alibi else None
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+
+    dv = lambda t: None if t is None else t.to(DEV)
+    kc_d, vc_d = kc.to(DEV), vc.to(DEV)
+    out, lse = fa.kvcache_decode(q.to(DEV), kc_d, vc_d, lens_t.to(DEV), dv(table), dv(knew), dv(vnew), dv(cos), dv(sin),
+                                 scale, causal, (wl, -1), dv(slopes), num_splits=ns, max_splits=16)
+    torch.cuda.synchronize()
+    ref_out, ref_lse, k_app, v_app = oracle.attention_kvcache(
+        q, kc, vc, lens, scale, block_table=None if table is None else table.numpy(), k_new=knew, v_new=vnew,
+        rotary_cos=cos, rotary_sin=sin, rotary_dim=rd, causal=causal, window_left=wl, alibi_slopes=slopes)
+    check_lse(lse.cpu(), ref_lse)
+    check_out(out.cpu(), ref_out)
+    check_empty_rows_zero(out.cpu(), ref_lse)
+
+    # the cache: appended rows where they belong, everything else untouched
+    kc_got, vc_got = kc_d.cpu(), vc_d.cpu()
+    touched = torch.zeros(kc.shape[0], kc.shape[1], dtype=torch.bool)
+    for bb in range(b):
+        for i in range(snew):
+            j = lens[bb] + i
+            blk, row = (bb, j) if table is None else (int(table[bb, j // page]), j % page)
+            touched[blk, row] = True
+            assert torch.equal(vc_got[blk, row], vnew[bb, i]), f"v row {bb},{i} not appended exactly"
+            kg = kc_got[blk, row].view(torch.int16).int()
+            kr = torch.from_numpy(k_app[bb, i]).to(torch.float32).to(torch.bfloat16).view(torch.int16).int()
+            assert int((kg - kr).abs().max()) <= 1, f"k row {bb},{i}: more than one bf16 step off"
+    assert torch.equal(kc_got[~touched], kc[~touched]) and torch.equal(vc_got[~touched], vc[~touched])
