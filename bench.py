@@ -15,8 +15,9 @@ Printed: ONE JSON line with the contract fields plus
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the workload;
   extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k), the
                 split-KV decode workload in HBM GB/s, a packed batch of causal
-                sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), and
-                the backward (fa_bwd) on the benchmark shape.
+                sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), the
+                backward (fa_bwd) on the benchmark shape, and a paged-KV-cache decode
+                step (fa_fwd_kvcache).
 """
 
 from __future__ import annotations
@@ -224,6 +225,42 @@ def varlen_bench(dev, reps: int, warmup: int):
             "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4), "algorithmic_gflop": round(flops / 1e9, 2)}
 
 
+def kvcache_bench(dev, reps: int, warmup: int):
+    """fa_fwd_kvcache on the decode workload's sizes with a paged cache: batch 8, 16 query
+    heads over 4 K/V heads x 128, 32767 cached keys + 1 appended (rotary on q and the new
+    key), 256-row blocks in shuffled order, automatic split count.  HBM bytes: the K/V rows
+    read plus q, the appended row, partials and outputs."""
+    w = WORKLOADS["decode_s32768"]
+    b, h, hk, d, page = w.batch, w.nheads, 4, w.headdim, 256
+    cached = w.seqlen_k - 1
+    blocks = w.seqlen_k // page
+    g = torch.Generator(device=dev).manual_seed(9)
+    mk = lambda *shape: torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kc, vc = mk(b * blocks, page, hk, d), mk(b * blocks, page, hk, d)
+    table = torch.randperm(b * blocks, generator=g, device=dev).to(torch.int32).view(b, blocks).contiguous()
+    lens = torch.full((b,), cached, dtype=torch.int32, device=dev)
+    q, knew, vnew = mk(b, 1, h, d), mk(b, 1, hk, d), mk(b, 1, hk, d)
+    theta = torch.rand(w.seqlen_k + 8, d // 2, generator=g, device=dev) * 6.2831853
+    cos, sin = torch.cos(theta), torch.sin(theta)
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, 1, dtype=torch.float32, device=dev)
+    op = torch.empty(64, b, h, 1, d, dtype=torch.float32, device=dev)
+    lp = torch.empty(64, b, h, 1, dtype=torch.float32, device=dev)
+
+    def launch():
+        fa.fwd_kvcache(q, kc, vc, lens, out, lse, op, lp, table, knew, vnew, cos, sin, w.softmax_scale, True)
+
+    for _ in range(warmup):
+        launch()
+    mean_ms, min_ms = time_events(launch, reps)
+    nbytes = 2 * b * w.seqlen_k * hk * d * 2 + q.numel() * 2 * 2 + 2 * knew.numel() * 2 + out.numel() * 2
+    return {"workload": f"paged KV cache: batch {b}, {h} query heads over {hk} K/V heads x {d}, {cached} cached + 1 "
+                        f"appended key, {page}-row blocks, rotary, causal, automatic splits",
+            "gbs": round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "mean_us": round(mean_ms * 1e3, 2), "min_us": round(min_ms * 1e3, 2), "bytes": nbytes}
+
+
 def backward_bench(dev, reps: int, warmup: int):
     """fa_bwd on the benchmark shape, non-causal and causal.  Algorithmic FLOPs: the five
     products of the backward (S, dP, dV, dQ, dK) are 10 * headdim per visible pair, 2.5x
@@ -348,7 +385,8 @@ def main():
         result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
                            "decode": decode_bench(dev, reps=20, warmup=3),
                            "varlen_gqa": varlen_bench(dev, reps=10, warmup=3),
-                           "backward": backward_bench(dev, reps=10, warmup=5)}
+                           "backward": backward_bench(dev, reps=10, warmup=5),
+                           "kvcache_paged": kvcache_bench(dev, reps=20, warmup=5)}
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -269,6 +269,21 @@ def kvcache_decode(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=N
     cache in place, then attends.  q [B,Sq,H,D]; k_cache/v_cache [num_blocks, page, H_k, D]
     with block_table [B, max_blocks] int32, or [B, capacity, H_k, D] without; cache_seqlens
     [B] int32.  Returns (out [B,Sq,H,D] bf16, lse [B,H,Sq] fp32)."""
+    b, sq, h, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
+    op = torch.empty(max_splits, b, h, sq, d, dtype=torch.float32, device=q.device)
+    lp = torch.empty(max_splits, b, h, sq, dtype=torch.float32, device=q.device)
+    fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, op, lp, block_table, k_new, v_new, rotary_cos,
+                rotary_sin, softmax_scale, causal, window_size, alibi_slopes, num_splits)
+    return out, lse
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_partial, block_table=None, k_new=None,
+                v_new=None, rotary_cos=None, rotary_sin=None, softmax_scale=None, causal=False, window_size=(-1, -1),
+                alibi_slopes=None, num_splits=0) -> None:
+    """fa_fwd_kvcache with preallocated out [B,Sq,H,D], lse [B,H,Sq] and split scratch
+    out_partial [S,B,H,Sq,D] / lse_partial [S,B,H,Sq] (fp32; S = max_splits)."""
     _require(q, "q", torch.bfloat16, 4)
     _require(k_cache, "k_cache", torch.bfloat16, 4, q.device)
     _require(v_cache, "v_cache", torch.bfloat16, 4, q.device)
@@ -300,13 +315,17 @@ def kvcache_decode(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=N
         _require(rotary_sin, "rotary_sin", torch.float32, 2, q.device)
         rd = 2 * rotary_cos.shape[1]
     slopes = _alibi(alibi_slopes, h, q.device)
-    out = torch.empty_like(q)
-    lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
-    op = torch.empty(max_splits, b, h, sq, d, dtype=torch.float32, device=q.device)
-    lp = torch.empty(max_splits, b, h, sq, dtype=torch.float32, device=q.device)
+    _require(out, "out", torch.bfloat16, 4, q.device)
+    _require(lse, "lse", torch.float32, 3, q.device)
+    _require(out_partial, "out_partial", torch.float32, 5, q.device)
+    _require(lse_partial, "lse_partial", torch.float32, 4, q.device)
+    max_splits = out_partial.shape[0]
+    if out.shape != q.shape or tuple(lse.shape) != (b, h, sq) or tuple(out_partial.shape[1:]) != (b, h, sq, d) or \
+            tuple(lse_partial.shape) != (max_splits, b, h, sq):
+        raise ValueError("out/lse/partials do not match q")
+    op, lp = out_partial, lse_partial
     _check(load_library().fa_fwd_kvcache(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(), _ptr(block_table), page,
         max_blocks, _ptr(k_new), _ptr(v_new), snew, _ptr(rotary_cos), _ptr(rotary_sin), rd, out.data_ptr(),
         lse.data_ptr(), op.data_ptr(), lp.data_ptr(), int(max_splits), b, sq, h, hk, d, _scale(softmax_scale, d),
         int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), int(num_splits), _stream_handle(q)))
-    return out, lse
