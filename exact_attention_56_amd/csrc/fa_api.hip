@@ -20,6 +20,7 @@ hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new
                           uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
                           uint16_t* qrot, hipStream_t stream);
 int decode_step_keys(int headdim);
+int decode_queries_per_block(int nq_total);
 }  // namespace fa
 
 namespace {
@@ -250,10 +251,13 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
   const int st = prepare(q, k_cache, v_cache, batch, seqlen_q, (int)capacity, nheads, headdim, softmax_scale,
                          causal, window_left, window_right, alibi_slopes, &p);
   if (st != FA_OK) return st;
-  // automatic split count: about 2048 workgroups (eight per CU), at least 256 keys each
+  // automatic split count: about 2048 workgroups (eight per CU), at least 256 keys each;
+  // a workgroup serves up to eight queries of one K/V head
   int ns = num_splits;
   if (ns == 0) {
-    const long rows = (long)batch * nheads * seqlen_q;
+    const int nq = nheads / nheads_k * seqlen_q;
+    const int per_block = fa::decode_queries_per_block(nq);
+    const long rows = (long)batch * nheads_k * ((nq + per_block - 1) / per_block);
     ns = (int)std::min<long>(max_splits, std::max<long>(1, (2048 + rows - 1) / rows));
     ns = (int)std::min<long long>(ns, std::max<long long>(1, capacity / 256));
   }

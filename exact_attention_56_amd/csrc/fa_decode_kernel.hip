@@ -12,6 +12,9 @@
 // four waves walk interleaved slices of the chunk with their own online-softmax
 // state, merged through LDS at the end.  The output of a split is normalised
 // within the split, with its logsumexp; an empty split gives 0 and -inf.
+// When a K/V head serves several queries (grouped heads, or seqlen_q > 1) a grouped
+// variant takes up to eight of them per workgroup, so each key row is loaded once
+// for all of them.
 //
 // Combine kernel: out = sum_s exp(lse_s - L) out_s with L = ln sum_s exp(lse_s).
 #include "fa_common.h"
@@ -191,6 +194,195 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
   if (tid == 0) p.lse[rowid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
 }
 
+// Grouped decode partial kernel: one workgroup per (batch, K/V head, split, chunk of
+// NQ queries).  The queries of a K/V head are its nheads / nheads_k query heads times
+// the seqlen_q rows (query n: head hk * G + n / Sq, row n % Sq); one workgroup takes NQ
+// of them, so each key row it loads serves NQ dot products instead of one.  Each
+// query keeps its own visible range, ALiBi slope and online-softmax state.
+template <int HD, bool ALIBI, bool KVC, int NQ>
+__global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) {
+  constexpr int LPR = HD / 8;
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNROLL = NQ <= 2 ? DEC_UNROLL : DEC_UNROLL / 2;  // registers: NQ copies of the state
+  constexpr int STEP = UNROLL * RPW;
+  __shared__ float sm_m[4][NQ], sm_l[4][NQ];
+  __shared__ float sm_acc[4][NQ][HD];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane / LPR;
+  const int cidx = lane % LPR;
+
+  const int Sq = p.seqlen_q;
+  const int G = p.nheads / p.nheads_k;
+  const int nq_total = G * Sq;
+  const int nchunks = (nq_total + NQ - 1) / NQ;
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int qc = w % nchunks;
+  w /= nchunks;
+  const int split = w % p.num_splits;
+  w /= p.num_splits;
+  const int hk = w % p.nheads_k;
+  const int b = w / p.nheads_k;
+  const int Sk = KVC ? p.cache_seqlens[b] + p.seqlen_new : p.seqlen_k;
+
+  const long row_stride = (long)p.nheads * HD;
+  const long kv_stride = (long)p.nheads_k * HD;
+  const int row_bytes = (int)kv_stride * 2;
+  const int s_lo = min(Sk, split * p.split_len);
+  const int s_hi = min(Sk, s_lo + p.split_len);
+
+  const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
+  float qv[NQ][8], slope[NQ];
+  int q_lo[NQ], q_hi[NQ], q_pos[NQ];
+  int lo = s_hi, hi = s_lo;  // union of the queries' visible ranges in this split
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int n = qc * NQ + j;
+    const bool valid = n < nq_total;
+    const int h = hk * G + (valid ? n / Sq : 0);
+    const int i = valid ? n % Sq : 0;
+    q_pos[j] = i + Sk - Sq;
+    int l0 = s_lo, h0 = s_hi;
+    if (p.window_left >= 0) l0 = max(l0, q_pos[j] - p.window_left);
+    if (p.window_right >= 0) h0 = min(h0, q_pos[j] + p.window_right + 1);
+    if (!valid) h0 = l0;  // an empty query
+    q_lo[j] = l0;
+    q_hi[j] = h0;
+    if (h0 > l0) {
+      lo = min(lo, l0);
+      hi = max(hi, h0);
+    }
+    const u32x4 raw = valid ? *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and
+                            : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[j][2 * e] = bf16_lo(raw[e]) * c;
+      qv[j][2 * e + 1] = bf16_hi(raw[e]) * c;
+    }
+    slope[j] = 0.f;
+    if constexpr (ALIBI) slope[j] = p.alibi[h] * kLog2e;
+  }
+  if (hi <= lo) lo = hi = 0;  // no query sees a key of this split
+  const long kvb = KVC ? (long)hk * HD : (long)b * Sk * kv_stride + (long)hk * HD;
+  const int first = KVC ? (lo & ~(STEP - 1)) : lo;
+
+  float m_run[NQ], l_run[NQ], acc[NQ][8];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
+
+  for (int base = first + wave * STEP; base < hi; base += 4 * STEP) {
+    const int nrec = min(hi - base, STEP) * row_bytes;
+    long row0 = base;
+    if constexpr (KVC) {
+      if (p.block_table != nullptr)
+        row0 = (long)p.block_table[(long)b * p.max_blocks + (base >> p.page_shift)] * p.page_size +
+               (base & (p.page_size - 1));
+      else
+        row0 = (long)b * p.page_size + base;
+    }
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvb + row0 * kv_stride), (short)0, nrec,
+                                                       0x00020000);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvb + row0 * kv_stride), (short)0, nrec,
+                                                       0x00020000);
+    u32x4 kr[UNROLL], vr[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int off = (u * RPW + g) * row_bytes + cidx * 16;
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, DEC_CPOL));
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, DEC_CPOL));
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float sj[UNROLL];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part = fmaf(qv[j][2 * e], bf16_lo(kr[u][e]), part);
+          part = fmaf(qv[j][2 * e + 1], bf16_hi(kr[u][e]), part);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+        const int key = base + u * RPW + g;
+        if constexpr (ALIBI) part -= slope[j] * fabsf((float)(q_pos[j] - key));
+        sj[u] = (key >= q_lo[j] && key < q_hi[j]) ? part : -INFINITY;
+        bmax = fmaxf(bmax, sj[u]);
+      }
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+      const float m_new = fmaxf(m_run[j], bmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[j] - m_use);
+      l_run[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const float pu = fast_exp2(sj[u] - m_use);
+        l_run[j] += pu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[j][2 * e] = fmaf(pu, bf16_lo(vr[u][e]), acc[j][2 * e]);
+          acc[j][2 * e + 1] = fmaf(pu, bf16_hi(vr[u][e]), acc[j][2 * e + 1]);
+        }
+      }
+      m_run[j] = m_new;
+    }
+  }
+
+  // merge the row groups of each wave, then the four waves, per query
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      l_run[j] += __shfl_xor(l_run[j], o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] += __shfl_xor(acc[j][e], o);
+    }
+    if (lane == 0) {
+      sm_m[wave][j] = m_run[j];
+      sm_l[wave][j] = l_run[j];
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][j][cidx * 8 + e] = acc[j][e];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int n = qc * NQ + j;
+    if (n >= nq_total) break;
+    const int h = hk * G + n / Sq, i = n % Sq;
+    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float wgt[4], L = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      wgt[x] = fast_exp2(sm_m[x][j] - M_use);
+      L += sm_l[x][j] * wgt[x];
+    }
+    const long rowid = (((long)split * p.batch + b) * p.nheads + h) * Sq + i;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* out = (float*)p.out + rowid * HD;
+    for (int d = tid; d < HD; d += DEC_THREADS) {
+      float o = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o = fmaf(sm_acc[x][j][d], wgt[x], o);
+      out[d] = o * inv;
+    }
+    if (tid == 0) p.lse[rowid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+  }
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int PER_LANE = HD / 64;
@@ -290,8 +482,35 @@ __global__ __launch_bounds__(256) void kvcache_prep_kernel(FwdParams p, const ui
   }
 }
 
+template <int HD, bool ALIBI, bool KVC, int NQ>
+static void launch_group(const FwdParams& p, hipStream_t stream) {
+  const int nq_total = p.nheads / p.nheads_k * p.seqlen_q;
+  const long nblocks = (long)p.batch * p.nheads_k * p.num_splits * ((nq_total + NQ - 1) / NQ);
+  hipLaunchKernelGGL((decode_group_kernel<HD, ALIBI, KVC, NQ>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
+                     stream, p);
+}
+
+// Queries one decode workgroup serves when a K/V head has nq_total of them.
+int decode_queries_per_block(int nq_total) { return nq_total <= 1 ? 1 : nq_total <= 2 ? 2 : nq_total <= 4 ? 4 : 8; }
+
+template <int HD, bool ALIBI, bool KVC>
+static void launch_group_nq(const FwdParams& p, hipStream_t stream) {
+  switch (decode_queries_per_block(p.nheads / p.nheads_k * p.seqlen_q)) {
+    case 2: launch_group<HD, ALIBI, KVC, 2>(p, stream); break;
+    case 4: launch_group<HD, ALIBI, KVC, 4>(p, stream); break;
+    default: launch_group<HD, ALIBI, KVC, 8>(p, stream); break;
+  }
+}
+
 template <int HD, bool KVC>
 static hipError_t launch_decode_kvc(const FwdParams& p, hipStream_t stream) {
+  // several queries per K/V head (grouped heads or seqlen_q > 1): the grouped kernel
+  // loads each key row once for all of them
+  if (p.nheads / p.nheads_k * p.seqlen_q > 1) {
+    if (p.alibi) launch_group_nq<HD, true, KVC>(p, stream);
+    else launch_group_nq<HD, false, KVC>(p, stream);
+    return hipGetLastError();
+  }
   const long nblocks = (long)p.batch * p.nheads * p.num_splits * p.seqlen_q;
   if (p.alibi)
     hipLaunchKernelGGL((decode_split_kernel<HD, true, KVC>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream,

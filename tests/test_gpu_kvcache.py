@@ -32,6 +32,7 @@ KVC_CASES = [
     (2, 3, 4, 2, 128, None, 300, (0, 250), 3, 64, False, -1, False, 0),
     (1, 8, 2, 2, 64, None, 1000, (900,), 8, 64, True, 100, True, 7),
     (4, 1, 16, 16, 128, 256, 4, (1023, 1, 500, 768), 1, 128, True, -1, False, 0),
+    (2, 1, 12, 4, 128, 64, 4, (150, 77), 1, 0, True, -1, True, 0),
 ]
 
 
