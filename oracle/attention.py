@@ -12,8 +12,8 @@ Sources (the pages are web articles; each is cited by title and section):
     - section "使用示例": the method computes softmax(Q @ K^T * softmax_scale) @ V
       exactly (the title says "准确", exact).
     - section "参数说明": softmax_scale defaults to 1/sqrt(headdim); window_size
-      (left, right), (-1, -1) = no window; alibi_slopes fp32 (nheads,) add
-      -slope * |i - j| to the score of query i and key j.
+      (left, right), (-1, -1) = no window; alibi_slopes fp32 (nheads,) or
+      (batch, nheads) add -slope * |i - j| to the score of query i and key j.
     - section "算法 / 前向传播": the forward also writes the row-wise
       logsumexp L, which the backward uses.
     - section "算法 / 反向传播": the backward recomputes P from L alone.
@@ -58,6 +58,17 @@ def as_f64(x) -> np.ndarray:
 
         return x.detach().to(device="cpu", dtype=torch.float64).numpy()
     return np.asarray(x, dtype=np.float64)
+
+
+def slope_table(alibi_slopes, batch: int, nheads: int) -> Optional[np.ndarray]:
+    """ALiBi slopes as a [batch, nheads] fp64 table [FA-overview §参数说明: the slopes are
+    (nheads,), shared by every batch element, or (batch, nheads)], or None."""
+    if alibi_slopes is None:
+        return None
+    sl = as_f64(alibi_slopes)
+    if sl.ndim == 1:
+        return np.tile(sl.reshape(1, nheads), (batch, 1))
+    return sl.reshape(batch, nheads)
 
 
 def aligned_key_position(i, seqlen_q: int, seqlen_k: int):
@@ -149,13 +160,13 @@ def attention_forward(q, k, v, softmax_scale: float, causal: bool = False, windo
     """
     qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
     batch, seqlen_q, nheads, headdim = qd.shape
-    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    slopes = slope_table(alibi_slopes, batch, nheads)
     out = np.zeros((batch, seqlen_q, nheads, headdim))
     lse = np.zeros((batch, nheads, seqlen_q))
     for b in range(batch):
         for h in range(nheads):
             kh, vh = kd[b, :, h, :], vd[b, :, h, :]
-            slope = None if slopes is None else float(slopes[h])
+            slope = None if slopes is None else float(slopes[b, h])
             for r0 in range(0, seqlen_q, row_chunk):
                 rows = np.arange(r0, min(seqlen_q, r0 + row_chunk))
                 o, l = head_rows(qd[b, rows, h, :], kh, vh, rows, seqlen_q, softmax_scale, causal,
@@ -182,7 +193,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale: float, 
     ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
     total_q, nheads, headdim = qd.shape
     group = nheads // kd.shape[1]
-    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    slopes = slope_table(alibi_slopes, len(cq) - 1, nheads)  # one row per sequence when (batch, nheads)
     out = np.zeros((total_q, nheads, headdim))
     lse = np.full((nheads, total_q), -np.inf)
     for b in range(len(cq) - 1):
@@ -190,7 +201,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale: float, 
         k0, sk = ck[b], ck[b + 1] - ck[b]
         for h in range(nheads):
             kh, vh = kd[k0:k0 + sk, h // group, :], vd[k0:k0 + sk, h // group, :]
-            slope = None if slopes is None else float(slopes[h])
+            slope = None if slopes is None else float(slopes[b, h])
             for r0 in range(0, sq, row_chunk):
                 rows = np.arange(r0, min(sq, r0 + row_chunk))
                 o, l = head_rows(qd[q0 + rows, h, :], kh, vh, rows, sq, softmax_scale, causal, window_left,
@@ -215,7 +226,7 @@ def attention_backward(q, k, v, dout, softmax_scale: float, causal: bool = False
     qd, kd, vd, gd = as_f64(q), as_f64(k), as_f64(v), as_f64(dout)
     batch, seqlen_q, nheads, headdim = qd.shape
     seqlen_k = kd.shape[1]
-    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    slopes = slope_table(alibi_slopes, batch, nheads)
     dq, dk, dv = np.zeros(qd.shape), np.zeros(kd.shape), np.zeros(vd.shape)
     rows = np.arange(seqlen_q)
     keep = visible_mask(seqlen_q, seqlen_k, causal, window_left, window_right, rows)
@@ -224,7 +235,7 @@ def attention_backward(q, k, v, dout, softmax_scale: float, causal: bool = False
             qh, kh, vh, gh = qd[b, :, h], kd[b, :, h], vd[b, :, h], gd[b, :, h]
             scores = softmax_scale * (qh @ kh.T)
             if slopes is not None:
-                scores = scores + alibi_bias(float(slopes[h]), seqlen_q, seqlen_k, rows)
+                scores = scores + alibi_bias(float(slopes[b, h]), seqlen_q, seqlen_k, rows)
             p, _ = softmax_rows(scores, keep)
             dv[b, :, h] = p.T @ gh
             dp = gh @ vh.T
@@ -241,6 +252,16 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     import torch  # local import: rounding through torch's own RNE conversion
 
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to IEEE binary16 (round to nearest, ties to even; overflow to
+    inf, gradual underflow), returned as fp64: the fp16 counterpart of round_bf16."""
+    with np.errstate(over="ignore"):  # overflow to inf is the IEEE result
+        return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+ROUNDING = {"bf16": round_bf16, "fp16": round_fp16}
 
 
 def rotary(x: np.ndarray, positions: np.ndarray, cos: np.ndarray, sin: np.ndarray, rotary_dim: int) -> np.ndarray:
@@ -260,7 +281,7 @@ def rotary(x: np.ndarray, positions: np.ndarray, cos: np.ndarray, sin: np.ndarra
 
 def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, block_table=None, k_new=None,
                       v_new=None, rotary_cos=None, rotary_sin=None, rotary_dim: int = 0, causal: bool = False,
-                      window_left: int = -1, window_right: int = -1, alibi_slopes=None):
+                      window_left: int = -1, window_right: int = -1, alibi_slopes=None, storage: str = "bf16"):
     """Decode against a KV cache, fp64 [FA-overview §2.2 (KV-cache decoding: rotary embedding,
     in-place cache update), §2.5 (paged KV cache)].
 
@@ -269,7 +290,8 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, 
     with block_table None.  Sequence b holds cache_seqlens[b] keys; the new rows k_new, v_new
     [B, S_new, H_k, D] are appended at positions cache_seqlens[b] .. + S_new - 1.  With rotary
     tables, q row i and new key row i are rotated at position cache_seqlens[b] + i and rounded
-    to bf16 (the cache stores bf16 and the kernels multiply bf16 operands).  Query head h reads
+    to the storage type `storage` ("bf16" or "fp16": the cache stores it and the kernels
+    multiply operands of that type).  Query head h reads
     K/V head h // (H / H_k).  Returns out [B, Sq, H, D], lse [B, H, Sq], and the appended key
     and value rows as stored [B, S_new, H_k, D] (None without new rows).
     """
@@ -290,6 +312,8 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, 
     k_app = None if kn is None else np.zeros(kn.shape)
     v_app = None if vn is None else np.zeros(vn.shape)
     heads = [h // group for h in range(nheads)]
+    slopes = slope_table(alibi_slopes, batch, nheads)
+    rnd = ROUNDING[storage]
     for b in range(batch):
         rows = []
         for j in range(lens[b]):  # the cached keys, through the block table
@@ -302,14 +326,14 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, 
         if snew:
             knb, vnb = kn[b], vn[b]
             if use_rot:
-                knb = round_bf16(rotary(knb, lens[b] + np.arange(snew), cos, sin, rotary_dim))
+                knb = rnd(rotary(knb, lens[b] + np.arange(snew), cos, sin, rotary_dim))
             k_app[b], v_app[b] = knb, vnb
             kb, vb = np.concatenate([kb, knb]), np.concatenate([vb, vnb])
         qb = qd[b]
         if use_rot:
-            qb = round_bf16(rotary(qb, lens[b] + np.arange(seqlen_q), cos, sin, rotary_dim))
+            qb = rnd(rotary(qb, lens[b] + np.arange(seqlen_q), cos, sin, rotary_dim))
         o, l = attention_forward(qb[None], kb[:, heads][None], vb[:, heads][None], softmax_scale, causal,
-                                 window_left, window_right, alibi_slopes)
+                                 window_left, window_right, None if slopes is None else slopes[b:b + 1])
         out[b], lse[b] = o[0], l[0]
     return out, lse, k_app, v_app
 
@@ -325,7 +349,7 @@ def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_
     """
     samples = list(samples)
     seqlen_q, headdim = q.shape[1], q.shape[3]
-    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    slopes = slope_table(alibi_slopes, q.shape[0], q.shape[2])
     out = np.zeros((len(samples), headdim))
     lse = np.zeros(len(samples))
     groups = {}
@@ -335,7 +359,7 @@ def attention_sampled(q, k, v, samples: Iterable[Tuple[int, int, int]], softmax_
         kh, vh = as_f64(k[b, :, h, :]), as_f64(v[b, :, h, :])
         rows = np.array([i for _, i in items], dtype=np.int64)
         qr = as_f64(q[b, :, h, :])[rows]
-        slope = None if slopes is None else float(slopes[h])
+        slope = None if slopes is None else float(slopes[b, h])
         o, l = head_rows(qr, kh, vh, rows, seqlen_q, softmax_scale, causal, window_left, window_right, slope)
         for r, (n, _) in enumerate(items):
             out[n] = o[r]
@@ -360,14 +384,14 @@ def splitkv_partials(q, k, v, softmax_scale: float, num_splits: int, causal: boo
     qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
     batch, seqlen_q, nheads, headdim = qd.shape
     seqlen_k = kd.shape[1]
-    slopes = None if alibi_slopes is None else as_f64(alibi_slopes).reshape(-1)
+    slopes = slope_table(alibi_slopes, batch, nheads)
     out_p = np.zeros((num_splits, batch, nheads, seqlen_q, headdim))
     lse_p = np.zeros((num_splits, batch, nheads, seqlen_q))
     rows = np.arange(seqlen_q)
     for s, key_range in enumerate(split_bounds(seqlen_k, num_splits)):
         for b in range(batch):
             for h in range(nheads):
-                slope = None if slopes is None else float(slopes[h])
+                slope = None if slopes is None else float(slopes[b, h])
                 o, l = head_rows(qd[b, :, h, :], kd[b, :, h, :], vd[b, :, h, :], rows, seqlen_q,
                                  softmax_scale, causal, window_left, window_right, slope, key_range)
                 out_p[s, b, h] = o
@@ -406,7 +430,11 @@ def brute_force(q, k, v, softmax_scale: float, causal: bool = False, window_left
     qd, kd, vd = as_f64(q), as_f64(k), as_f64(v)
     batch, seqlen_q, nheads, headdim = qd.shape
     seqlen_k = kd.shape[1]
-    slopes = None if alibi_slopes is None else [float(s) for s in as_f64(alibi_slopes).reshape(-1)]
+    slopes = None
+    if alibi_slopes is not None:
+        arr = as_f64(alibi_slopes)
+        # (nheads,): every batch element uses the same slopes; (batch, nheads): row b
+        slopes = [[float(x) for x in (arr if arr.ndim == 1 else arr[b])] for b in range(batch)]
     out = [[[[0.0] * headdim for _ in range(nheads)] for _ in range(seqlen_q)] for _ in range(batch)]
     lse = [[[0.0] * seqlen_q for _ in range(nheads)] for _ in range(batch)]
     for b in range(batch):
@@ -424,7 +452,7 @@ def brute_force(q, k, v, softmax_scale: float, causal: bool = False, window_left
                     dot = math.fsum(qd[b, i, h, d] * kd[b, j, h, d] for d in range(headdim))
                     s = softmax_scale * dot
                     if slopes is not None:
-                        s -= slopes[h] * abs(pos - j)
+                        s -= slopes[b][h] * abs(pos - j)
                     scores[j] = s
                 if not scores:
                     lse[b][h][i] = -math.inf

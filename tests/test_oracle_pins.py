@@ -370,11 +370,13 @@ def _rot_complex(x, pos, cos, sin, rd):
     return y
 
 
-def pin_kvcache():
+def pin_kvcache(storage="bf16"):
     """KV-cache decode: rotary equals complex multiplication by e^{i theta}; a paged cache
     with a shuffled block table equals the contiguous cache; the result equals the scalar
     brute force on the explicitly gathered keys, with the new rows appended (rotated and
-    rounded to bf16 when rotary tables are given); the appended rows are returned as stored."""
+    rounded to the storage type when rotary tables are given); the appended rows are
+    returned as stored."""
+    rnd = oracle.round_bf16 if storage == "bf16" else oracle.round_fp16
     rng = np.random.default_rng(70)
     batch, sq, nh, nhk, d, page, rd = 3, 2, 4, 2, 8, 4, 6
     theta = rng.uniform(0, 2 * np.pi, (40, rd // 2))
@@ -402,7 +404,7 @@ def pin_kvcache():
                                              (False, -1, None, True, True), (True, -1, None, True, True)]:
         kw = dict(k_new=knew if use_new else None, v_new=vnew if use_new else None,
                   rotary_cos=cos if use_rot else None, rotary_sin=sin if use_rot else None, rotary_dim=rd,
-                  causal=causal, window_left=wl, alibi_slopes=al)
+                  causal=causal, window_left=wl, alibi_slopes=al, storage=storage)
         o1, l1, ka1, va1 = oracle.attention_kvcache(q, kc, vc, lens, 0.4, **kw)
         o2, l2, ka2, va2 = oracle.attention_kvcache(q, kp, vp, lens, 0.4, block_table=table, **kw)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
@@ -411,16 +413,91 @@ def pin_kvcache():
             if use_new:
                 kn = knew[b]
                 if use_rot:
-                    kn = oracle.round_bf16(_rot_complex(kn, lens[b] + np.arange(2), cos, sin, rd))
+                    kn = rnd(_rot_complex(kn, lens[b] + np.arange(2), cos, sin, rd))
                 assert np.array_equal(ka1[b], kn) and np.array_equal(va1[b], vnew[b])
                 kb, vb = np.concatenate([kb, kn]), np.concatenate([vb, vnew[b]])
             if use_rot:
-                qb = oracle.round_bf16(_rot_complex(qb, lens[b] + np.arange(sq), cos, sin, rd))
+                qb = rnd(_rot_complex(qb, lens[b] + np.arange(sq), cos, sin, rd))
             ob, lb = oracle.brute_force(qb[None], kb[:, heads][None], vb[:, heads][None], 0.4, causal, wl, -1, al)
             assert np.allclose(o1[b], ob[0], atol=1e-12)
             assert np.array_equal(np.isneginf(l1[b]), np.isneginf(lb[0]))
             fin = np.isfinite(lb[0])
             assert np.allclose(l1[b][fin], lb[0][fin], atol=1e-12)
+
+
+def pin_round_fp16():
+    """Rounding to IEEE binary16 from first principles: spacing 2^-10 on [1, 2), ties to
+    the even neighbour, largest finite value 65504 (a tie at 65520 goes to infinity),
+    subnormal spacing 2^-24."""
+    cases = [(1 + 2.0 ** -11, 1.0), (1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9), (1 + 2.0 ** -11 + 2.0 ** -30, 1 + 2.0 ** -10),
+             (-(1 + 2.0 ** -11), -1.0), (65504.0, 65504.0), (65519.99, 65504.0), (65520.0, math.inf),
+             (2.0 ** -25, 0.0), (3 * 2.0 ** -25, 2.0 ** -23), (2.0 ** -25 + 2.0 ** -40, 2.0 ** -24),
+             (2.0 ** -14 - 2.0 ** -25, 2.0 ** -14), (0.1, 1638.0 / 16384.0)]
+    x = np.array([c[0] for c in cases])
+    assert np.array_equal(oracle.round_fp16(x), np.array([c[1] for c in cases]))
+
+
+def pin_per_batch_slopes():
+    """ALiBi slopes of shape (batch, nheads) [FA-overview §参数说明]: batch element (or packed
+    sequence) b uses row b.  Checked against the scalar brute force, which reads the table
+    on its own, and through every oracle entry that takes slopes; a table whose rows are
+    all equal is the (nheads,) form."""
+    rng = np.random.default_rng(80)
+    B, Sq, Sk, H, D = 3, 5, 7, 2, 4
+    q, k, v = rand((B, Sq, H, D), 81), rand((B, Sk, H, D), 82), rand((B, Sk, H, D), 83)
+    sl = rng.uniform(0.05, 1.0, (B, H))
+
+    def close(a, b, la, lb):
+        assert np.allclose(a, b, atol=1e-12)
+        assert np.array_equal(np.isneginf(la), np.isneginf(lb))
+        fin = np.isfinite(lb)
+        assert np.allclose(la[fin], lb[fin], atol=1e-12)
+
+    for causal, wl in [(False, -1), (True, 2)]:
+        o, l = oracle.attention_forward(q, k, v, 0.7, causal, wl, -1, sl)
+        ob, lb = oracle.brute_force(q, k, v, 0.7, causal, wl, -1, sl)
+        close(o, ob, l, lb)
+        # split + combine, and sampled rows, with the same table
+        oc, lc = oracle.combine(*oracle.splitkv_partials(q, k, v, 0.7, 3, causal, wl, -1, sl))
+        close(oc, ob, lc, lb)
+        samples = [(2, 1, 4), (0, 0, 0), (1, 1, 3)]
+        os_, ls_ = oracle.attention_sampled(q, k, v, samples, 0.7, causal, wl, -1, sl)
+        for n, (b, h, i) in enumerate(samples):
+            close(os_[n], ob[b, i, h], ls_[n:n + 1], lb[b, h, i:i + 1])
+    o_eq, _ = oracle.attention_forward(q, k, v, 0.7, True, -1, -1, np.tile(sl[1], (B, 1)))
+    o_1d, _ = oracle.attention_forward(q, k, v, 0.7, True, -1, -1, sl[1])
+    assert np.array_equal(o_eq, o_1d)
+
+    # packed sequences: sequence b, of its own lengths, uses row b
+    sq_b, sk_b = [5, 3, 0], [7, 2, 4]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(sq_b)]), np.concatenate([[0], np.cumsum(sk_b)])
+    qp = np.concatenate([q[b, :sq_b[b]] for b in range(B)])
+    kp = np.concatenate([k[b, :sk_b[b]] for b in range(B)])
+    vp = np.concatenate([v[b, :sk_b[b]] for b in range(B)])
+    ov, lv = oracle.attention_varlen(qp, kp, vp, cu_q, cu_k, 0.7, True, -1, -1, sl)
+    for b in range(B):
+        if sq_b[b] == 0:
+            continue
+        ob, lb = oracle.brute_force(q[b:b + 1, :sq_b[b]], k[b:b + 1, :sk_b[b]], v[b:b + 1, :sk_b[b]], 0.7, True, -1,
+                                    -1, sl[b])
+        close(ov[cu_q[b]:cu_q[b + 1]], ob[0], lv[:, cu_q[b]:cu_q[b + 1]], lb[0])
+
+    # backward: element b of the batch equals the (nheads,) form with row b alone
+    g = rand((B, Sq, H, D), 84)
+    dq, dk, dv = oracle.attention_backward(q, k, v, g, 0.7, True, -1, -1, sl)
+    for b in range(B):
+        ref = oracle.attention_backward(q[b:b + 1], k[b:b + 1], v[b:b + 1], g[b:b + 1], 0.7, True, -1, -1, sl[b])
+        for x, r in zip((dq, dk, dv), ref):
+            assert np.allclose(x[b], r[0], atol=1e-13)
+
+    # KV cache (contiguous, grouped heads): brute force on each sequence's keys
+    lens = [4, 0, 6]
+    kc, vc = rand((B, 8, 1, D), 85), rand((B, 8, 1, D), 86)
+    o, l, _, _ = oracle.attention_kvcache(q[:, :2], kc, vc, lens, 0.7, causal=True, alibi_slopes=sl)
+    for b in range(B):
+        ob, lb = oracle.brute_force(q[b:b + 1, :2], kc[b:b + 1, :lens[b], [0, 0]], vc[b:b + 1, :lens[b], [0, 0]], 0.7,
+                                    True, -1, -1, sl[b])
+        close(o[b], ob[0], l[b], lb[0])
 
 
 def pin_bf16_widening():
@@ -507,6 +584,18 @@ def test_kvcache():
     pin_kvcache()
 
 
+def test_kvcache_fp16_storage():
+    pin_kvcache("fp16")
+
+
+def test_round_fp16():
+    pin_round_fp16()
+
+
+def test_per_batch_slopes():
+    pin_per_batch_slopes()
+
+
 def test_bf16_widening():
     pin_bf16_widening()
 
@@ -531,6 +620,9 @@ def _all_pins():
     pin_backward_autograd()
     pin_backward_closed_forms()
     pin_kvcache()
+    pin_kvcache("fp16")
+    pin_round_fp16()
+    pin_per_batch_slopes()
 
 
 def _top_left(i, seqlen_q, seqlen_k):
@@ -651,6 +743,23 @@ def _rotary_wrong_sign(x, positions, cos, sin, rotary_dim):
     return _ORIG_ROTARY(x, positions, cos, -sin, rotary_dim)
 
 
+def _slopes_first_row(alibi_slopes, batch, nheads):
+    # a (batch, nheads) table read as if every batch element had row 0
+    t = _ORIG_SLOPES(alibi_slopes, batch, nheads)
+    return None if t is None else np.tile(t[0], (batch, 1))
+
+
+def _round_fp16_via_bf16(x):
+    return oa.round_bf16(x)
+
+
+def _round_fp16_truncate(x):
+    # toward zero instead of to nearest
+    y = np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+    over = np.abs(y) > np.abs(x)
+    return np.where(over, np.nextafter(y.astype(np.float16), np.float16(0)).astype(np.float64), y)
+
+
 _ORIG_HEAD_ROWS = oa.head_rows
 _ORIG_ROTARY = oa.rotary
 _ORIG_VARLEN = oa.attention_varlen
@@ -658,6 +767,7 @@ _ORIG_ALIBI = oa.alibi_bias
 _ORIG_SOFTMAX = oa.softmax_rows
 _ORIG_VISIBLE = oa.visible_mask
 _ORIG_COMBINE = oa.combine
+_ORIG_SLOPES = oa.slope_table
 
 
 @pytest.mark.parametrize("target,replacement", [
@@ -675,6 +785,9 @@ _ORIG_COMBINE = oa.combine
     ("attention_backward", _bwd_variant(unscaled_dk=True)),
     ("attention_backward", _bwd_variant(dv_from_dp=True)),
     ("rotary", _rotary_wrong_sign),
+    ("slope_table", _slopes_first_row),
+    ("round_fp16", _round_fp16_via_bf16),
+    ("round_fp16", _round_fp16_truncate),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, replacement):
     """Each planted oracle mistake must make at least one pin fail."""
