@@ -16,8 +16,8 @@ Printed: ONE JSON line with the contract fields plus
   extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k), the
                 split-KV decode workload in HBM GB/s, a packed batch of causal
                 sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), the
-                backward (fa_bwd) on the benchmark shape, and a paged-KV-cache decode
-                step (fa_fwd_kvcache).
+                backward (fa_bwd) on the benchmark shape, a paged-KV-cache decode
+                step (fa_fwd_kvcache), and the benchmark shape with fp16 tensors.
 """
 
 from __future__ import annotations
@@ -225,6 +225,24 @@ def varlen_bench(dev, reps: int, warmup: int):
             "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4), "algorithmic_gflop": round(flops / 1e9, 2)}
 
 
+def fp16_bench(dev, reps: int, warmup: int):
+    """The benchmark shape (non-causal and causal) with fp16 q/k/v/out: the same kernels
+    with the fp16 matrix-core instruction, against the same dense peak."""
+    res = {}
+    for name in ("bench_s2048", "bench_s2048_causal"):
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev,
+                           dtype=torch.float16)
+        case = FwdCase(w, q, k, v)
+        for _ in range(warmup):
+            case.launch()
+        mean_ms, min_ms = time_events(case.launch, reps)
+        tf = case.flops / (mean_ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4)}
+    return res
+
+
 def kvcache_bench(dev, reps: int, warmup: int):
     """fa_fwd_kvcache on the decode workload's sizes with a paged cache: batch 8, 16 query
     heads over 4 K/V heads x 128, 32767 cached keys + 1 appended (rotary on q and the new
@@ -379,14 +397,15 @@ def main():
                    "headdim": base.headdim, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "fa::fwd_kernel<128,4,false,false>", "per_launch": per_case},
+                     "kernel": "fa::fwd_kernel<128,4,false,false,__bf16>", "per_launch": per_case},
     }
     if not args.no_extra:
         result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
                            "decode": decode_bench(dev, reps=20, warmup=3),
                            "varlen_gqa": varlen_bench(dev, reps=10, warmup=3),
                            "backward": backward_bench(dev, reps=10, warmup=5),
-                           "kvcache_paged": kvcache_bench(dev, reps=20, warmup=5)}
+                           "kvcache_paged": kvcache_bench(dev, reps=20, warmup=5),
+                           "fp16_fwd": fp16_bench(dev, reps=20, warmup=10)}
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

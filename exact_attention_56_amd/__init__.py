@@ -1,10 +1,12 @@
-"""MI355X (gfx950) exact-attention forward: thin Python binding over libfa_mi355x.so.
+"""MI355X (gfx950) exact attention: thin Python binding over libfa_mi355x.so.
 
 The binding only marshals arguments: it checks dtypes, devices, shapes and
 contiguity, allocates outputs with torch when asked to, and passes raw device
 pointers and torch's current HIP stream to the C ABI declared in include/fa.h.
 Every step of the computation runs in the library's HIP kernels; there is no
 other implementation to fall back to.  A missing library raises at the first call.
+q/k/v (and out, the gradients and the KV cache) are torch.bfloat16 or torch.float16,
+all of one type; alibi_slopes are fp32 of shape (nheads,) or (batch, nheads).
 
 Functions
   flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
@@ -34,6 +36,9 @@ _LIB = None
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
 
 FA_OK = 0
+FA_BF16 = 0
+FA_FP16 = 1
+_DTYPES = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
 
 
 class FAError(RuntimeError):
@@ -50,18 +55,19 @@ def load_library() -> ctypes.CDLL:
                            "(python -m exact_attention_56_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
+    # every alibi_slopes pointer is followed by alibi_per_batch and dtype
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_fwd.restype = i
-    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, vp]
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, i, vp]
     lib.fa_fwd_splitkv.restype = i
-    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, i, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i,
-                                   i, f, i, i, i, vp, i, vp]
+                                   i, f, i, i, i, vp, i, i, i, vp]
     lib.fa_fwd_kvcache.restype = i
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_bwd.restype = i
-    lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.fa_combine.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -98,10 +104,22 @@ def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=N
         raise ValueError(f"{name} must be contiguous")
 
 
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be torch.bfloat16 or torch.float16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
 def _check_qkv(q, k, v):
-    _require(q, "q", torch.bfloat16, 4)
-    _require(k, "k", torch.bfloat16, 4, q.device)
-    _require(v, "v", torch.bfloat16, 4, q.device)
+    _dtype_code(q, "q")
+    for t, name in ((k, "k"), (v, "v")):
+        if isinstance(t, torch.Tensor) and t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
+    _require(q, "q", q.dtype, 4)
+    _require(k, "k", q.dtype, 4, q.device)
+    _require(v, "v", q.dtype, 4, q.device)
     b, sq, h, d = q.shape
     if k.shape != v.shape:
         raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
@@ -110,13 +128,16 @@ def _check_qkv(q, k, v):
     return b, sq, k.shape[1], h, d
 
 
-def _alibi(alibi_slopes, nheads, device):
+def _alibi(alibi_slopes, batch, nheads, device):
+    """(slopes, alibi_per_batch) for slopes of shape (nheads,) or (batch, nheads)."""
     if alibi_slopes is None:
-        return None
-    _require(alibi_slopes, "alibi_slopes", torch.float32, 1, device)
-    if alibi_slopes.shape[0] != nheads:
-        raise ValueError(f"alibi_slopes must have shape ({nheads},)")
-    return alibi_slopes
+        return None, 0
+    _require(alibi_slopes, "alibi_slopes", torch.float32, alibi_slopes.dim(), device)
+    if tuple(alibi_slopes.shape) == (nheads,):
+        return alibi_slopes, 0
+    if tuple(alibi_slopes.shape) == (batch, nheads):
+        return alibi_slopes, 1
+    raise ValueError(f"alibi_slopes must have shape ({nheads},) or ({batch}, {nheads})")
 
 
 def _scale(softmax_scale, headdim) -> float:
@@ -125,22 +146,22 @@ def _scale(softmax_scale, headdim) -> float:
 
 def fwd(q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
         alibi_slopes=None) -> None:
-    """fa_fwd on preallocated out [B,Sq,H,D] bf16 and lse [B,H,Sq] fp32."""
+    """fa_fwd on preallocated out [B,Sq,H,D] (q's dtype) and lse [B,H,Sq] fp32."""
     b, sq, sk, h, d = _check_qkv(q, k, v)
-    _require(out, "out", torch.bfloat16, 4, q.device)
+    _require(out, "out", q.dtype, 4, q.device)
     _require(lse, "lse", torch.float32, 3, q.device)
     if out.shape != q.shape or tuple(lse.shape) != (b, h, sq):
         raise ValueError("out must match q and lse must be [batch, nheads, seqlen_q]")
-    slopes = _alibi(alibi_slopes, h, q.device)
+    slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
     _check(load_library().fa_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), b, sq, sk, h, d,
         _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]), int(window_size[1]),
-        _ptr(slopes), _stream_handle(q)))
+        _ptr(slopes), per_batch, _DTYPES[q.dtype], _stream_handle(q)))
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1),
                     alibi_slopes=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Attention forward; returns (out [B,Sq,H,D] bf16, lse [B,H,Sq] fp32)."""
+    """Attention forward; returns (out [B,Sq,H,D] in q's dtype, lse [B,H,Sq] fp32)."""
     b, sq, sk, h, d = _check_qkv(q, k, v)
     out = torch.empty_like(q)
     lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
@@ -150,16 +171,17 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=False, window_size=(-1, 
 
 def fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None) -> None:
-    """fa_fwd_varlen on preallocated out [total_q,H,D] bf16 and lse [H,total_q] fp32.
+    """fa_fwd_varlen on preallocated out [total_q,H,D] (q's dtype) and lse [H,total_q] fp32.
 
     q [total_q, H, D], k/v [total_k, H_k, D] (H_k divides H), cu_seqlens_* int32 [batch+1]
     on the same device.  The cumulative lengths are read by the kernel only: they must
     lie inside the tensors (see fa_fwd_varlen in include/fa.h).
     """
-    _require(q, "q", torch.bfloat16, 3)
-    _require(k, "k", torch.bfloat16, 3, q.device)
-    _require(v, "v", torch.bfloat16, 3, q.device)
-    _require(out, "out", torch.bfloat16, 3, q.device)
+    _dtype_code(q, "q")
+    _require(q, "q", q.dtype, 3)
+    _require(k, "k", q.dtype, 3, q.device)
+    _require(v, "v", q.dtype, 3, q.device)
+    _require(out, "out", q.dtype, 3, q.device)
     _require(lse, "lse", torch.float32, 2, q.device)
     _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
     _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, q.device)
@@ -174,17 +196,17 @@ def fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_
     if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [batch + 1]")
     batch = cu_seqlens_q.shape[0] - 1
-    slopes = _alibi(alibi_slopes, h, q.device)
+    slopes, per_batch = _alibi(alibi_slopes, batch, h, q.device)
     _check(load_library().fa_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
         cu_seqlens_k.data_ptr(), batch, int(max_seqlen_q), int(max_seqlen_k), total_q, h, hk, d,
         _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes),
-        _stream_handle(q)))
+        per_batch, _DTYPES[q.dtype], _stream_handle(q)))
 
 
 def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
                            causal=False, window_size=(-1, -1), alibi_slopes=None):
-    """Packed-sequence forward; returns (out [total_q,H,D] bf16, lse [H,total_q] fp32)."""
+    """Packed-sequence forward; returns (out [total_q,H,D] in q's dtype, lse [H,total_q] fp32)."""
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
     fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
@@ -200,24 +222,26 @@ def fwd_splitkv(q, k, v, out_partial, lse_partial, num_splits, softmax_scale=Non
     _require(lse_partial, "lse_partial", torch.float32, 4, q.device)
     if tuple(out_partial.shape) != (num_splits, b, h, sq, d) or tuple(lse_partial.shape) != (num_splits, b, h, sq):
         raise ValueError("partials must be [num_splits, B, H, Sq, D] and [num_splits, B, H, Sq]")
-    slopes = _alibi(alibi_slopes, h, q.device)
+    slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
     _check(load_library().fa_fwd_splitkv(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out_partial.data_ptr(), lse_partial.data_ptr(),
         b, sq, sk, h, d, _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]),
-        int(window_size[1]), _ptr(slopes), int(num_splits), _stream_handle(q)))
+        int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype], int(num_splits), _stream_handle(q)))
 
 
 def combine(out_partial, lse_partial, out, lse) -> None:
-    """fa_combine: merge [S,B,H,Sq,D] / [S,B,H,Sq] partials into out [B,Sq,H,D] bf16, lse [B,H,Sq]."""
+    """fa_combine: merge [S,B,H,Sq,D] / [S,B,H,Sq] partials into out [B,Sq,H,D] (bf16 or fp16),
+    lse [B,H,Sq]."""
     _require(out_partial, "out_partial", torch.float32, 5)
     _require(lse_partial, "lse_partial", torch.float32, 4, out_partial.device)
-    _require(out, "out", torch.bfloat16, 4, out_partial.device)
+    _dtype_code(out, "out")
+    _require(out, "out", out.dtype, 4, out_partial.device)
     _require(lse, "lse", torch.float32, 3, out_partial.device)
     s, b, h, sq, d = out_partial.shape
     if tuple(lse_partial.shape) != (s, b, h, sq) or tuple(out.shape) != (b, sq, h, d) or tuple(lse.shape) != (b, h, sq):
         raise ValueError("inconsistent shapes for combine")
     _check(load_library().fa_combine(out_partial.data_ptr(), lse_partial.data_ptr(), out.data_ptr(),
-                                     lse.data_ptr(), b, sq, h, d, s, _stream_handle(out)))
+                                     lse.data_ptr(), b, sq, h, d, s, _DTYPES[out.dtype], _stream_handle(out)))
 
 
 def decode(q, k_cache, v_cache, num_splits=16, softmax_scale=None, causal=False, window_size=(-1, -1),
@@ -235,22 +259,23 @@ def decode(q, k_cache, v_cache, num_splits=16, softmax_scale=None, causal=False,
 
 def bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, softmax_scale=None, causal=False, window_size=(-1, -1),
         alibi_slopes=None) -> None:
-    """fa_bwd: gradients into preallocated dq/dk/dv (bf16, shapes of q/k/v); delta [B,H,Sq]
+    """fa_bwd: gradients into preallocated dq/dk/dv (q's dtype, shapes of q/k/v); delta [B,H,Sq]
     fp32 is scratch.  out and lse must be the forward's outputs for the same arguments."""
     b, sq, sk, h, d = _check_qkv(q, k, v)
     for t, name, like in ((out, "out", q), (dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-        _require(t, name, torch.bfloat16, 4, q.device)
+        _require(t, name, q.dtype, 4, q.device)
         if t.shape != like.shape:
             raise ValueError(f"{name} must have shape {tuple(like.shape)}")
     _require(lse, "lse", torch.float32, 3, q.device)
     _require(delta, "delta", torch.float32, 3, q.device)
     if tuple(lse.shape) != (b, h, sq) or tuple(delta.shape) != (b, h, sq):
         raise ValueError("lse and delta must be [batch, nheads, seqlen_q]")
-    slopes = _alibi(alibi_slopes, h, q.device)
+    slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
     _check(load_library().fa_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
         dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), b, sq, sk, h, d, _scale(softmax_scale, d),
-        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), _stream_handle(q)))
+        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype],
+        _stream_handle(q)))
 
 
 def attention_backward(q, k, v, out, lse, dout, softmax_scale=None, causal=False, window_size=(-1, -1),
@@ -268,7 +293,7 @@ def kvcache_decode(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=N
     """fa_fwd_kvcache: appends k_new/v_new (rotated with the rotary tables if given) to the
     cache in place, then attends.  q [B,Sq,H,D]; k_cache/v_cache [num_blocks, page, H_k, D]
     with block_table [B, max_blocks] int32, or [B, capacity, H_k, D] without; cache_seqlens
-    [B] int32.  Returns (out [B,Sq,H,D] bf16, lse [B,H,Sq] fp32)."""
+    [B] int32.  Returns (out [B,Sq,H,D] in q's dtype, lse [B,H,Sq] fp32)."""
     b, sq, h, d = q.shape
     out = torch.empty_like(q)
     lse = torch.empty(b, h, sq, dtype=torch.float32, device=q.device)
@@ -284,9 +309,10 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
                 alibi_slopes=None, num_splits=0) -> None:
     """fa_fwd_kvcache with preallocated out [B,Sq,H,D], lse [B,H,Sq] and split scratch
     out_partial [S,B,H,Sq,D] / lse_partial [S,B,H,Sq] (fp32; S = max_splits)."""
-    _require(q, "q", torch.bfloat16, 4)
-    _require(k_cache, "k_cache", torch.bfloat16, 4, q.device)
-    _require(v_cache, "v_cache", torch.bfloat16, 4, q.device)
+    _dtype_code(q, "q")
+    _require(q, "q", q.dtype, 4)
+    _require(k_cache, "k_cache", q.dtype, 4, q.device)
+    _require(v_cache, "v_cache", q.dtype, 4, q.device)
     _require(cache_seqlens, "cache_seqlens", torch.int32, 1, q.device)
     b, sq, h, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[3] != d:
@@ -304,8 +330,8 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
         raise ValueError("a contiguous cache must be [batch, capacity, H_k, D]")
     snew = 0
     if k_new is not None:
-        _require(k_new, "k_new", torch.bfloat16, 4, q.device)
-        _require(v_new, "v_new", torch.bfloat16, 4, q.device)
+        _require(k_new, "k_new", q.dtype, 4, q.device)
+        _require(v_new, "v_new", q.dtype, 4, q.device)
         if k_new.shape != v_new.shape or k_new.shape[0] != b or k_new.shape[2] != hk or k_new.shape[3] != d:
             raise ValueError("k_new and v_new must be [batch, seqlen_new, H_k, D]")
         snew = k_new.shape[1]
@@ -314,8 +340,8 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
         _require(rotary_cos, "rotary_cos", torch.float32, 2, q.device)
         _require(rotary_sin, "rotary_sin", torch.float32, 2, q.device)
         rd = 2 * rotary_cos.shape[1]
-    slopes = _alibi(alibi_slopes, h, q.device)
-    _require(out, "out", torch.bfloat16, 4, q.device)
+    slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
+    _require(out, "out", q.dtype, 4, q.device)
     _require(lse, "lse", torch.float32, 3, q.device)
     _require(out_partial, "out_partial", torch.float32, 5, q.device)
     _require(lse_partial, "lse_partial", torch.float32, 4, q.device)
@@ -328,4 +354,5 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(), _ptr(block_table), page,
         max_blocks, _ptr(k_new), _ptr(v_new), snew, _ptr(rotary_cos), _ptr(rotary_sin), rd, out.data_ptr(),
         lse.data_ptr(), op.data_ptr(), lp.data_ptr(), int(max_splits), b, sq, h, hk, d, _scale(softmax_scale, d),
-        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), int(num_splits), _stream_handle(q)))
+        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype],
+        int(num_splits), _stream_handle(q)))

@@ -44,11 +44,13 @@ long long elems4(long long a, long long b, long long c, long long d) {
   return r;
 }
 
-// Shared validation of fa_fwd / fa_fwd_splitkv.  Fills p on success.
+// Shared validation of the entry points.  Fills p on success.
 int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q, int seqlen_k,
             int nheads, int headdim, float softmax_scale, int causal, int window_left, int window_right,
-            const float* alibi_slopes, fa::FwdParams* p) {
+            const float* alibi_slopes, int alibi_per_batch, int dtype, fa::FwdParams* p) {
   if (!q || !k || !v) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
+  if (alibi_per_batch != 0 && alibi_per_batch != 1) return FA_ERR_INVALID_ARG;
   if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || nheads < 1 || headdim < 1) return FA_ERR_INVALID_ARG;
   if (seqlen_q > kMaxSeqlen || seqlen_k > kMaxSeqlen) return FA_ERR_INVALID_ARG;
   if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
@@ -72,6 +74,8 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
   p->k = (const uint16_t*)k;
   p->v = (const uint16_t*)v;
   p->alibi = alibi_slopes;
+  p->alibi_bstride = alibi_per_batch ? nheads : 0;
+  p->f16 = dtype == FA_FP16 ? 1 : 0;
   p->batch = batch;
   p->seqlen_q = seqlen_q;
   p->seqlen_k = seqlen_k;
@@ -113,11 +117,11 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen_q,
            int seqlen_k, int nheads, int headdim, float softmax_scale, int causal, int window_left,
-           int window_right, const float* alibi_slopes, hipStream_t stream) {
+           int window_right, const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
   if (!out || !lse) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, &p);
+                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
   p.out = out;
   p.lse = lse;
@@ -128,12 +132,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_partial, float* lse_partial,
                    int batch, int seqlen_q, int seqlen_k, int nheads, int headdim, float softmax_scale,
-                   int causal, int window_left, int window_right, const float* alibi_slopes, int num_splits,
-                   hipStream_t stream) {
+                   int causal, int window_left, int window_right, const float* alibi_slopes,
+                   int alibi_per_batch, int dtype, int num_splits, hipStream_t stream) {
   if (!out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, &p);
+                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > seqlen_k) return FA_ERR_INVALID_ARG;
   if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
@@ -156,7 +160,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_parti
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_seqlens_q,
                   const int* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int nheads,
                   int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
-                  const float* alibi_slopes, hipStream_t stream) {
+                  const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
   if (!out || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1) return FA_ERR_INVALID_ARG;
   // The per-sequence lengths live on the device; the maxima size the grid and the
@@ -164,7 +168,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
   // their place (every sequence is at most that long).
   fa::FwdParams p;
   const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, &p);
+                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
   if (batch < 1 || elems4(total_q, nheads, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
   p.batch = batch;
@@ -182,11 +186,11 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* delta, int batch, int seqlen_q, int seqlen_k, int nheads,
            int headdim, float softmax_scale, int causal, int window_left, int window_right,
-           const float* alibi_slopes, hipStream_t stream) {
+           const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
   fa::FwdParams f;  // the forward's validation and window normalisation
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, &f);
+                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
   if (st != FA_OK) return st;
   if (headdim != 64 && headdim != 128) return FA_ERR_UNSUPPORTED;
   fa::BwdParams p;
@@ -201,6 +205,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
   p.alibi = alibi_slopes;
+  p.alibi_bstride = f.alibi_bstride;
+  p.f16 = f.f16;
   p.batch = batch;
   p.seqlen_q = seqlen_q;
   p.seqlen_k = seqlen_k;
@@ -226,7 +232,8 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
                    const float* rotary_cos, const float* rotary_sin, int rotary_dim, void* out, float* lse,
                    float* out_partial, float* lse_partial, int max_splits, int batch, int seqlen_q, int nheads,
                    int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
-                   const float* alibi_slopes, int num_splits, hipStream_t stream) {
+                   const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
+                   hipStream_t stream) {
   if (!cache_seqlens || !out || !lse || !out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
   if (seqlen_q < 1 || seqlen_q > kDecodeMaxRows || seqlen_new < 0 || page_size < 1 || max_splits < 1)
     return FA_ERR_INVALID_ARG;
@@ -249,7 +256,7 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
   if (capacity > kMaxSeqlen) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
   const int st = prepare(q, k_cache, v_cache, batch, seqlen_q, (int)capacity, nheads, headdim, softmax_scale,
-                         causal, window_left, window_right, alibi_slopes, &p);
+                         causal, window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
   // automatic split count: about 2048 workgroups (eight per CU), at least 256 keys each;
   // a workgroup serves up to eight queries of one K/V head
@@ -287,12 +294,14 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
   c.seqlen_q = seqlen_q;
   c.nheads = nheads;
   c.num_splits = ns;
+  c.f16 = p.f16;
   return fa::launch_combine(c, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,
-               int seqlen_q, int nheads, int headdim, int num_splits, hipStream_t stream) {
+               int seqlen_q, int nheads, int headdim, int num_splits, int dtype, hipStream_t stream) {
   if (!out_partial || !lse_partial || !out || !lse) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
   if (batch < 1 || seqlen_q < 1 || nheads < 1 || headdim < 1 || num_splits < 1) return FA_ERR_INVALID_ARG;
   if (seqlen_q > kMaxSeqlen) return FA_ERR_INVALID_ARG;
   if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
@@ -308,6 +317,7 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
   p.seqlen_q = seqlen_q;
   p.nheads = nheads;
   p.num_splits = num_splits;
+  p.f16 = dtype == FA_FP16 ? 1 : 0;
   (void)hipGetLastError();
   return fa::launch_combine(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

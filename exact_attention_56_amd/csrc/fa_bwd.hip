@@ -1,32 +1,38 @@
 // fa_bwd.hip - instantiates the delta and dK/dV passes of the backward (headdim 64
-// and 128) and launches the three passes in order on one stream: delta, dK/dV, dQ.
+// and 128, bf16 and fp16) and launches the three passes in order on one stream:
+// delta, dK/dV, dQ.
 #include "fa_bwd_kernel.h"
 
 namespace fa {
 
-template <int HD>
+template <int HD, typename E>
 static hipError_t launch_bwd_hd(const BwdParams& p, hipStream_t stream) {
   const long rows = (long)p.batch * p.seqlen_q * p.nheads;
   constexpr int rows_per_block = 4 * (64 / (HD / 8));
-  hipLaunchKernelGGL(delta_kernel<HD>, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256), 0,
-                     stream, p, rows);
+  hipLaunchKernelGGL((delta_kernel<HD, E>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
+                     0, stream, p, rows);
   const bool alibi = p.alibi != nullptr;
   const int kv_items = p.batch * p.nheads * p.num_k_tiles;
   if (alibi)
-    hipLaunchKernelGGL((dkdv_kernel<HD, true>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
+    hipLaunchKernelGGL((dkdv_kernel<HD, true, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
   else
-    hipLaunchKernelGGL((dkdv_kernel<HD, false>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
+    hipLaunchKernelGGL((dkdv_kernel<HD, false, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return HD == 64 ? launch_dq_d64(p, stream) : launch_dq_d128(p, stream);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int headdim, hipStream_t stream) {
+template <typename E>
+static hipError_t launch_bwd_e(const BwdParams& p, int headdim, hipStream_t stream) {
   switch (headdim) {
-    case 64: return launch_bwd_hd<64>(p, stream);
-    case 128: return launch_bwd_hd<128>(p, stream);
+    case 64: return launch_bwd_hd<64, E>(p, stream);
+    case 128: return launch_bwd_hd<128, E>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bwd(const BwdParams& p, int headdim, hipStream_t stream) {
+  return p.f16 ? launch_bwd_e<_Float16>(p, headdim, stream) : launch_bwd_e<__bf16>(p, headdim, stream);
 }
 
 }  // namespace fa

@@ -36,17 +36,19 @@ namespace fa {
 
 // Backward problem description, filled on the host.  Sizes are in elements.
 struct BwdParams {
-  const uint16_t* q;      // bf16 [B, Sq, H, D]
-  const uint16_t* k;      // bf16 [B, Sk, H, D]
-  const uint16_t* v;      // bf16 [B, Sk, H, D]
-  const uint16_t* out;    // bf16 [B, Sq, H, D]  forward output
-  const uint16_t* dout;   // bf16 [B, Sq, H, D]  upstream gradient
+  const uint16_t* q;      // bf16/fp16 [B, Sq, H, D]
+  const uint16_t* k;      // bf16/fp16 [B, Sk, H, D]
+  const uint16_t* v;      // bf16/fp16 [B, Sk, H, D]
+  const uint16_t* out;    // bf16/fp16 [B, Sq, H, D]  forward output
+  const uint16_t* dout;   // bf16/fp16 [B, Sq, H, D]  upstream gradient
   const float* lse;       // fp32 [B, H, Sq]     forward logsumexp (natural log)
   float* delta;           // fp32 [B, H, Sq]     D, written by delta_kernel
-  uint16_t* dq;           // bf16 [B, Sq, H, D]
-  uint16_t* dk;           // bf16 [B, Sk, H, D]
-  uint16_t* dv;           // bf16 [B, Sk, H, D]
-  const float* alibi;     // fp32 [H] or nullptr
+  uint16_t* dq;           // bf16/fp16 [B, Sq, H, D]
+  uint16_t* dk;           // bf16/fp16 [B, Sk, H, D]
+  uint16_t* dv;           // bf16/fp16 [B, Sk, H, D]
+  const float* alibi;     // fp32 [H] or [B, H], or nullptr
+  int alibi_bstride;      // 0: one slope per head for every batch; nheads: [B, H]
+  int f16;                // 1: every 16-bit tensor is fp16, 0: bf16
   int batch, seqlen_q, seqlen_k, nheads;
   float scale;            // softmax_scale as given
   float scale_log2;       // |scale| * log2(e), or 1 when scale == 0
@@ -120,46 +122,48 @@ struct PairStream {
 
 // A operand (32 rows x 16 columns) read from a row-major LDS tile: lane l takes row
 // k_lds_row(l % 32) + 32 blk, 16 bytes at column 16 kk + 8 (l / 32).
-template <int PITCH>
-__device__ __forceinline__ bf16x8 row_operand(const lds_u8* tile, int lrow, int half, int blk, int kk) {
-  return *(const __attribute__((address_space(3))) bf16x8*)(tile + (k_lds_row(lrow) + 32 * blk) * PITCH +
-                                                             32 * kk + 16 * half);
+template <int PITCH, typename E>
+__device__ __forceinline__ x8<E> row_operand(const lds_u8* tile, int lrow, int half, int blk, int kk) {
+  return *(const __attribute__((address_space(3))) x8<E>*)(tile + (k_lds_row(lrow) + 32 * blk) * PITCH + 32 * kk +
+                                                            16 * half);
 }
 
 // A operand of a transposed product: X^T[d][rows 16 ci + 8 (l / 32) + 0..7] for
 // d = 32 db + l % 32, from a row-major LDS tile (two transpose reads; see
 // vt_lane_offset for the lane pattern, here with any row pitch).
-template <int PITCH>
-__device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, int lane, int db, int ci) {
+template <int PITCH, typename E>
+__device__ __forceinline__ x8<E> tr_operand(const lds_u8* tile, int lane, int db, int ci) {
   const int g = lane >> 4, r = lane & 15;
   const lds_u8* p = tile + (8 * (g >> 1) + (r >> 2)) * PITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * ci * PITCH + 64 * db));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (16 * ci + 4) * PITCH + 64 * db));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(x8<E>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 16 bytes of row `row` of a [rows][row_stride] bf16 tensor as a B operand (8
+// 16 bytes of row `row` of a [rows][row_stride] 16-bit tensor as a B operand (8
 // consecutive columns starting at 16 kk + 8 half), zero past the last row.
-__device__ __forceinline__ bf16x8 row_fragment(const uint16_t* base, long row_stride, int row, int nrows, int kk,
+template <typename E>
+__device__ __forceinline__ x8<E> row_fragment(const uint16_t* base, long row_stride, int row, int nrows, int kk,
                                                int half, uint32_t and_mask, uint32_t xor_mask) {
   u32x4 raw = {0u, 0u, 0u, 0u};
   if (row < nrows) raw = *(const u32x4*)(base + (long)row * row_stride + 16 * kk + 8 * half);
   raw = (raw & and_mask) ^ xor_mask;
-  return __builtin_bit_cast(bf16x8, raw);
+  return __builtin_bit_cast(x8<E>, raw);
 }
 
 // Pack register pairs (2e, 2e+1) of 8 consecutive accumulator rows r0..r0+7 into the
-// bf16 B operand of the next product.
-__device__ __forceinline__ bf16x8 pack_rows(const f32x16& x, int r0) {
-  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[r0], x[r0 + 1]), pack_bf16x2(x[r0 + 2], x[r0 + 3]),
-                                          pack_bf16x2(x[r0 + 4], x[r0 + 5]), pack_bf16x2(x[r0 + 6], x[r0 + 7])});
+// B operand (element type E) of the next product.
+template <typename E>
+__device__ __forceinline__ x8<E> pack_rows(const f32x16& x, int r0) {
+  return __builtin_bit_cast(x8<E>, u32x4{pack2<E>(x[r0], x[r0 + 1]), pack2<E>(x[r0 + 2], x[r0 + 3]),
+                                         pack2<E>(x[r0 + 4], x[r0 + 5]), pack2<E>(x[r0 + 6], x[r0 + 7])});
 }
 
-// Store a transposed accumulator X^T [HD rows (d) x 32 columns] of this wave as bf16
+// Store a transposed accumulator X^T [HD rows (d) x 32 columns] of this wave as E
 // row `row` (the lane's column) of a [rows][row_stride] tensor, times `mul`.
-template <int HD>
-__device__ __forceinline__ void store_rows_bf16(uint16_t* base, long row_stride, int row, const f32x16 (&x)[HD / 32],
+template <int HD, typename E>
+__device__ __forceinline__ void store_rows(uint16_t* base, long row_stride, int row, const f32x16 (&x)[HD / 32],
                                                 float mul, int half) {
   uint16_t* o = base + (long)row * row_stride;
 #pragma unroll
@@ -168,8 +172,8 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* base, long row_stride,
     for (int g = 0; g < 4; ++g) {
       // accumulator rows 4g..4g+3 of block db hold columns 32db + 8g + 4*half + 0..3
       const int d0 = 32 * db + 8 * g + 4 * half;
-      u32x2 w = {pack_bf16x2(x[db][4 * g] * mul, x[db][4 * g + 1] * mul),
-                 pack_bf16x2(x[db][4 * g + 2] * mul, x[db][4 * g + 3] * mul)};
+      u32x2 w = {pack2<E>(x[db][4 * g] * mul, x[db][4 * g + 1] * mul),
+                 pack2<E>(x[db][4 * g + 2] * mul, x[db][4 * g + 3] * mul)};
       *(u32x2*)(o + d0) = w;
     }
 }
@@ -177,7 +181,7 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* base, long row_stride,
 // ---------------------------------------------------------------------------------
 // delta_kernel: D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32.  One
 // wave per 8 rows; HD/8 lanes per row, 16 bytes each, then a lane-group sum.
-template <int HD>
+template <int HD, typename E>
 __global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
   constexpr int LPR = HD / 8;       // lanes per row
@@ -191,8 +195,8 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows) {
     const u32x4 g = *(const u32x4*)(p.dout + row * HD + 8 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc += __uint_as_float(o[e] << 16) * __uint_as_float(g[e] << 16);
-      acc += __uint_as_float(o[e] & 0xffff0000u) * __uint_as_float(g[e] & 0xffff0000u);
+      acc += widen_lo<E>(o[e]) * widen_lo<E>(g[e]);
+      acc += widen_hi<E>(o[e]) * widen_hi<E>(g[e]);
     }
   }
 #pragma unroll
@@ -218,7 +222,7 @@ __device__ __forceinline__ float alibi_log2(float slope_log2, int pos_i, int key
 //   S^T = K Q^T, dP^T = V dO^T   (lane = query; K, V rows from LDS, Q, dO in registers)
 //   P^T = exp2(S^T c + bias - L'), dS^T = P^T (dP^T - D)
 //   dQ^T += K^T dS^T              (K^T by transpose reads, dS^T as the B operand)
-template <int HD, bool ALIBI>
+template <int HD, bool ALIBI, typename E>
 __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
   constexpr int KS = HD / 8 + 2;  // K rows: transpose reads dominate (V-style pitch)
@@ -257,11 +261,11 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   const int t_begin = hi >= lo ? lo / DQ_TILE : 0;
   const int t_end = hi >= lo ? hi / DQ_TILE + 1 : 0;
 
-  bf16x8 qf[HD / 16], gf[HD / 16];
+  x8<E> qf[HD / 16], gf[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
-    qf[kk] = row_fragment(p.q + qoff, rs, my_q, Sq, kk, half, p.q_and, p.q_sign);
-    gf[kk] = row_fragment(p.dout + qoff, rs, my_q, Sq, kk, half, 0xffffffffu, 0u);
+    qf[kk] = row_fragment<E>(p.q + qoff, rs, my_q, Sq, kk, half, p.q_and, p.q_sign);
+    gf[kk] = row_fragment<E>(p.dout + qoff, rs, my_q, Sq, kk, half, 0xffffffffu, 0u);
   }
   // L in log2 units (an empty row gets +inf, so that every P of it is 0) and D
   float lrow2 = INFINITY, drow = 0.f;
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   }
   const float c = p.scale_log2;
   float slope2 = 0.f;
-  if constexpr (ALIBI) slope2 = p.alibi[h] * kLog2e;
+  if constexpr (ALIBI) slope2 = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
 
   f32x16 dq[HD / 32];
 #pragma unroll
@@ -304,10 +308,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
     for (int kk = 0; kk < HD / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<KP>(kt, lrow, half, kb, kk), qf[kk], s[kb], 0,
-                                                        0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<VP>(vt, lrow, half, kb, kk), gf[kk], dp[kb], 0,
-                                                         0, 0);
+        s[kb] = mfma32(row_operand<KP, E>(kt, lrow, half, kb, kk), qf[kk], s[kb]);
+        dp[kb] = mfma32(row_operand<VP, E>(vt, lrow, half, kb, kk), gf[kk], dp[kb]);
       }
 
     // P^T and dS^T.  Register r of block kb holds key j0 + 32 kb + 16 (r / 8) + 8 half + r % 8.
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
       vlo = klo;
       vspan = khi - klo;
     }
-    bf16x8 dsf[4];
+    x8<E> dsf[4];
 #pragma unroll
     for (int ci = 0; ci < 4; ++ci) {
       const int kb = ci >> 1, r0 = 8 * (ci & 1);
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
         }
         tmp[e] = pv * (dp[kb][r0 + e] - drow);
       }
-      dsf[ci] = pack_rows(tmp, 0);
+      dsf[ci] = pack_rows<E>(tmp, 0);
     }
 
     // dQ^T += K^T dS^T
@@ -346,9 +348,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
     for (int ci = 0; ci < 4; ++ci)
 #pragma unroll
       for (int db = 0; db < HD / 32; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<KP>(kt, lane, db, ci), dsf[ci], dq[db], 0, 0, 0);
+        dq[db] = mfma32(tr_operand<KP, E>(kt, lane, db, ci), dsf[ci], dq[db]);
   }
-  if (my_q < Sq) store_rows_bf16<HD>(p.dq + qoff, rs, my_q, dq, p.scale, half);
+  if (my_q < Sq) store_rows<HD, E>(p.dq + qoff, rs, my_q, dq, p.scale, half);
 #endif
 }
 
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 //   S = Q K^T, dP = dO V^T        (lane = key; Q, dO rows from LDS, K, V in registers)
 //   P = exp2(S c + bias - L'), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by transpose reads; P, dS as B operands)
-template <int HD, bool ALIBI>
+template <int HD, bool ALIBI, typename E>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   constexpr int DKV_TILE = dkv_tile<HD>(), DKV_QB = DKV_TILE / 32;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
@@ -399,15 +401,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int t_begin = hi >= lo ? lo / DKV_TILE : 0;
   const int t_end = hi >= lo ? hi / DKV_TILE + 1 : 0;
 
-  bf16x8 kf[HD / 16], vf[HD / 16];
+  x8<E> kf[HD / 16], vf[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
-    kf[kk] = row_fragment(p.k + koff, rs, my_k, Sk, kk, half, p.q_and, p.q_sign);
-    vf[kk] = row_fragment(p.v + koff, rs, my_k, Sk, kk, half, 0xffffffffu, 0u);
+    kf[kk] = row_fragment<E>(p.k + koff, rs, my_k, Sk, kk, half, p.q_and, p.q_sign);
+    vf[kk] = row_fragment<E>(p.v + koff, rs, my_k, Sk, kk, half, 0xffffffffu, 0u);
   }
   const float c = p.scale_log2;
   float slope2 = 0.f;
-  if constexpr (ALIBI) slope2 = p.alibi[h] * kLog2e;
+  if constexpr (ALIBI) slope2 = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
   // visible queries of this key: c_i in [my_k - wr, my_k + wl]
   const int qlo = wr < 0 ? 0 : max(0, my_k - wr - off);
   const int qhi = wl < 0 ? Sq - 1 : min(Sq - 1, my_k + wl - off);
@@ -460,10 +462,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     for (int kk = 0; kk < HD / 16; ++kk)
 #pragma unroll
       for (int qb = 0; qb < DKV_QB; ++qb) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(qt, lrow, half, qb, kk), kf[kk], s[qb], 0, 0,
-                                                        0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<QP>(gt, lrow, half, qb, kk), vf[kk], dp[qb], 0,
-                                                         0, 0);
+        s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
+        dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
       }
 
     // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     // every (query of the tile, key of the block) pair visible, no query past the end
     const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
                       (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
-    bf16x8 pf[2 * DKV_QB], dsf[2 * DKV_QB];
+    x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
 #pragma unroll
     for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
       const int qb = cc >> 1, ci = cc & 1;
@@ -494,21 +494,21 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
         pt[e] = pv;
         dt[e] = pv * (dp[qb][8 * ci + e] - dd);
       }
-      pf[cc] = pack_rows(pt, 0);
-      dsf[cc] = pack_rows(dt, 0);
+      pf[cc] = pack_rows<E>(pt, 0);
+      dsf[cc] = pack_rows<E>(dt, 0);
     }
 
 #pragma unroll
     for (int cc = 0; cc < 2 * DKV_QB; ++cc)
 #pragma unroll
       for (int db = 0; db < HD / 32; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(gt, lane, db, cc), pf[cc], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<QP>(qt, lane, db, cc), dsf[cc], dk[db], 0, 0, 0);
+        dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
+        dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
       }
   }
   if (my_k < Sk) {
-    store_rows_bf16<HD>(p.dk + koff, rs, my_k, dk, p.scale, half);
-    store_rows_bf16<HD>(p.dv + koff, rs, my_k, dv, 1.f, half);
+    store_rows<HD, E>(p.dk + koff, rs, my_k, dk, p.scale, half);
+    store_rows<HD, E>(p.dv + koff, rs, my_k, dv, 1.f, half);
   }
 #endif
 }
@@ -518,13 +518,13 @@ hipError_t launch_bwd(const BwdParams& p, int headdim, hipStream_t stream);
 hipError_t launch_dq_d64(const BwdParams& p, hipStream_t stream);
 hipError_t launch_dq_d128(const BwdParams& p, hipStream_t stream);
 
-template <int HD>
+template <int HD, typename E>
 hipError_t launch_dq_hd(const BwdParams& p, hipStream_t stream) {
   const int items = p.batch * p.nheads * p.num_q_tiles;
   if (p.alibi != nullptr)
-    hipLaunchKernelGGL((dq_kernel<HD, true>), dim3(items), dim3(256), 0, stream, p, items);
+    hipLaunchKernelGGL((dq_kernel<HD, true, E>), dim3(items), dim3(256), 0, stream, p, items);
   else
-    hipLaunchKernelGGL((dq_kernel<HD, false>), dim3(items), dim3(256), 0, stream, p, items);
+    hipLaunchKernelGGL((dq_kernel<HD, false, E>), dim3(items), dim3(256), 0, stream, p, items);
   return hipGetLastError();
 }
 

@@ -15,6 +15,15 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// q, k, v, out (and the gradients) are bf16 or fp16: the same 16-bit storage, so
+// loads, LDS layouts and address arithmetic are shared; the element type E
+// (__bf16 or _Float16) only picks the matrix-core instruction, the rounding of fp32
+// results to 16 bits and the widening to fp32.
+template <typename E>
+using x8 = E __attribute__((ext_vector_type(8)));
+template <typename E>
+using x2 = E __attribute__((ext_vector_type(2)));
+
 // Matrix-core forward: query rows per workgroup of the default four-wave launch
 // (the eight-wave launch recounts its 256-row tiles itself).
 constexpr int FWD_BLOCK_ROWS = 128;
@@ -29,7 +38,9 @@ struct FwdParams {
   const uint16_t* v;      // bf16 [B, Sk, H, D]
   void* out;              // bf16 [B, Sq, H, D]  or fp32 [S, B, H, Sq, D] (split mode)
   float* lse;             // fp32 [B, H, Sq]     or fp32 [S, B, H, Sq]    (split mode)
-  const float* alibi;     // fp32 [H] ALiBi slopes, or nullptr
+  const float* alibi;     // fp32 ALiBi slopes [H] or [B, H], or nullptr
+  int alibi_bstride;      // 0: one slope per head for every batch; nheads: [B, H]
+  int f16;                // 1: q/k/v/out are fp16, 0: bf16
   int batch, seqlen_q, seqlen_k, nheads;  // varlen: seqlen_q/k are the maximum lengths
   int nheads_k;           // K/V heads; query head h reads K/V head h / (nheads / nheads_k)
   const int* cu_q;        // varlen: [batch + 1] first q/out row of each sequence, or nullptr
@@ -58,9 +69,10 @@ struct FwdParams {
 struct CombineParams {
   const float* out_partial;  // [S, B, H, Sq, D]
   const float* lse_partial;  // [S, B, H, Sq]
-  uint16_t* out;             // bf16 [B, Sq, H, D]
+  uint16_t* out;             // bf16 or fp16 [B, Sq, H, D]
   float* lse;                // [B, H, Sq]
   int batch, seqlen_q, nheads, num_splits;
+  int f16;                   // 1: out is fp16, 0: bf16
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -81,6 +93,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, b);
+}
+
+// 32x32x16 matrix-core product with fp32 accumulation, for either element type.
+__device__ __forceinline__ f32x16 mfma32(const x8<__bf16>& a, const x8<__bf16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const x8<_Float16>& a, const x8<_Float16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Round two fp32 to E (round-to-nearest-even) and pack them, low half first.
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, x2<E>));
+}
+
+// fp32 value of the low / high 16-bit element of a packed pair.
+template <typename E>
+__device__ __forceinline__ float widen_lo(uint32_t x) {
+  if constexpr (__is_same(E, __bf16)) return __uint_as_float(x << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+}
+template <typename E>
+__device__ __forceinline__ float widen_hi(uint32_t x) {
+  if constexpr (__is_same(E, __bf16)) return __uint_as_float(x & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
 }
 
 // Map a linear workgroup id to a work index so that the workgroups the dispatcher

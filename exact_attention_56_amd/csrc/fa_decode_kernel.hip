@@ -7,7 +7,7 @@
 //
 // Partial kernel: one workgroup per (batch, head, split, query row).  A query row
 // against a KV chunk is a matrix-vector product, so it runs on the vector ALUs and
-// is bound by HBM bandwidth: each key row (headdim bf16) is read by HD/8 lanes with
+// is bound by HBM bandwidth: each key row (headdim 16-bit values) is read by HD/8 lanes with
 // one 16-byte load each, the dot product is finished with lane shuffles, and the
 // four waves walk interleaved slices of the chunk with their own online-softmax
 // state, merged through LDS at the end.  The output of a split is normalised
@@ -31,13 +31,11 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_UNROLL = FA_DEC_UNROLL;  // key rows per lane per step
 constexpr int DEC_CPOL = FA_DEC_CPOL;      // KV loads are non-temporal (read once, streamed)
 
-__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // KVC: the keys come from a KV cache (fa_fwd_kvcache): sequence b has
 // cache_seqlens[b] + seqlen_new keys, block n of it lives in block block_table[b, n]
 // (or block b of a contiguous cache), and K/V may have fewer heads than Q.
-template <int HD, bool ALIBI, bool KVC>
+template <int HD, bool ALIBI, bool KVC, typename E>
 __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) {
   constexpr int LPR = HD / 8;    // lanes per key row
   constexpr int RPW = 64 / LPR;  // key rows per wave per load
@@ -83,12 +81,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
     const u32x4 raw = *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qv[2 * e] = bf16_lo(raw[e]) * c;
-      qv[2 * e + 1] = bf16_hi(raw[e]) * c;
+      qv[2 * e] = widen_lo<E>(raw[e]) * c;
+      qv[2 * e + 1] = widen_hi<E>(raw[e]) * c;
     }
   }
   float slope = 0.f;
-  if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;
+  if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[8];
@@ -124,8 +122,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        part = fmaf(qv[2 * e], bf16_lo(kr[u][e]), part);
-        part = fmaf(qv[2 * e + 1], bf16_hi(kr[u][e]), part);
+        part = fmaf(qv[2 * e], widen_lo<E>(kr[u][e]), part);
+        part = fmaf(qv[2 * e + 1], widen_hi<E>(kr[u][e]), part);
       }
 #pragma unroll
       for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
@@ -149,8 +147,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
       l_run += pu;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(pu, bf16_lo(vr[u][e]), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(pu, bf16_hi(vr[u][e]), acc[2 * e + 1]);
+        acc[2 * e] = fmaf(pu, widen_lo<E>(vr[u][e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(pu, widen_hi<E>(vr[u][e]), acc[2 * e + 1]);
       }
     }
     m_run = m_new;
@@ -199,7 +197,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) 
 // the seqlen_q rows (query n: head hk * G + n / Sq, row n % Sq); one workgroup takes NQ
 // of them, so each key row it loads serves NQ dot products instead of one.  Each
 // query keeps its own visible range, ALiBi slope and online-softmax state.
-template <int HD, bool ALIBI, bool KVC, int NQ>
+template <int HD, bool ALIBI, bool KVC, int NQ, typename E>
 __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) {
   constexpr int LPR = HD / 8;
   constexpr int RPW = 64 / LPR;
@@ -257,11 +255,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
                             : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qv[j][2 * e] = bf16_lo(raw[e]) * c;
-      qv[j][2 * e + 1] = bf16_hi(raw[e]) * c;
+      qv[j][2 * e] = widen_lo<E>(raw[e]) * c;
+      qv[j][2 * e + 1] = widen_hi<E>(raw[e]) * c;
     }
     slope[j] = 0.f;
-    if constexpr (ALIBI) slope[j] = p.alibi[h] * kLog2e;
+    if constexpr (ALIBI) slope[j] = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
   }
   if (hi <= lo) lo = hi = 0;  // no query sees a key of this split
   const long kvb = KVC ? (long)hk * HD : (long)b * Sk * kv_stride + (long)hk * HD;
@@ -306,8 +304,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          part = fmaf(qv[j][2 * e], bf16_lo(kr[u][e]), part);
-          part = fmaf(qv[j][2 * e + 1], bf16_hi(kr[u][e]), part);
+          part = fmaf(qv[j][2 * e], widen_lo<E>(kr[u][e]), part);
+          part = fmaf(qv[j][2 * e + 1], widen_hi<E>(kr[u][e]), part);
         }
 #pragma unroll
         for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
@@ -330,8 +328,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
         l_run[j] += pu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[j][2 * e] = fmaf(pu, bf16_lo(vr[u][e]), acc[j][2 * e]);
-          acc[j][2 * e + 1] = fmaf(pu, bf16_hi(vr[u][e]), acc[j][2 * e + 1]);
+          acc[j][2 * e] = fmaf(pu, widen_lo<E>(vr[u][e]), acc[j][2 * e]);
+          acc[j][2 * e + 1] = fmaf(pu, widen_hi<E>(vr[u][e]), acc[j][2 * e + 1]);
         }
       }
       m_run[j] = m_new;
@@ -383,7 +381,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
   }
 }
 
-template <int HD>
+template <int HD, typename E>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int PER_LANE = HD / 64;
   const int lane = threadIdx.x & 63;
@@ -421,35 +419,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   uint16_t* out = p.out + (((long)b * p.seqlen_q + i) * p.nheads + h) * HD;
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) {
-    const uint32_t pk = pack_bf16x2(o[e] * inv, 0.f);
+    const uint32_t pk = pack2<E>(o[e] * inv, 0.f);
     out[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
   }
   if (lane == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
-// Element e of a bf16 row x rotated at position `pos` (half-split rotary layout:
+// Element e of a row x of E rotated at position `pos` (half-split rotary layout:
 // the pair (x_d, x_{d + rd/2}) turns by the angle of cos[pos, d], sin[pos, d];
-// columns from rd on are unchanged), rounded to bf16.
+// columns from rd on are unchanged), rounded to E.
+template <typename E>
 __device__ __forceinline__ uint16_t rotated(const uint16_t* x, int e, long pos, const float* cos, const float* sin,
                                             int rd) {
   const int half = rd >> 1;
-  const float xe = __uint_as_float((uint32_t)x[e] << 16);
+  const float xe = widen_lo<E>(x[e]);
   float y = xe;
   if (e < half) {
     const float c = cos[pos * half + e], s = sin[pos * half + e];
-    y = xe * c - __uint_as_float((uint32_t)x[e + half] << 16) * s;
+    y = xe * c - widen_lo<E>(x[e + half]) * s;
   } else if (e < rd) {
     const float c = cos[pos * half + e - half], s = sin[pos * half + e - half];
-    y = xe * c + __uint_as_float((uint32_t)x[e - half] << 16) * s;
+    y = xe * c + widen_lo<E>(x[e - half]) * s;
   }
-  return (uint16_t)(pack_bf16x2(y, 0.f) & 0xffffu);
+  return (uint16_t)(pack2<E>(y, 0.f) & 0xffffu);
 }
 
 // KV-cache preparation, one wave per row: rows [0, n_kv) append k_new / v_new row
 // (b, i, hk) at position cache_seqlens[b] + i of the cache (keys rotated when cos is
 // given); rows [n_kv, n_kv + n_q) write query row (b, i, h) rotated at position
 // cache_seqlens[b] + i into qrot.
-template <int HD>
+template <int HD, typename E>
 __global__ __launch_bounds__(256) void kvcache_prep_kernel(FwdParams p, const uint16_t* k_new, const uint16_t* v_new,
                                                            uint16_t* k_cache, uint16_t* v_cache, const float* cos,
                                                            const float* sin, int rd, uint16_t* qrot, long n_kv,
@@ -469,7 +468,7 @@ __global__ __launch_bounds__(256) void kvcache_prep_kernel(FwdParams p, const ui
     const long src = bi * p.nheads_k * HD + (long)hk * HD;
     const long dst = (row * p.nheads_k + hk) * HD;
     for (int e = lane; e < HD; e += 64) {
-      k_cache[dst + e] = cos != nullptr ? rotated(k_new + src, e, j, cos, sin, rd) : k_new[src + e];
+      k_cache[dst + e] = cos != nullptr ? rotated<E>(k_new + src, e, j, cos, sin, rd) : k_new[src + e];
       v_cache[dst + e] = v_new[src + e];
     }
   } else if (task < n_kv + n_q) {
@@ -478,68 +477,75 @@ __global__ __launch_bounds__(256) void kvcache_prep_kernel(FwdParams p, const ui
     const int i = (int)(bi % p.seqlen_q);
     const int b = (int)(bi / p.seqlen_q);
     const long pos = (long)p.cache_seqlens[b] + i;
-    for (int e = lane; e < HD; e += 64) qrot[t * HD + e] = rotated(p.q + t * HD, e, pos, cos, sin, rd);
+    for (int e = lane; e < HD; e += 64) qrot[t * HD + e] = rotated<E>(p.q + t * HD, e, pos, cos, sin, rd);
   }
 }
 
-template <int HD, bool ALIBI, bool KVC, int NQ>
+template <int HD, bool ALIBI, bool KVC, int NQ, typename E>
 static void launch_group(const FwdParams& p, hipStream_t stream) {
   const int nq_total = p.nheads / p.nheads_k * p.seqlen_q;
   const long nblocks = (long)p.batch * p.nheads_k * p.num_splits * ((nq_total + NQ - 1) / NQ);
-  hipLaunchKernelGGL((decode_group_kernel<HD, ALIBI, KVC, NQ>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
+  hipLaunchKernelGGL((decode_group_kernel<HD, ALIBI, KVC, NQ, E>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
                      stream, p);
 }
 
 // Queries one decode workgroup serves when a K/V head has nq_total of them.
 int decode_queries_per_block(int nq_total) { return nq_total <= 1 ? 1 : nq_total <= 2 ? 2 : nq_total <= 4 ? 4 : 8; }
 
-template <int HD, bool ALIBI, bool KVC>
+template <int HD, bool ALIBI, bool KVC, typename E>
 static void launch_group_nq(const FwdParams& p, hipStream_t stream) {
   switch (decode_queries_per_block(p.nheads / p.nheads_k * p.seqlen_q)) {
-    case 2: launch_group<HD, ALIBI, KVC, 2>(p, stream); break;
-    case 4: launch_group<HD, ALIBI, KVC, 4>(p, stream); break;
-    default: launch_group<HD, ALIBI, KVC, 8>(p, stream); break;
+    case 2: launch_group<HD, ALIBI, KVC, 2, E>(p, stream); break;
+    case 4: launch_group<HD, ALIBI, KVC, 4, E>(p, stream); break;
+    default: launch_group<HD, ALIBI, KVC, 8, E>(p, stream); break;
   }
 }
 
-template <int HD, bool KVC>
+template <int HD, bool KVC, typename E>
 static hipError_t launch_decode_kvc(const FwdParams& p, hipStream_t stream) {
   // several queries per K/V head (grouped heads or seqlen_q > 1): the grouped kernel
   // loads each key row once for all of them
   if (p.nheads / p.nheads_k * p.seqlen_q > 1) {
-    if (p.alibi) launch_group_nq<HD, true, KVC>(p, stream);
-    else launch_group_nq<HD, false, KVC>(p, stream);
+    if (p.alibi) launch_group_nq<HD, true, KVC, E>(p, stream);
+    else launch_group_nq<HD, false, KVC, E>(p, stream);
     return hipGetLastError();
   }
   const long nblocks = (long)p.batch * p.nheads * p.num_splits * p.seqlen_q;
   if (p.alibi)
-    hipLaunchKernelGGL((decode_split_kernel<HD, true, KVC>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream,
-                       p);
+    hipLaunchKernelGGL((decode_split_kernel<HD, true, KVC, E>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<HD, false, KVC>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0, stream,
-                       p);
+    hipLaunchKernelGGL((decode_split_kernel<HD, false, KVC, E>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
-template <int HD>
-static hipError_t launch_decode_hd(const FwdParams& p, hipStream_t stream) {
-  return launch_decode_kvc<HD, false>(p, stream);
-}
-
-template <int HD>
+template <int HD, typename E>
 static hipError_t launch_kvcache_hd(const FwdParams& p, const uint16_t* k_new, const uint16_t* v_new,
                                     uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
                                     uint16_t* qrot, hipStream_t stream) {
   const long n_kv = (long)p.batch * p.seqlen_new * p.nheads_k;
   const long n_q = cos != nullptr ? (long)p.batch * p.seqlen_q * p.nheads : 0;
   if (n_kv + n_q > 0)
-    hipLaunchKernelGGL(kvcache_prep_kernel<HD>, dim3((unsigned)((n_kv + n_q + 3) / 4)), dim3(256), 0, stream, p,
-                       k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, n_kv, n_q);
+    hipLaunchKernelGGL((kvcache_prep_kernel<HD, E>), dim3((unsigned)((n_kv + n_q + 3) / 4)), dim3(256), 0, stream,
+                       p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, n_kv, n_q);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   FwdParams d = p;
   if (cos != nullptr) d.q = qrot;  // the decode kernel reads the rotated queries
-  return launch_decode_kvc<HD, true>(d, stream);
+  return launch_decode_kvc<HD, true, E>(d, stream);
+}
+
+template <typename E>
+static hipError_t launch_kvcache_e(const FwdParams& p, int headdim, const uint16_t* k_new, const uint16_t* v_new,
+                                   uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
+                                   uint16_t* qrot, hipStream_t stream) {
+  switch (headdim) {
+    case 64: return launch_kvcache_hd<64, E>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    case 128: return launch_kvcache_hd<128, E>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    case 256: return launch_kvcache_hd<256, E>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // KV-cache decode: append (and rotate), then the split partials.  The caller runs
@@ -547,37 +553,43 @@ static hipError_t launch_kvcache_hd(const FwdParams& p, const uint16_t* k_new, c
 hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new, const uint16_t* v_new,
                           uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
                           uint16_t* qrot, hipStream_t stream) {
-  switch (headdim) {
-    case 64: return launch_kvcache_hd<64>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
-    case 128: return launch_kvcache_hd<128>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
-    case 256: return launch_kvcache_hd<256>(p, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return p.f16 ? launch_kvcache_e<_Float16>(p, headdim, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream)
+               : launch_kvcache_e<__bf16>(p, headdim, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
 }
 
 // Key rows one decode step covers per wave (blocks of a paged cache must hold a whole
 // number of them): DEC_UNROLL * 64 / (headdim / 8).
 int decode_step_keys(int headdim) { return DEC_UNROLL * 64 / (headdim / 8); }
 
-hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream) {
+template <typename E>
+static hipError_t launch_decode_e(const FwdParams& p, int headdim, hipStream_t stream) {
   switch (headdim) {
-    case 64: return launch_decode_hd<64>(p, stream);
-    case 128: return launch_decode_hd<128>(p, stream);
-    case 256: return launch_decode_hd<256>(p, stream);
+    case 64: return launch_decode_kvc<64, false, E>(p, stream);
+    case 128: return launch_decode_kvc<128, false, E>(p, stream);
+    case 256: return launch_decode_kvc<256, false, E>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream) {
+hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream) {
+  return p.f16 ? launch_decode_e<_Float16>(p, headdim, stream) : launch_decode_e<__bf16>(p, headdim, stream);
+}
+
+template <typename E>
+static hipError_t launch_combine_e(const CombineParams& p, int headdim, hipStream_t stream) {
   const long rows = (long)p.batch * p.nheads * p.seqlen_q;
   const dim3 grid((unsigned)((rows + 3) / 4));
   switch (headdim) {
-    case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<256>), grid, dim3(256), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<64, E>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<128, E>), grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<256, E>), grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream) {
+  return p.f16 ? launch_combine_e<_Float16>(p, headdim, stream) : launch_combine_e<__bf16>(p, headdim, stream);
 }
 
 }  // namespace fa

@@ -11,18 +11,19 @@
 // the second output), "并行性" (grid over batch x heads, plus the sequence
 // dimension for long inputs), "工作分区" (query rows split across the waves of a
 // block, K and V shared by all of them), "2.1" (bottom-right causal alignment,
-// zero rows) and "2.3" (sliding window).
+// zero rows), "2.3" (sliding window) and "2.4" (ALiBi).  q/k/v/out are bf16 or
+// fp16 (the element type E); the arithmetic is the same for both.
 //
 // Design for CDNA4 (not a translation of the pages' A100 layout):
 //  * one workgroup = 4 wave64s = 128 query rows (32 per wave); one workgroup per
 //    (batch, head, query tile[, key split]); the linear block id is remapped so
 //    that each XCD works on a contiguous range of (batch, head) and keeps that
 //    head's K/V in its own L2;
-//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16/f16:
 //    every lane owns one query column, so the softmax row statistics are
 //    lane-local plus one v_permlane32_swap between the two half-waves;
 //  * K rows are stored in LDS with bits 2 and 3 of the row index swapped; with
-//    that order the fp32 S^T accumulator, rounded to bf16, is already laid out as
+//    that order the fp32 S^T accumulator, rounded to 16 bits, is already laid out as
 //    the B operand of O^T += V^T P^T, so P never leaves the registers;
 //  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
 //    destination, no staging registers); V stays in its natural [key][d] layout
@@ -37,7 +38,7 @@
 //    grows by more than 2^8; otherwise the stale maximum is kept, which leaves the
 //    result exact (O and l share it) and removes the rescale from almost every tile;
 //  * exponentials use exp2 with scale*log2(e) folded into one FMA; the row sum is
-//    accumulated from the fp32 exponentials (P is rounded to bf16 only for P V);
+//    accumulated from the fp32 exponentials (P is rounded to E only for P V);
 //  * the buffer loads' range ends at the last valid key, so ragged tails land in
 //    LDS as zeros without branches; only tiles crossing a mask boundary run the
 //    per-element visibility test.
@@ -164,8 +165,8 @@ __device__ __forceinline__ void wait_tile_loads() {
 
 // S^T (64 keys x 32 queries of this wave) = K_tile Q^T, two 32x32 blocks.
 // `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
-template <int HD>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const bf16x8 (&qf)[HD / 16]) {
+template <int HD, typename E>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const x8<E> (&qf)[HD / 16]) {
   using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   s[0] = f32x16{};
   s[1] = f32x16{};
@@ -173,8 +174,8 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
   for (int kk = 0; kk < HD / 16; ++kk) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kt + 32 * kb * T::KPITCH + 32 * kk);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+      const x8<E> a = *(const __attribute__((address_space(3))) x8<E>*)(kt + 32 * kb * T::KPITCH + 32 * kk);
+      s[kb] = mfma32(a, qf[kk], s[kb]);
     }
   }
 }
@@ -182,14 +183,14 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
 // A operand of O^T += V^T P^T for column block db and key chunk ci: V^T[d][16ci + 8*(lane/32) + 0..7]
 // for d = 32db + lane%32.  `vt` is this lane's transpose-read address in a V buffer
 // (see vt_lane_offset); each read returns 4 consecutive keys of one column.
-template <int HD>
-__device__ __forceinline__ bf16x8 v_operand(const lds_u8* vt, int db, int ci) {
+template <int HD, typename E>
+__device__ __forceinline__ x8<E> v_operand(const lds_u8* vt, int db, int ci) {
   using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + 16 * ci * T::VPITCH + 64 * db));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (16 * ci + 4) * T::VPITCH + 64 * db));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
+  return __builtin_bit_cast(x8<E>, both);
 }
 
 // Byte offset of this lane's transpose reads in a V buffer.  Within each group of
@@ -275,9 +276,9 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ
               SG_TRANS = 0x400;
 
 // Per-wave state of the forward loop.
-template <int HD>
+template <int HD, typename E>
 struct FwdState {
-  bf16x8 qf[HD / 16];       // Q^T fragments (B operand of S^T = K Q^T)
+  x8<E> qf[HD / 16];       // Q^T fragments (B operand of S^T = K Q^T)
   f32x16 oacc[HD / 32];     // O^T accumulator, unscaled
   float m_run;              // reference maximum of the exponentials (log2 units)
   float l_run;              // this lane's share of the row sum against m_run
@@ -320,8 +321,8 @@ struct LdsBufs {
 // One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), loads of
 // K(t+2) and V(t+1) into the free buffers, reference-maximum update.  Ends with
 // the tile barrier.
-template <int HD, int NW, bool ALIBI>
-__device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
+template <int HD, int NW, bool ALIBI, typename E>
+__device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
                                           int t_begin, const KVStream<HD, NW>& kv, const LdsBufs& lb, int half,
                                           float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
                                           int i_last, int off) {
@@ -336,11 +337,11 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
   kv.load_v(lb.v[bm1], t + NB - 1);
 
   // S(t+1) = K(t+1) Q^T
-  qk_tile<HD>(s_nxt, lb.kl[b1], st.qf);
+  qk_tile<HD, E>(s_nxt, lb.kl[b1], st.qf);
 
-  // P(t) = exp2(S(t) * cs - m), rounded to bf16 for the P V product
+  // P(t) = exp2(S(t) * cs - m), rounded to E for the P V product
   const float negm = (st.m_run == -INFINITY) ? 0.f : st.b_cur - st.m_run;
-  bf16x8 pf[4];
+  x8<E> pf[4];
   float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
   for (int ci = 0; ci < 4; ++ci) {
@@ -350,13 +351,13 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
     for (int e = 0; e < 4; ++e) {
       const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm));
       const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm));
-      pk[e] = pack_bf16x2(p0, p1);
+      pk[e] = pack2<E>(p0, p1);
       // the row sum stays in fp32: the lse needs it to ~1e-4 relative, which a sum
       // of bf16-rounded terms (2^-9 each) cannot guarantee
       lsum0 += p0;
       lsum1 += p1;
     }
-    pf[ci] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    pf[ci] = __builtin_bit_cast(x8<E>, u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
   // At headdim 256 (one wave per SIMD) keep the row-sum adds in this block, between
   // the products; left alone they sink past the masking branch below.  With two
@@ -370,8 +371,8 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
   for (int ci = 0; ci < 4; ++ci) {
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      const bf16x8 a = v_operand<HD>(lb.vl[b0], db, ci);
-      st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ci], st.oacc[db], 0, 0, 0);
+      const x8<E> a = v_operand<HD, E>(lb.vl[b0], db, ci);
+      st.oacc[db] = mfma32(a, pf[ci], st.oacc[db]);
     }
   }
 
@@ -468,7 +469,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD>& st, const f32x16 (&s_cur
 }
 
 // One work item: (batch, head, query tile[, key split]) number `item` of `items`.
-template <int HD, int NW, bool ALIBI, bool SPLIT>
+template <int HD, int NW, bool ALIBI, bool SPLIT, typename E>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int item, int items) {
   using T = Tile<HD, NW>;
   constexpr int BR = 32 * NW;  // query rows per workgroup
@@ -556,7 +557,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   }
 
   // ---- Q fragments: B operand of S^T = K Q^T, held for the whole loop ----------
-  FwdState<HD> st;
+  FwdState<HD, E> st;
   const int my_q = i0 + wave * 32 + lrow;
   const int my_pos = my_q + off;
 #pragma unroll
@@ -564,7 +565,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_q < Sq) raw = *(const u32x4*)(qbase + (long)my_q * row_stride + 16 * kk + 8 * half);
     raw = (raw & p.q_and) ^ p.q_sign;
-    st.qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    st.qf[kk] = __builtin_bit_cast(x8<E>, raw);
   }
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) st.oacc[db] = f32x16{};
@@ -573,7 +574,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   st.b_cur = 0.f;
   const float c = p.scale_log2;
   float slope = 0.f;
-  if constexpr (ALIBI) slope = p.alibi[h] * kLog2e;  // bias in log2 units
+  if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;  // bias in log2 units
   // multiplier turning the stored scores into log2 units
   const float cs = ALIBI ? 1.f : c;
 
@@ -588,7 +589,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     for (int j = 0; j + 1 < T::NBUF; ++j) kv.load_v(lb.v[j], t_begin + j);
     wait_tile_loads<0>();
     __syncthreads();
-    qk_tile<HD>(s_a, lb.kl[0], st.qf);
+    qk_tile<HD, E>(s_a, lb.kl[0], st.qf);
     const int j0 = key_lo + t_begin * BC;
     st.m_run = prep_scores<ALIBI>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
@@ -596,10 +597,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 
   // two tiles per trip so S(t) and S(t+1) swap roles without register copies
   for (int t = t_begin; t < t_end; t += 2) {
-    tile_step<HD, NW, ALIBI>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
+    tile_step<HD, NW, ALIBI, E>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
     if (t + 1 >= t_end) break;
-    tile_step<HD, NW, ALIBI>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
-                             i_last, off);
+    tile_step<HD, NW, ALIBI, E>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+                                i_last, off);
   }
   f32x16* const oacc = st.oacc;
   const float m_run = st.m_run;
@@ -619,8 +620,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
       for (int g = 0; g < 4; ++g) {
         // accumulator rows 4g..4g+3 of block db hold columns 32db + 8g + 4*half + 0..3
         const int d0 = 32 * db + 8 * g + 4 * half;
-        u32x2 o = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                   pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        u32x2 o = {pack2<E>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                   pack2<E>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
         *(u32x2*)(obase + d0) = o;
       }
     if (half == 0) {
@@ -647,16 +648,20 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 // One workgroup per work item.  (A grid of only the resident workgroups looping
 // over items with a static stride was measured slower: the causal items' unequal
 // lengths then leave CUs idle.)
-template <int HD, int NW, bool ALIBI, bool SPLIT>
+template <int HD, int NW, bool ALIBI, bool SPLIT, typename E>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p, int items) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD, NW>::LDS_BYTES];
-  fwd_item<HD, NW, ALIBI, SPLIT>(p, smem, blockIdx.x, items);
+  fwd_item<HD, NW, ALIBI, SPLIT, E>(p, smem, blockIdx.x, items);
 }
 
 template <int HD, int NW, bool ALIBI, bool SPLIT>
 hipError_t launch_fwd_instance(const FwdParams& p, long nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<HD, NW, ALIBI, SPLIT>), dim3((unsigned)nblocks), dim3(64 * NW), 0, stream, p,
-                     (int)nblocks);
+  if (p.f16)
+    hipLaunchKernelGGL((fwd_kernel<HD, NW, ALIBI, SPLIT, _Float16>), dim3((unsigned)nblocks), dim3(64 * NW), 0,
+                       stream, p, (int)nblocks);
+  else
+    hipLaunchKernelGGL((fwd_kernel<HD, NW, ALIBI, SPLIT, __bf16>), dim3((unsigned)nblocks), dim3(64 * NW), 0,
+                       stream, p, (int)nblocks);
   return hipGetLastError();
 }
 

@@ -65,8 +65,9 @@ def sweep_workload(seqlen: int, causal: bool = False) -> Workload:
 
 
 def make_qkv(batch: int, seqlen_q: int, seqlen_k: int, nheads: int, headdim: int, seed: int,
-             nheads_k: Optional[int] = None, device: str = "cpu"):
-    """Draw q [B,Sq,H,D], k and v [B,Sk,H,D] as bf16 tensors from one seeded generator.
+             nheads_k: Optional[int] = None, device: str = "cpu", dtype: torch.dtype = torch.bfloat16):
+    """Draw q [B,Sq,H,D], k and v [B,Sk,H,D] from one seeded generator: N(0, 1) in fp32,
+    rounded to `dtype` (bf16 or fp16, nearest even).
 
     device="cpu" (the default) gives the tensors the oracle and the parity tests
     use.  A GPU device draws from that device's generator instead: same
@@ -76,7 +77,7 @@ def make_qkv(batch: int, seqlen_q: int, seqlen_k: int, nheads: int, headdim: int
     g = torch.Generator(device=device).manual_seed(seed)
 
     def draw(*shape):
-        return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+        return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(dtype)
 
     q = draw(batch, seqlen_q, nheads, headdim)
     k = draw(batch, seqlen_k, hk, headdim)
@@ -84,9 +85,13 @@ def make_qkv(batch: int, seqlen_q: int, seqlen_k: int, nheads: int, headdim: int
     return q, k, v
 
 
-def make_alibi_slopes(nheads: int) -> torch.Tensor:
-    """fp32 slopes 2^(-8 (i+1) / nheads), i = 0..nheads-1."""
-    return torch.tensor([2.0 ** (-8.0 * (i + 1) / nheads) for i in range(nheads)], dtype=torch.float32)
+def make_alibi_slopes(nheads: int, batch: Optional[int] = None) -> torch.Tensor:
+    """fp32 slopes 2^(-8 (i+1) / nheads), i = 0..nheads-1, shape (nheads,); with `batch`,
+    a (batch, nheads) table whose row b is that row times 2^(-b/4)."""
+    row = [2.0 ** (-8.0 * (i + 1) / nheads) for i in range(nheads)]
+    if batch is None:
+        return torch.tensor(row, dtype=torch.float32)
+    return torch.tensor([[x * 2.0 ** (-b / 4.0) for x in row] for b in range(batch)], dtype=torch.float32)
 
 
 def workload_inputs(w: Workload):

@@ -18,11 +18,17 @@
  *                                when seqlen_q != seqlen_k; an all-masked row gives zeros;
  *     section "2.2：针对推理进行优化": for very short queries the KV cache is split over
  *                                workgroups and a separate kernel merges the results;
- *     section "2.3：局部（即滑动窗口）注意力": sliding-window local attention.
+ *     section "2.3：局部（即滑动窗口）注意力": sliding-window local attention;
+ *     section "2.4：ALiBi": ALiBi slopes, one per head or one per (batch, head).
+ *   The interface's dtype checks ("代码解读：FlashSelfAttention") accept fp16 and bf16.
  *
  * Conventions shared by every entry point
- *   - q, k, v, out: bf16, contiguous [batch, seqlen, nheads, headdim], headdim innermost.
- *     q and out have seqlen_q rows, k and v have seqlen_k rows, same nheads.
+ *   - q, k, v, out: 16-bit floating point, contiguous [batch, seqlen, nheads, headdim],
+ *     headdim innermost.  q and out have seqlen_q rows, k and v have seqlen_k rows,
+ *     same nheads.  `dtype` names the element type of every such tensor of a call
+ *     (the gradients of fa_bwd and the KV cache included): FA_BF16 or FA_FP16.  The
+ *     arithmetic is the same for both: fp32 accumulation, the probabilities rounded
+ *     to dtype for the P V product, the output rounded to dtype (nearest even).
  *   - lse: fp32, contiguous [batch, nheads, seqlen_q], natural logarithm of
  *     sum_j exp(softmax_scale * q_i . k_j + bias_ij) over the visible keys.
  *   - Visibility (bottom-right alignment): query i sits at key position
@@ -30,8 +36,10 @@
  *         (window_left  < 0 || j >= c_i - window_left) &&
  *         (window_right < 0 || j <= c_i + window_right),
  *     bounds inclusive; causal != 0 sets window_right to 0 (causal wins).
- *   - ALiBi: alibi_slopes is NULL (no bias) or a device fp32 array [nheads];
- *     bias_ij = -alibi_slopes[h] * |c_i - j|, added after the scaling.
+ *   - ALiBi: alibi_slopes is NULL (no bias) or a device fp32 array, [nheads] when
+ *     alibi_per_batch is 0 and [batch, nheads] when it is 1 (for fa_fwd_varlen, one
+ *     row per packed sequence); bias_ij = -slope(b, h) * |c_i - j|, added after the
+ *     scaling.  alibi_per_batch must be 0 or 1 (it is ignored without slopes).
  *   - A row with no visible key gets out = 0 and lse = -inf.
  *   - softmax_scale is used exactly as given (any finite value, negative included).
  *   - headdim must be 64, 128 or 256.
@@ -48,7 +56,9 @@
  *   FA_OK (0) on success.  On any error nothing is launched and no output is touched:
  *   FA_ERR_INVALID_ARG (-1): a NULL required pointer, a size < 1, a window side < -1,
  *                            num_splits outside [1, seqlen_k], a non-finite softmax_scale,
- *                            or a problem whose element count overflows 64-bit indexing;
+ *                            a dtype other than FA_BF16 / FA_FP16, alibi_per_batch
+ *                            other than 0 / 1, or a problem whose element count
+ *                            overflows 64-bit indexing;
  *   FA_ERR_UNSUPPORTED (-2): headdim not in {64, 128, 256}, or nheads * headdim > 2^22;
  *   FA_ERR_LAUNCH      (-3): the HIP runtime reported an error for the launch.
  *   No exception crosses the ABI and nothing is printed.
@@ -67,21 +77,26 @@ extern "C" {
 #define FA_ERR_UNSUPPORTED (-2)
 #define FA_ERR_LAUNCH (-3)
 
+/* element type of the 16-bit tensors (the dtype argument) */
+#define FA_BF16 0
+#define FA_FP16 1
+
 /*
  * fa_fwd - attention forward for a padded batch [FA-overview, "使用示例", "参数说明",
  * "算法 / 前向传播", "2.1", "2.3"].
- *   q      [batch, seqlen_q, nheads, headdim] bf16 (device, read)
- *   k, v   [batch, seqlen_k, nheads, headdim] bf16 (device, read)
- *   out    [batch, seqlen_q, nheads, headdim] bf16 (device, written)
+ *   q      [batch, seqlen_q, nheads, headdim] dtype (device, read)
+ *   k, v   [batch, seqlen_k, nheads, headdim] dtype (device, read)
+ *   out    [batch, seqlen_q, nheads, headdim] dtype (device, written)
  *   lse    [batch, nheads, seqlen_q]          fp32 (device, written)
- *   causal, window_left, window_right, alibi_slopes: see the conventions above.
+ *   causal, window_left, window_right, alibi_slopes, alibi_per_batch, dtype: see the
+ *   conventions above.
  * One workgroup per (batch, head, block of 128 query rows); every output element
  * is written exactly once, without atomics, so results are bitwise reproducible.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
            int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
            float softmax_scale, int causal, int window_left, int window_right,
-           const float* alibi_slopes, hipStream_t stream);
+           const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
 
 /*
  * fa_fwd_splitkv - first half of the split-KV forward [FA-overview, "2.2"].
@@ -100,7 +115,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v,
                    float* out_partial, float* lse_partial,
                    int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
                    float softmax_scale, int causal, int window_left, int window_right,
-                   const float* alibi_slopes, int num_splits, hipStream_t stream);
+                   const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
+                   hipStream_t stream);
 
 /*
  * fa_fwd_varlen - attention forward over a packed batch of sequences of different
@@ -112,8 +128,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v,
  *                [cu_seqlens_q[b], cu_seqlens_q[b+1]); cu_seqlens_q[0] = 0 and the
  *                array is non-decreasing;
  *   cu_seqlens_k [batch + 1] int32 (device, read): the same for k/v rows;
- *   q, out [total_q, nheads, headdim]   bf16 (device), total_q = cu_seqlens_q[batch]
- *   k, v   [total_k, nheads_k, headdim] bf16 (device), total_k = cu_seqlens_k[batch]
+ *   q, out [total_q, nheads, headdim]   dtype (device), total_q = cu_seqlens_q[batch]
+ *   k, v   [total_k, nheads_k, headdim] dtype (device), total_k = cu_seqlens_k[batch]
  *   lse    [nheads, total_q]            fp32 (device, written)
  *   max_seqlen_q, max_seqlen_k: at least every sequence's length (they size the grid;
  *                rows of a longer sequence past max_seqlen_q are left unwritten);
@@ -121,7 +137,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v,
  *             (nheads_k = nheads: ordinary multi-head, 1: a single shared K/V head).
  * Each sequence is its own attention problem: causal alignment, windows and ALiBi
  * use that sequence's lengths (query i of sequence b sits at key position
- * i + Sk_b - Sq_b).  alibi_slopes is indexed by query head.  The cu_seqlens arrays
+ * i + Sk_b - Sq_b).  alibi_slopes is indexed by query head (and by sequence when
+ * alibi_per_batch is 1).  The cu_seqlens arrays
  * are read on the device only, so the host cannot check them: they must describe
  * rows inside q/k/v/out (an invalid array makes the kernel read or write outside
  * the buffers).  Errors as for fa_fwd, plus FA_ERR_INVALID_ARG for a NULL cu_seqlens
@@ -131,19 +148,19 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int max_seqlen_q,
                   int max_seqlen_k, int total_q, int nheads, int nheads_k, int headdim,
                   float softmax_scale, int causal, int window_left, int window_right,
-                  const float* alibi_slopes, hipStream_t stream);
+                  const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
 
 /*
  * fa_combine - second half of the split-KV forward [FA-overview, "2.2"].
  * Per row: L = ln sum_s exp(lse_partial[s]); out = sum_s exp(lse_partial[s] - L) *
  * out_partial[s]; lse = L.  A row where every split is empty gets out = 0, lse = -inf.
  *   out_partial, lse_partial: as written by fa_fwd_splitkv (device, read)
- *   out [batch, seqlen_q, nheads, headdim] bf16 (device, written)
+ *   out [batch, seqlen_q, nheads, headdim] dtype (device, written)
  *   lse [batch, nheads, seqlen_q]          fp32 (device, written)
  * num_splits must be >= 1 (the partial layout does not depend on seqlen_k).
  */
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse,
-               int batch, int seqlen_q, int nheads, int headdim, int num_splits,
+               int batch, int seqlen_q, int nheads, int headdim, int num_splits, int dtype,
                hipStream_t stream);
 
 /*
@@ -151,21 +168,21 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
  * the keys are split across workgroups and merged by a second kernel; the KV-cache
  * entry rotates q and the new keys and appends them to the cache in place), "2.5"
  * (paged KV cache)].
- *   q [batch, seqlen_q, nheads, headdim] bf16 (device, read), 1 <= seqlen_q <= 8
+ *   q [batch, seqlen_q, nheads, headdim] dtype (device, read), 1 <= seqlen_q <= 8
  *   k_cache, v_cache (device, read and written): block_table != NULL: paged,
- *       [num_blocks, page_size, nheads_k, headdim] bf16, logical block n of sequence b
+ *       [num_blocks, page_size, nheads_k, headdim] dtype, logical block n of sequence b
  *       is physical block block_table[b * max_blocks_per_seq + n]; page_size a power of
  *       two, at least 64;  block_table == NULL: contiguous [batch, page_size, nheads_k,
  *       headdim], page_size being the capacity per sequence.
  *   cache_seqlens [batch] int32 (device, read): rows already in the cache.
- *   k_new, v_new [batch, seqlen_new, nheads_k, headdim] bf16 (device, read) or NULL when
+ *   k_new, v_new [batch, seqlen_new, nheads_k, headdim] dtype (device, read) or NULL when
  *       seqlen_new = 0: appended at rows cache_seqlens[b] .. + seqlen_new - 1 (written into
  *       the cache before the attention reads it).
  *   rotary_cos, rotary_sin [positions, rotary_dim / 2] fp32 (device, read) or both NULL:
  *       query row i and new key row i are rotated at position cache_seqlens[b] + i, pairs
  *       (x_d, x_{d + rotary_dim/2}) for d < rotary_dim / 2 (rotary_dim even, <= headdim);
- *       the rotated keys are stored in the cache.
- *   out [batch, seqlen_q, nheads, headdim] bf16, lse [batch, nheads, seqlen_q] fp32
+ *       the rotated keys are stored in the cache, rounded to dtype.
+ *   out [batch, seqlen_q, nheads, headdim] dtype, lse [batch, nheads, seqlen_q] fp32
  *       (device, written; out also holds the rotated queries between the two passes).
  *   out_partial, lse_partial: caller-owned scratch of at least max_splits splits in the
  *       fa_fwd_splitkv layout.  num_splits = 0 picks the split count (about 2048
@@ -184,7 +201,8 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
                    void* out, float* lse, float* out_partial, float* lse_partial, int max_splits,
                    int batch, int seqlen_q, int nheads, int nheads_k, int headdim,
                    float softmax_scale, int causal, int window_left, int window_right,
-                   const float* alibi_slopes, int num_splits, hipStream_t stream);
+                   const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
+                   hipStream_t stream);
 
 /*
  * fa_bwd - gradients of the attention forward [FA-overview, "算法 / 反向传播": P is
@@ -194,9 +212,9 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
  *   dV = P^T dO,  D = rowsum(dO o O),  dS = P o (dO V^T - D),
  *   dQ = softmax_scale * dS K,  dK = softmax_scale * dS^T Q.
  *   q, k, v, out   as for fa_fwd; out and lse are the forward's outputs (device, read)
- *   dout [batch, seqlen_q, nheads, headdim] bf16 (device, read): gradient of out
- *   dq   [batch, seqlen_q, nheads, headdim] bf16 (device, written)
- *   dk, dv [batch, seqlen_k, nheads, headdim] bf16 (device, written)
+ *   dout [batch, seqlen_q, nheads, headdim] dtype (device, read): gradient of out
+ *   dq   [batch, seqlen_q, nheads, headdim] dtype (device, written)
+ *   dk, dv [batch, seqlen_k, nheads, headdim] dtype (device, written)
  *   delta [batch, nheads, seqlen_q] fp32 (device): caller-owned scratch, written with D
  *   The other arguments mean what they mean for fa_fwd and must be the forward's.
  * Rows with no visible key (lse = -inf) get dq = 0 and add nothing to dk, dv.  Keys no
@@ -209,7 +227,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int batch, int seqlen_q, int seqlen_k, int nheads, int headdim,
            float softmax_scale, int causal, int window_left, int window_right,
-           const float* alibi_slopes, hipStream_t stream);
+           const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
 
 /* fa_status_str - static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -51,7 +51,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 def fwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, batch=1, seqlen_q=4, seqlen_k=4, nheads=2,
-             headdim=64, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None, stream=None)
+             headdim=64, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None, per_batch=0, dtype=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -61,7 +61,8 @@ def fwd_args(**over):
     (dict(batch=0), -1), (dict(seqlen_q=0), -1), (dict(seqlen_k=-3), -1), (dict(nheads=0), -1),
     (dict(headdim=0), -1), (dict(wl=-2), -1), (dict(wr=-5), -1), (dict(scale=math.inf), -1),
     (dict(scale=math.nan), -1), (dict(headdim=96), -2), (dict(headdim=32), -2), (dict(headdim=512), -2),
-    (dict(seqlen_q=(1 << 30) + 1), -1),
+    (dict(seqlen_q=(1 << 30) + 1), -1), (dict(dtype=2), -1), (dict(dtype=-1), -1), (dict(per_batch=2), -1),
+    (dict(per_batch=-1, alibi=FAKE), -1),
 ])
 def test_fwd_rejects_invalid(lib, over, code):
     assert lib.fa_fwd(*fwd_args(**over)) == code
@@ -69,18 +70,18 @@ def test_fwd_rejects_invalid(lib, over, code):
 
 @pytest.mark.parametrize("over,ns,code", [
     (dict(), 0, -1), (dict(), 5, -1), (dict(), -1, -1), (dict(out=None), 2, -1),
-    (dict(headdim=80), 2, -2), (dict(scale=math.nan), 2, -1),
+    (dict(headdim=80), 2, -2), (dict(scale=math.nan), 2, -1), (dict(dtype=3), 2, -1), (dict(per_batch=5), 2, -1),
 ])
 def test_splitkv_rejects_invalid(lib, over, ns, code):
     a = fwd_args(**over)
-    a.insert(15, ns)  # num_splits comes just before the stream
+    a.insert(17, ns)  # num_splits comes just before the stream
     assert lib.fa_fwd_splitkv(*a) == code
 
 
 def varlen_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, batch=2, max_sq=8, max_sk=8,
              total_q=10, nheads=4, nheads_k=2, headdim=128, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None,
-             stream=None)
+             per_batch=0, dtype=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -90,6 +91,7 @@ def varlen_args(**over):
     (dict(nheads_k=0), -1), (dict(nheads_k=3), -1), (dict(nheads=2, nheads_k=4), -1), (dict(total_q=0), -1),
     (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(max_sk=-1), -1), (dict(wl=-3), -1),
     (dict(scale=math.inf), -1), (dict(headdim=80), -2), (dict(nheads=1 << 16, nheads_k=1 << 16), -2),
+    (dict(dtype=2), -1), (dict(per_batch=3), -1),
 ])
 def test_varlen_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_varlen(*varlen_args(**over)) == code
@@ -98,7 +100,8 @@ def test_varlen_rejects_invalid(lib, over, code):
 def kvc_args(**over):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, table=FAKE, page=256, max_blocks=4, knew=None, vnew=None, snew=0,
              cos=None, sin=None, rd=0, out=FAKE, lse=FAKE, op=FAKE, lp=FAKE, max_splits=16, batch=2, sq=1, nheads=8,
-             nheads_k=2, headdim=128, scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, num_splits=0, stream=None)
+             nheads_k=2, headdim=128, scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, per_batch=0, dtype=0,
+             num_splits=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -108,7 +111,8 @@ def kvc_args(**over):
     (dict(sq=9), -1), (dict(snew=2), -1), (dict(snew=-1), -1), (dict(page=100), -1), (dict(page=32), -1),
     (dict(max_blocks=0), -1), (dict(nheads_k=3), -1), (dict(cos=FAKE), -1), (dict(cos=FAKE, sin=FAKE, rd=3), -1),
     (dict(cos=FAKE, sin=FAKE, rd=256), -1), (dict(num_splits=17), -1), (dict(num_splits=-1), -1),
-    (dict(max_splits=0), -1), (dict(headdim=80), -2), (dict(table=None, page=0), -1),
+    (dict(max_splits=0), -1), (dict(headdim=80), -2), (dict(table=None, page=0), -1), (dict(dtype=7), -1),
+    (dict(per_batch=2), -1),
 ])
 def test_kvcache_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_kvcache(*kvc_args(**over)) == code
@@ -117,7 +121,7 @@ def test_kvcache_rejects_invalid(lib, over, code):
 def bwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, batch=1,
              seqlen_q=4, seqlen_k=4, nheads=2, headdim=128, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None,
-             stream=None)
+             per_batch=0, dtype=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -126,16 +130,18 @@ def bwd_args(**over):
     (dict(out=None), -1), (dict(lse=None), -1), (dict(dout=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
     (dict(dv=None), -1), (dict(delta=None), -1), (dict(q=None), -1), (dict(batch=0), -1), (dict(seqlen_k=0), -1),
     (dict(wl=-2), -1), (dict(scale=math.nan), -1), (dict(headdim=256), -2), (dict(headdim=96), -2),
+    (dict(dtype=2), -1), (dict(per_batch=4), -1),
 ])
 def test_bwd_rejects_invalid(lib, over, code):
     assert lib.fa_bwd(*bwd_args(**over)) == code
 
 
 @pytest.mark.parametrize("args,code", [
-    ((None, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, None), -1),
-    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, None), -1),
-    ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 2, None), -1),
-    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 100, 2, None), -2),
+    ((None, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 0, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 0, 0, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 2, 0, None), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 100, 2, 0, None), -2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 2, None), -1),
 ])
 def test_combine_rejects_invalid(lib, args, code):
     assert lib.fa_combine(*args) == code
@@ -148,3 +154,5 @@ def test_binding_requires_gpu_tensors():
         fa.flash_attn_func(q, q, q)
     with pytest.raises(TypeError):
         fa.flash_attn_func(q.float(), q, q)
+    with pytest.raises(TypeError):  # one element type for q, k and v
+        fa.flash_attn_func(q, q.half(), q)
