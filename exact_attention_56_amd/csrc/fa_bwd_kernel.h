@@ -237,12 +237,24 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  int w = xcd_remap(blockIdx.x, items);
-  int qt = w % p.num_q_tiles;
-  w /= p.num_q_tiles;
-  const int b = w % p.batch;
-  const int h = w / p.batch;
-  if (p.window_right >= 0) qt = p.num_q_tiles - 1 - qt;  // longest rows first
+  // Causal mask or right window: later query tiles see more keys.  The query tile
+  // is then the slowest index, heaviest first over the whole grid (workgroup i
+  // serves (batch, head) i mod (batch * nheads)); otherwise tiles run fastest within
+  // the XCD-contiguous ranges of xcd_remap.
+  int qt, b, h;
+  if (p.window_right >= 0) {
+    const int bh_count = p.batch * p.nheads;
+    const int bh = blockIdx.x % bh_count;
+    qt = p.num_q_tiles - 1 - (int)blockIdx.x / bh_count;
+    b = bh % p.batch;
+    h = bh / p.batch;
+  } else {
+    int w = xcd_remap(blockIdx.x, items);
+    qt = w % p.num_q_tiles;
+    w /= p.num_q_tiles;
+    b = w % p.batch;
+    h = w / p.batch;
+  }
 
   const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
   const int wl = p.window_left, wr = p.window_right;
@@ -378,11 +390,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  int w = xcd_remap(blockIdx.x, items);
-  const int kt_idx = w % p.num_k_tiles;
-  w /= p.num_k_tiles;
-  const int b = w % p.batch;
-  const int h = w / p.batch;
+  // Causal mask or right window: earlier key tiles are seen by more queries; they
+  // run first over the whole grid, as in dq_kernel.
+  int kt_idx, b, h;
+  if (p.window_right >= 0) {
+    const int bh_count = p.batch * p.nheads;
+    const int bh = blockIdx.x % bh_count;
+    kt_idx = (int)blockIdx.x / bh_count;
+    b = bh % p.batch;
+    h = bh / p.batch;
+  } else {
+    int w = xcd_remap(blockIdx.x, items);
+    kt_idx = w % p.num_k_tiles;
+    w /= p.num_k_tiles;
+    b = w % p.batch;
+    h = w / p.batch;
+  }
 
   const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
   const int wl = p.window_left, wr = p.window_right;

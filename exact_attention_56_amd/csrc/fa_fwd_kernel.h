@@ -484,17 +484,30 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   // takes a contiguous range of items (xcd_remap), i.e. a slice of the heads over
   // every sequence of the batch: the XCDs then get equal work even when sequences
   // differ in length, and the query heads that share a K/V head stay on one XCD.
-  int w = xcd_remap(item, items);
-  int qt = w % p.num_q_tiles;
-  w /= p.num_q_tiles;
-  int split = 0;
-  if constexpr (SPLIT) {
-    split = w % p.num_splits;
-    w /= p.num_splits;
+  // Padded batches with a causal mask or right window (tiles of unequal length)
+  // instead run the query tile slowest, heaviest first over the whole grid, so the
+  // short tiles fill the end of the launch; workgroup i then serves (batch, head)
+  // i mod (batch * nheads), which keeps each (batch, head) on one XCD whenever
+  // batch * nheads is a multiple of 8 (the dispatcher deals ids round-robin).
+  int qt, split = 0, b, h;
+  if (!SPLIT && p.reverse_q && p.cu_q == nullptr) {
+    const int bh_count = p.batch * p.nheads;
+    const int bh = item % bh_count;
+    qt = p.num_q_tiles - 1 - item / bh_count;
+    b = bh % p.batch;
+    h = bh / p.batch;
+  } else {
+    int w = xcd_remap(item, items);
+    qt = w % p.num_q_tiles;
+    w /= p.num_q_tiles;
+    if constexpr (SPLIT) {
+      split = w % p.num_splits;
+      w /= p.num_splits;
+    }
+    b = w % p.batch;
+    h = w / p.batch;
+    if (p.reverse_q) qt = p.num_q_tiles - 1 - qt;
   }
-  const int b = w % p.batch;
-  const int h = w / p.batch;
-  if (p.reverse_q) qt = p.num_q_tiles - 1 - qt;
 
   // This sequence's rows: a padded batch has them at b * seqlen; a packed (varlen)
   // batch lists each sequence's first row in cu_q / cu_k.
