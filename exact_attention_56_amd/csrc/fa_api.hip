@@ -307,7 +307,7 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
   if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
   if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
   const long rows = (long)batch * nheads * seqlen_q;
-  if ((rows + 3) / 4 > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  if (rows > kMaxBlocks) return FA_ERR_INVALID_ARG;  // one workgroup per row
   fa::CombineParams p;
   p.out_partial = out_partial;
   p.lse_partial = lse_partial;

@@ -1,22 +1,22 @@
-// fa_decode_kernel.hip - split-KV decode partial kernel and the combine kernel (gfx950).
+// fa_decode_kernel.hip - split-KV decode partial kernel, KV-cache preparation and the
+// combine kernel (gfx950).
 //
 // Page "FlashAttention：快速且内存高效的准确注意力机制"
 // (cloud.tencent.com.cn/developer/article/2433927), section "2.2：针对推理进行优化":
 // with very short queries the cost is reading the KV cache, so the keys are split
-// across workgroups and a separate kernel merges the per-split results.
+// across workgroups and a separate kernel merges the per-split results; section
+// "2.5" (paged KV cache) for the block-table reads.
 //
-// Partial kernel: one workgroup per (batch, head, split, query row).  A query row
-// against a KV chunk is a matrix-vector product, so it runs on the vector ALUs and
-// is bound by HBM bandwidth: each key row (headdim 16-bit values) is read by HD/8 lanes with
-// one 16-byte load each, the dot product is finished with lane shuffles, and the
-// four waves walk interleaved slices of the chunk with their own online-softmax
-// state, merged through LDS at the end.  The output of a split is normalised
-// within the split, with its logsumexp; an empty split gives 0 and -inf.
-// When a K/V head serves several queries (grouped heads, or seqlen_q > 1) a grouped
-// variant takes up to eight of them per workgroup, so each key row is loaded once
-// for all of them.
+// Partial kernel: a few query rows against a KV chunk are matrix-vector products,
+// so they run on the vector ALUs and are bound by HBM bandwidth.  One workgroup per
+// (batch, K/V head, split, chunk of up to eight queries of that K/V head); each key
+// row (headdim 16-bit values) is read by HD/8 lanes with one 16-byte load each, and
+// the four waves walk interleaved slices of the chunk with their own online-softmax
+// state, merged through LDS at the end.  The output of a split is normalised within
+// the split, with its logsumexp; an empty split gives 0 and -inf.
 //
-// Combine kernel: out = sum_s exp(lse_s - L) out_s with L = ln sum_s exp(lse_s).
+// Combine kernel: out = sum_s exp(lse_s - L) out_s with L = ln sum_s exp(lse_s), one
+// workgroup per row.
 #include "fa_common.h"
 
 namespace fa {
@@ -31,178 +31,76 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_UNROLL = FA_DEC_UNROLL;  // key rows per lane per step
 constexpr int DEC_CPOL = FA_DEC_CPOL;      // KV loads are non-temporal (read once, streamed)
 
-
-// KVC: the keys come from a KV cache (fa_fwd_kvcache): sequence b has
-// cache_seqlens[b] + seqlen_new keys, block n of it lives in block block_table[b, n]
-// (or block b of a contiguous cache), and K/V may have fewer heads than Q.
-template <int HD, bool ALIBI, bool KVC, typename E>
-__global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(FwdParams p) {
-  constexpr int LPR = HD / 8;    // lanes per key row
-  constexpr int RPW = 64 / LPR;  // key rows per wave per load
-  constexpr int STEP = DEC_UNROLL * RPW;
-  __shared__ float sm_m[4], sm_l[4];
-  __shared__ float sm_acc[4][HD];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int g = lane / LPR;   // row group inside the wave
-  const int cidx = lane % LPR;  // 8-column chunk of the head dimension
-
-  int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int Sq = p.seqlen_q;
-  const int i = w % Sq;
-  w /= Sq;
-  const int split = w % p.num_splits;
-  w /= p.num_splits;
-  const int h = w % p.nheads;
-  const int b = w / p.nheads;
-  const int Sk = KVC ? p.cache_seqlens[b] + p.seqlen_new : p.seqlen_k;
-
-  const long row_stride = (long)p.nheads * HD;       // q
-  const long kv_stride = (long)p.nheads_k * HD;      // k, v
-  const int row_bytes = (int)kv_stride * 2;
-  const int hk = h / (p.nheads / p.nheads_k);
-
-  // visible keys of row i inside this split: [lo, hi)
-  const int pos = i + Sk - Sq;
-  int lo = min(Sk, split * p.split_len);
-  int hi = min(Sk, lo + p.split_len);
-  if (p.window_left >= 0) lo = max(lo, pos - p.window_left);
-  if (p.window_right >= 0) hi = min(hi, pos + p.window_right + 1);
-  const long kvb = KVC ? (long)hk * HD : (long)b * Sk * kv_stride + (long)hk * HD;  // key 0 / head offset
-  // KV-cache steps start on multiples of STEP so that none crosses a block; keys
-  // below lo are then masked
-  const int first = KVC ? (lo & ~(STEP - 1)) : lo;
-
-  // q chunk, pre-multiplied by softmax_scale * log2(e) (sign included)
-  const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
-  float qv[8];
-  {
-    const u32x4 raw = *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and;
+// Helpers of the grouped kernel.  Dot product of 8 packed 16-bit values (two 16-byte
+// chunks) in fp32: four v_dot2 instructions.  Each element is copied to a scalar
+// before the bit cast: a bit cast applied directly to a vector element expression
+// was compiled as a cast of element 0 every time.
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc, __bf16) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[2 * e] = widen_lo<E>(raw[e]) * c;
-      qv[2 * e + 1] = widen_hi<E>(raw[e]) * c;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ae = a[e], be = b[e];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, ae), __builtin_bit_cast(v2, be), acc, false);
   }
-  float slope = 0.f;
-  if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
-
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[8];
+  return acc;
+}
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc, _Float16) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-
-  for (int base = first + wave * STEP; base < hi; base += 4 * STEP) {
-    // buffer resources over keys [base, min(hi, base + STEP)): later keys read as zeros
-    const int nrec = min(hi - base, STEP) * row_bytes;
-    long row0 = base;  // physical row of key `base`
-    if constexpr (KVC) {
-      if (p.block_table != nullptr)
-        row0 = (long)p.block_table[(long)b * p.max_blocks + (base >> p.page_shift)] * p.page_size +
-               (base & (p.page_size - 1));
-      else
-        row0 = (long)b * p.page_size + base;
-    }
-    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvb + row0 * kv_stride), (short)0, nrec,
-                                                       0x00020000);
-    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvb + row0 * kv_stride), (short)0, nrec,
-                                                       0x00020000);
-    u32x4 kr[DEC_UNROLL], vr[DEC_UNROLL];
-#pragma unroll
-    for (int u = 0; u < DEC_UNROLL; ++u) {
-      const int off = (u * RPW + g) * row_bytes + cidx * 16;
-      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, DEC_CPOL));
-      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, DEC_CPOL));
-    }
-    float s[DEC_UNROLL];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < DEC_UNROLL; ++u) {
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part = fmaf(qv[2 * e], widen_lo<E>(kr[u][e]), part);
-        part = fmaf(qv[2 * e + 1], widen_hi<E>(kr[u][e]), part);
-      }
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-      const int key = base + u * RPW + g;
-      if constexpr (ALIBI) part -= slope * fabsf((float)(pos - key));
-      s[u] = (key < hi && (!KVC || key >= lo)) ? part : -INFINITY;
-      bmax = fmaxf(bmax, s[u]);
-    }
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
-
-    const float m_new = fmaxf(m_run, bmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    l_run *= alpha;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int u = 0; u < DEC_UNROLL; ++u) {
-      const float pu = fast_exp2(s[u] - m_use);
-      l_run += pu;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(pu, widen_lo<E>(vr[u][e]), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(pu, widen_hi<E>(vr[u][e]), acc[2 * e + 1]);
-      }
-    }
-    m_run = m_new;
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ae = a[e], be = b[e];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, ae), __builtin_bit_cast(v2, be), acc, false);
   }
-
-  // merge the row groups of this wave (same m_run across the wave)
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
-    l_run += __shfl_xor(l_run, o);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-  }
-  if (lane == 0) {
-    sm_m[wave] = m_run;
-    sm_l[wave] = l_run;
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm_acc[wave][cidx * 8 + e] = acc[e];
-  }
-  __syncthreads();
-
-  // merge the four waves
-  float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float wgt[4], L = 0.f;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    wgt[x] = fast_exp2(sm_m[x] - M_use);
-    L += sm_l[x] * wgt[x];
-  }
-  const long rowid = (((long)split * p.batch + b) * p.nheads + h) * Sq + i;
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* out = (float*)p.out + rowid * HD;
-  for (int d = tid; d < HD; d += DEC_THREADS) {
-    float o = 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) o = fmaf(sm_acc[x][d], wgt[x], o);
-    out[d] = o * inv;
-  }
-  if (tid == 0) p.lse[rowid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+  return acc;
 }
 
-// Grouped decode partial kernel: one workgroup per (batch, K/V head, split, chunk of
-// NQ queries).  The queries of a K/V head are its nheads / nheads_k query heads times
+// x of lane (l op CTRL) within its 16-lane row (DPP; every lane has a source).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPR consecutive lanes (8, 16 or 32) that share a key row, returned in
+// all of them: two quad permutations, then within 8 lanes the half-row mirror, or
+// within 16 the row rotations by 4 and 8; 32 adds one swap of the 16-lane halves.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  x += dpp_move<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  x += dpp_move<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+  if constexpr (LPR == 8) x += dpp_move<0x141>(x);  // row_half_mirror: the other quad
+  if constexpr (LPR >= 16) {
+    x += dpp_move<0x124>(x);  // row_ror 4
+    x += dpp_move<0x128>(x);  // row_ror 8
+  }
+  if constexpr (LPR == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Decode partial kernel: one workgroup per (batch, K/V head, split, chunk of NQ
+// queries).  The queries of a K/V head are its nheads / nheads_k query heads times
 // the seqlen_q rows (query n: head hk * G + n / Sq, row n % Sq); one workgroup takes NQ
-// of them, so each key row it loads serves NQ dot products instead of one.  Each
-// query keeps its own visible range, ALiBi slope and online-softmax state.
+// of them, so each key row it loads serves NQ dot products.  Each query keeps its own
+// visible range and ALiBi slope.
+//
+// HD/8 lanes per key row (one 16-byte chunk each), 64/(HD/8) rows per wave per load.
+// The dot products take packed v_dot2 instructions on the raw 16-bit values, the
+// lane-group sums run on DPP moves (no LDS permutes), every row group of a wave
+// keeps its own online-softmax state (merged once at the end, so no per-step
+// exchange of maxima), the reference maximum moves only when a score exceeds it by
+// more than 2^8 (as in the forward kernel), and steps inside every query's visible
+// range skip the mask.
+//
+// KVC: the keys come from a KV cache (fa_fwd_kvcache): sequence b has
+// cache_seqlens[b] + seqlen_new keys, and block n of it lives in block
+// block_table[b, n] (or block b of a contiguous cache).  Steps then start on
+// multiples of STEP so that none crosses a block; keys below the range are masked.
 template <int HD, bool ALIBI, bool KVC, int NQ, typename E>
 __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) {
   constexpr int LPR = HD / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int UNROLL = NQ <= 2 ? DEC_UNROLL : DEC_UNROLL / 2;  // registers: NQ copies of the state
   constexpr int STEP = UNROLL * RPW;
+  constexpr float TH = 8.0f;  // log2 units: keep a stale reference maximum while p <= 2^8
   __shared__ float sm_m[4][NQ], sm_l[4][NQ];
   __shared__ float sm_acc[4][NQ][HD];
 
@@ -231,9 +129,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
   const int s_hi = min(Sk, s_lo + p.split_len);
 
   const float c = (p.q_sign ? -p.scale_log2 : p.scale_log2);
-  float qv[NQ][8], slope[NQ];
+  u32x4 qv[NQ];
+  float slope[NQ];
   int q_lo[NQ], q_hi[NQ], q_pos[NQ];
-  int lo = s_hi, hi = s_lo;  // union of the queries' visible ranges in this split
+  int lo = s_hi, hi = s_lo;              // union of the queries' visible ranges in this split
+  int in_lo = s_lo, in_hi = s_hi;        // keys every query of the chunk sees
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int n = qc * NQ + j;
@@ -251,13 +151,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
       lo = min(lo, l0);
       hi = max(hi, h0);
     }
-    const u32x4 raw = valid ? *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and
-                            : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[j][2 * e] = widen_lo<E>(raw[e]) * c;
-      qv[j][2 * e + 1] = widen_hi<E>(raw[e]) * c;
+    if (valid) {
+      in_lo = max(in_lo, l0);
+      in_hi = min(in_hi, h0);
     }
+    qv[j] = valid ? *(const u32x4*)(p.q + ((long)b * Sq + i) * row_stride + (long)h * HD + cidx * 8) & p.q_and
+                  : u32x4{0u, 0u, 0u, 0u};
     slope[j] = 0.f;
     if constexpr (ALIBI) slope[j] = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
   }
@@ -265,7 +164,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
   const long kvb = KVC ? (long)hk * HD : (long)b * Sk * kv_stride + (long)hk * HD;
   const int first = KVC ? (lo & ~(STEP - 1)) : lo;
 
-  float m_run[NQ], l_run[NQ], acc[NQ][8];
+  float m_run[NQ], l_run[NQ], acc[NQ][8];  // per row group of the wave
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     m_run[j] = -INFINITY;
@@ -295,33 +194,29 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
       kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, DEC_CPOL));
       vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, DEC_CPOL));
     }
+    const bool inside = base >= in_lo && base + STEP <= in_hi;  // wave-uniform
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float sj[UNROLL];
       float bmax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          part = fmaf(qv[j][2 * e], widen_lo<E>(kr[u][e]), part);
-          part = fmaf(qv[j][2 * e + 1], widen_hi<E>(kr[u][e]), part);
-        }
-#pragma unroll
-        for (int o = LPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+        float part = lane_group_sum<LPR>(dot8(qv[j], kr[u], 0.f, E{})) * c;
         const int key = base + u * RPW + g;
         if constexpr (ALIBI) part -= slope[j] * fabsf((float)(q_pos[j] - key));
-        sj[u] = (key >= q_lo[j] && key < q_hi[j]) ? part : -INFINITY;
+        sj[u] = (inside || (key >= q_lo[j] && key < q_hi[j])) ? part : -INFINITY;
         bmax = fmaxf(bmax, sj[u]);
       }
+      const bool grow = bmax > m_run[j] + TH;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = !grow ? 1.f : (m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - bmax));
+        m_run[j] = grow ? bmax : m_run[j];
+        l_run[j] *= alpha;
 #pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
-      const float m_new = fmaxf(m_run[j], bmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[j] - m_use);
-      l_run[j] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+        for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+      }
+      // a group whose reference is still -inf has seen only masked keys: p = 0
+      const float m_use = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const float pu = fast_exp2(sj[u] - m_use);
@@ -332,13 +227,20 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
           acc[j][2 * e + 1] = fmaf(pu, widen_hi<E>(vr[u][e]), acc[j][2 * e + 1]);
         }
       }
-      m_run[j] = m_new;
     }
   }
 
-  // merge the row groups of each wave, then the four waves, per query
+  // merge the row groups of each wave (each against its own reference), then the
+  // four waves, per query
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
+    float M = m_run[j];
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float sc = (m_run[j] == -INFINITY) ? 0.f : fast_exp2(m_run[j] - M);
+    l_run[j] *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] *= sc;
 #pragma unroll
     for (int o = LPR; o < 64; o <<= 1) {
       l_run[j] += __shfl_xor(l_run[j], o);
@@ -346,7 +248,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
       for (int e = 0; e < 8; ++e) acc[j][e] += __shfl_xor(acc[j][e], o);
     }
     if (lane == 0) {
-      sm_m[wave][j] = m_run[j];
+      sm_m[wave][j] = M;
       sm_l[wave][j] = l_run[j];
     }
     if (g == 0) {
@@ -381,48 +283,75 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
   }
 }
 
+// Maximum / sum of x over the 256 threads of a workgroup (every thread gets it).
+__device__ __forceinline__ float block_max(float x, float* sm) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  __syncthreads();  // sm is free (a previous reduction has been read)
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+__device__ __forceinline__ float block_sum(float x, float* sm) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (sm[0] + sm[1]) + (sm[2] + sm[3]);
+}
+
+// One workgroup per output row.  The split weights exp(lse_s - L) come from two
+// block reductions (maximum, then sum) over the splits; the weighted sum of the
+// partial rows runs 256 / (HD/4) splits at a time, HD/4 threads per split with one
+// 16-byte load each, and the split groups are added through LDS at the end.
 template <int HD, typename E>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int PER_LANE = HD / 64;
-  const int lane = threadIdx.x & 63;
+  constexpr int TPS = HD / 4;     // threads per partial row (4 floats each)
+  constexpr int SPP = 256 / TPS;  // partial rows read per pass
+  __shared__ float sm_red[4];
+  __shared__ __attribute__((aligned(16))) float sm_acc[SPP][HD];
+  const int tid = threadIdx.x;
   const long rows = (long)p.batch * p.nheads * p.seqlen_q;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h)*Sq + i
-  if (row >= rows) return;
+  const long row = blockIdx.x;  // (b*H + h)*Sq + i
   const int i = (int)(row % p.seqlen_q);
   const long bh = row / p.seqlen_q;
   const int h = (int)(bh % p.nheads);
   const int b = (int)(bh / p.nheads);
-
+  const int ns = p.num_splits;
   const float* lp = p.lse_partial + row;
   const float* op = p.out_partial + row * HD;
   const long lstride = rows, ostride = rows * HD;
 
-  float M = -INFINITY;
-  for (int s = 0; s < p.num_splits; ++s) M = fmaxf(M, lp[s * lstride]);
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, lp[s * lstride]);
+  const float M = block_max(mx, sm_red);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float sum = 0.f;
+  for (int s = tid; s < ns; s += 256) sum += fast_exp2((lp[s * lstride] - M_use) * kLog2e);  // 0: empty split
+  const float L = block_sum(sum, sm_red);
 
-  float o[PER_LANE];
-#pragma unroll
-  for (int e = 0; e < PER_LANE; ++e) o[e] = 0.f;
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.num_splits; ++s) {
-      const float ls = lp[s * lstride];
-      const float wgt = fast_exp2((ls - M) * kLog2e);  // 0 for an empty split
-      L += wgt;
-      if (wgt != 0.f) {
-#pragma unroll
-        for (int e = 0; e < PER_LANE; ++e) o[e] = fmaf(wgt, op[s * ostride + lane + 64 * e], o[e]);
-      }
+  const int sg = tid / TPS, c = tid % TPS;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = sg; s < ns; s += SPP) {
+    const float wgt = fast_exp2((lp[s * lstride] - M_use) * kLog2e);
+    if (wgt != 0.f) {  // an empty split's partial row is never read
+      const f32x4 v = *(const f32x4*)(op + s * ostride + 4 * c);
+      acc += wgt * v;
     }
   }
+  *(f32x4*)&sm_acc[sg][4 * c] = acc;
+  __syncthreads();
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* out = p.out + (((long)b * p.seqlen_q + i) * p.nheads + h) * HD;
+  if (tid < HD) {
+    float o = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER_LANE; ++e) {
-    const uint32_t pk = pack2<E>(o[e] * inv, 0.f);
-    out[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
+    for (int g = 0; g < SPP; ++g) o += sm_acc[g][tid];
+    out[tid] = (uint16_t)(pack2<E>(o * inv, 0.f) & 0xffffu);
   }
-  if (lane == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
+  if (tid == 0) p.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 // Element e of a row x of E rotated at position `pos` (half-split rotary layout:
@@ -495,6 +424,7 @@ int decode_queries_per_block(int nq_total) { return nq_total <= 1 ? 1 : nq_total
 template <int HD, bool ALIBI, bool KVC, typename E>
 static void launch_group_nq(const FwdParams& p, hipStream_t stream) {
   switch (decode_queries_per_block(p.nheads / p.nheads_k * p.seqlen_q)) {
+    case 1: launch_group<HD, ALIBI, KVC, 1, E>(p, stream); break;
     case 2: launch_group<HD, ALIBI, KVC, 2, E>(p, stream); break;
     case 4: launch_group<HD, ALIBI, KVC, 4, E>(p, stream); break;
     default: launch_group<HD, ALIBI, KVC, 8, E>(p, stream); break;
@@ -503,20 +433,8 @@ static void launch_group_nq(const FwdParams& p, hipStream_t stream) {
 
 template <int HD, bool KVC, typename E>
 static hipError_t launch_decode_kvc(const FwdParams& p, hipStream_t stream) {
-  // several queries per K/V head (grouped heads or seqlen_q > 1): the grouped kernel
-  // loads each key row once for all of them
-  if (p.nheads / p.nheads_k * p.seqlen_q > 1) {
-    if (p.alibi) launch_group_nq<HD, true, KVC, E>(p, stream);
-    else launch_group_nq<HD, false, KVC, E>(p, stream);
-    return hipGetLastError();
-  }
-  const long nblocks = (long)p.batch * p.nheads * p.num_splits * p.seqlen_q;
-  if (p.alibi)
-    hipLaunchKernelGGL((decode_split_kernel<HD, true, KVC, E>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<HD, false, KVC, E>), dim3((unsigned)nblocks), dim3(DEC_THREADS), 0,
-                       stream, p);
+  if (p.alibi) launch_group_nq<HD, true, KVC, E>(p, stream);
+  else launch_group_nq<HD, false, KVC, E>(p, stream);
   return hipGetLastError();
 }
 
@@ -578,7 +496,7 @@ hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream) {
 template <typename E>
 static hipError_t launch_combine_e(const CombineParams& p, int headdim, hipStream_t stream) {
   const long rows = (long)p.batch * p.nheads * p.seqlen_q;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)rows);
   switch (headdim) {
     case 64: hipLaunchKernelGGL((combine_kernel<64, E>), grid, dim3(256), 0, stream, p); break;
     case 128: hipLaunchKernelGGL((combine_kernel<128, E>), grid, dim3(256), 0, stream, p); break;
