@@ -237,15 +237,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  // Causal mask or right window: later query tiles see more keys.  The query tile
-  // is then the slowest index, heaviest first over the whole grid (workgroup i
-  // serves (batch, head) i mod (batch * nheads)); otherwise tiles run fastest within
-  // the XCD-contiguous ranges of xcd_remap.
+  // Causal mask or right window: later query tiles see more keys.  Each XCD's
+  // range then runs in groups of up to four (batch, head) pairs, query tile slowest
+  // and heaviest first inside a group (as in the forward); otherwise tiles run
+  // fastest within the XCD-contiguous ranges of xcd_remap.
   int qt, b, h;
   if (p.window_right >= 0) {
-    const int bh_count = p.batch * p.nheads;
-    const int bh = blockIdx.x % bh_count;
-    qt = p.num_q_tiles - 1 - (int)blockIdx.x / bh_count;
+    const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_q_tiles, p.batch * p.nheads, qt);
+    qt = p.num_q_tiles - 1 - qt;
     b = bh % p.batch;
     h = bh / p.batch;
   } else {
@@ -391,12 +390,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int lrow = lane & 31, half = lane >> 5;
 
   // Causal mask or right window: earlier key tiles are seen by more queries; they
-  // run first over the whole grid, as in dq_kernel.
+  // run first within each group of (batch, head) pairs, as in dq_kernel.
   int kt_idx, b, h;
   if (p.window_right >= 0) {
-    const int bh_count = p.batch * p.nheads;
-    const int bh = blockIdx.x % bh_count;
-    kt_idx = (int)blockIdx.x / bh_count;
+    const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_k_tiles, p.batch * p.nheads, kt_idx);
     b = bh % p.batch;
     h = bh / p.batch;
   } else {

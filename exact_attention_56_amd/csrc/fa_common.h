@@ -133,4 +133,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Launches whose tiles differ in length (causal mask or right window): item w of an
+// XCD-contiguous order (w = xcd_remap(...)) over (pair, tile), pairs = batch * nheads.
+// Pairs form groups of up to four (at most one XCD's share, whose K/V then stays in
+// that XCD's L2 while the group runs); inside a group the tile index runs slowest, so
+// the heaviest tiles of every pair start first and short ones fill the end.  Returns
+// the pair; `rank` gets the tile's position in the group's order (0 first).
+__device__ __forceinline__ int heavy_first_item(int w, int ntiles, int pairs, int& rank) {
+  const int gsize = min(4, max(1, pairs / 8));
+  const int group = w / (gsize * ntiles);
+  const int r = w % (gsize * ntiles);
+  const int gp = min(gsize, pairs - group * gsize);  // pairs in this group (the last may be short)
+  rank = r / gp;
+  return group * gsize + r % gp;
+}
+
 }  // namespace fa

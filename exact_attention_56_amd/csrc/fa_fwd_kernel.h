@@ -485,15 +485,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   // every sequence of the batch: the XCDs then get equal work even when sequences
   // differ in length, and the query heads that share a K/V head stay on one XCD.
   // Padded batches with a causal mask or right window (tiles of unequal length)
-  // instead run the query tile slowest, heaviest first over the whole grid, so the
-  // short tiles fill the end of the launch; workgroup i then serves (batch, head)
-  // i mod (batch * nheads), which keeps each (batch, head) on one XCD whenever
-  // batch * nheads is a multiple of 8 (the dispatcher deals ids round-robin).
+  // take the heavy-first order of heavy_first_item instead: groups of up to four
+  // (batch, head) pairs, query tile slowest and heaviest first inside a group, so
+  // no heavy tile of the last heads starts late.
   int qt, split = 0, b, h;
   if (!SPLIT && p.reverse_q && p.cu_q == nullptr) {
-    const int bh_count = p.batch * p.nheads;
-    const int bh = item % bh_count;
-    qt = p.num_q_tiles - 1 - item / bh_count;
+    const int bh = heavy_first_item(xcd_remap(item, items), p.num_q_tiles, p.batch * p.nheads, qt);
+    qt = p.num_q_tiles - 1 - qt;
     b = bh % p.batch;
     h = bh / p.batch;
   } else {
