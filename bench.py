@@ -373,7 +373,8 @@ def main():
     for c in cases:
         ts = [a.elapsed_time(b) for cc, a, b in evs if cc is c]
         m = sum(ts) / len(ts)
-        per_case[c.w.name] = {"mean_ms": round(m, 4), "min_ms": round(min(ts), 4),
+        per_case[c.w.name] = {"mean_ms": round(m, 4), "median_ms": round(sorted(ts)[len(ts) // 2], 4),
+                              "min_ms": round(min(ts), 4),
                               "tflops": round(c.flops / (m * 1e-3) / 1e12, 1),
                               "algorithmic_gflop": round(c.flops / 1e9, 2),
                               "convention_gflop": round(convention_flops(c.w) / 1e9, 2)}
