@@ -401,7 +401,7 @@ def main():
                      "kernel": "fa::fwd_kernel<128,4,false,false,__bf16>", "per_launch": per_case},
     }
     if not args.no_extra:
-        result["extra"] = {"sweep_noncausal": sweep(dev, reps=10, warmup=3),
+        result["extra"] = {"sweep_noncausal": sweep(dev, reps=20, warmup=10),
                            "decode": decode_bench(dev, reps=20, warmup=3),
                            "varlen_gqa": varlen_bench(dev, reps=10, warmup=3),
                            "backward": backward_bench(dev, reps=10, warmup=5),
