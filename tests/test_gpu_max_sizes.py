@@ -1,0 +1,83 @@
+"""GPU parity at the size limits of the C ABI: tensors past 2^31 elements (64-bit
+offsets), the widest accepted row (nheads * headdim = 2^22) and a KV cache of 2^20
+keys, against the fp64 oracle.
+
+The first case is a causal launch with a left window of 255 keys over 2^19 rows of
+32 heads x 128: every query row sees only the 256 keys ending at its own position,
+so the last L rows of a head form the same attention problem as the sub-problem
+made of the last L rows of q and the last L + 256 rows of k and v (the bottom-right
+alignment puts each row at its own key again).  The oracle solves that sub-problem;
+the inputs are drawn on the GPU (the full tensors are 4 GiB each) and only the
+compared slices come back.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_56_amd as fa
+import oracle
+from exact_attention_56_amd.inputs import make_qkv
+from tests.parity import check_lse, check_out
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = "cuda"
+
+
+def announce(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def test_fwd_past_2_31_elements():
+    b, h, s, d, wl = 1, 32, 1 << 19, 128, 255
+    announce(f"max size: fwd b{b} h{h} s{s} d{d} causal window ({wl}, 0), {b * s * h * d} elements per tensor")
+    assert b * s * h * d >= 1 << 31
+    q, k, v = make_qkv(b, s, s, h, d, seed=21, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((b, h, s), float("nan"), dtype=torch.float32, device=DEV)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    fa.fwd(q, k, v, out, lse, scale, True, (wl, 0))
+    torch.cuda.synchronize()
+    tail = 1024
+    for hh in (0, 17, h - 1):
+        # the last `tail` query rows against the keys from wl + 1 before them on:
+        # the bottom-right alignment puts every row at its own key position again
+        qs = q[:, s - tail:, hh:hh + 1].contiguous().cpu()
+        ks, vs = (t[:, s - tail - (wl + 1):, hh:hh + 1].contiguous().cpu() for t in (k, v))
+        ref_out, ref_lse = oracle.attention_forward(qs, ks, vs, scale, True, wl, -1)
+        check_out(out[:, s - tail:, hh:hh + 1].cpu(), ref_out, f"out head {hh}")
+        check_lse(lse[:, hh:hh + 1, s - tail:].cpu(), ref_lse, f"lse head {hh}")
+    # the first rows too (offsets near 0 and the empty-left-window start)
+    qs, ks, vs = (t[:, :tail, 5:6].contiguous().cpu() for t in (q, k, v))
+    ref_out, ref_lse = oracle.attention_forward(qs, ks, vs, scale, True, wl, -1)
+    check_out(out[:, :tail, 5:6].cpu(), ref_out, "out head 5, first rows")
+    check_lse(lse[:, 5:6, :tail].cpu(), ref_lse, "lse head 5, first rows")
+
+
+def test_fwd_widest_row():
+    b, s, h, d = 1, 3, 16384, 256  # nheads * headdim = 2^22, the largest accepted
+    announce(f"max size: fwd b{b} s{s} h{h} d{d} (row of {h * d} elements)")
+    q, k, v = make_qkv(b, s, s, h, d, seed=22)
+    out = torch.full((b, s, h, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((b, h, s), float("nan"), dtype=torch.float32, device=DEV)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, scale, True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention_forward(q, k, v, scale, True)
+    check_out(out.cpu(), ref_out)
+    check_lse(lse.cpu(), ref_lse)
+
+
+def test_decode_cache_of_2_20_keys():
+    b, h, sk, d, ns = 2, 2, 1 << 20, 128, 64
+    announce(f"max size: decode b{b} h{h} seqlen_k {sk} d{d} splits {ns}")
+    q, k, v = make_qkv(b, 1, sk, h, d, seed=23)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    out, lse = fa.decode(q.to(DEV), k.to(DEV), v.to(DEV), ns, scale, True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention_forward(q, k, v, scale, True)
+    check_out(out.cpu(), ref_out)
+    check_lse(lse.cpu(), ref_lse)
