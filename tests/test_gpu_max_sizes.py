@@ -1,6 +1,6 @@
 """GPU parity at the size limits of the C ABI: tensors past 2^31 elements (64-bit
-offsets), the widest accepted row (nheads * headdim = 2^22) and a KV cache of 2^20
-keys, against the fp64 oracle.
+offsets; forward and backward), the widest accepted row (nheads * headdim = 2^22)
+and a KV cache of 2^20 keys, against the fp64 oracle.
 
 The first case is a causal launch with a left window of 255 keys over 2^19 rows of
 32 heads x 128: every query row sees only the 256 keys ending at its own position,
@@ -81,3 +81,28 @@ def test_decode_cache_of_2_20_keys():
     ref_out, ref_lse = oracle.attention_forward(q, k, v, scale, True)
     check_out(out.cpu(), ref_out)
     check_lse(lse.cpu(), ref_lse)
+
+
+def test_bwd_past_2_31_elements():
+    b, h, s, d, wl = 1, 32, 1 << 19, 128, 255
+    announce(f"max size: bwd b{b} h{h} s{s} d{d} causal window ({wl}, 0)")
+    q, k, v = make_qkv(b, s, s, h, d, seed=24, device=DEV)
+    dout = make_qkv(b, s, 1, h, d, seed=25, device=DEV)[0]
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    out, lse = fa.flash_attn_func(q, k, v, scale, True, (wl, 0))
+    dq, dk, dv = fa.attention_backward(q, k, v, out, lse, dout, scale, True, (wl, 0))
+    torch.cuda.synchronize()
+    del out, lse
+    tail = 768
+    for hh in (3, h - 1):
+        # the same sub-problem as the forward case; dq of its rows is exact, dk and dv
+        # only for the keys of the last `tail` rows (earlier keys also serve earlier queries)
+        qs, gs = (t[:, s - tail:, hh:hh + 1].contiguous().cpu() for t in (q, dout))
+        ks, vs = (t[:, s - tail - (wl + 1):, hh:hh + 1].contiguous().cpu() for t in (k, v))
+        rq, rk, rv = oracle.attention_backward(qs, ks, vs, gs, scale, True, wl, -1)
+        for name, got, ref in (("dq", dq[:, s - tail:, hh:hh + 1], rq), ("dk", dk[:, s - tail:, hh:hh + 1],
+                                                                        rk[:, wl + 1:]),
+                               ("dv", dv[:, s - tail:, hh:hh + 1], rv[:, wl + 1:])):
+            g = got.cpu().double().numpy()
+            err = float(np.abs(g - ref).max())
+            assert err <= 2e-2 * float(np.abs(ref).max()), f"{name} head {hh}: max err {err:.3e}"
