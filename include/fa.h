@@ -1,10 +1,11 @@
 /*
- * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library, libfa_mi355x.so.
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library, libfa_mi355x.so.
  *
  * The library computes exact scaled-dot-product attention,
  *     out = softmax(Q K^T * softmax_scale + mask + ALiBi bias) V,
  * tile by tile with an online softmax, so the seqlen_q x seqlen_k score matrix
- * never reaches device memory, and writes the row-wise logsumexp as well.
+ * never reaches device memory, and writes the row-wise logsumexp as well; the
+ * split-KV pair and the KV-cache entry serve decoding, and fa_bwd the gradients.
  * Sources (web pages, cited by title and section):
  *   [FA-overview] "FlashAttention：快速且内存高效的准确注意力机制"
  *                 (cloud.tencent.com.cn/developer/article/2433927)
