@@ -150,7 +150,20 @@ def cpu_baseline(cases, budget_s: float):
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_slices} (batch, head) slices of each of: "
                       + ", ".join(c.w.name for c in cases)
-                      + f" (full seqlen rows, fp64 NumPy), {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+                      + f" (full seqlen rows, fp64 NumPy), {dt:.1f} s; host has {os.cpu_count()} logical CPUs"
+                      + (f" ({cpu_model()})" if cpu_model() else "")}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or ''."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def sweep(dev, reps: int, warmup: int):
