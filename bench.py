@@ -14,6 +14,7 @@ Printed: ONE JSON line with the contract fields plus
                 (HIP events on the launch stream), against the bf16 MFMA peak;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the workload;
   extra         the seqlen sweep of the pages' recipe (non-causal, 4k/8k/16k), the
+                long causal local ALiBi workload and the headdim-256 16k workload, the
                 split-KV decode workload in HBM GB/s, a packed batch of causal
                 sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), the
                 backward (fa_bwd) on the benchmark shape, a paged-KV-cache decode
@@ -37,8 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import exact_attention_56_amd as fa  # noqa: E402
-from exact_attention_56_amd.inputs import (VARLEN_GQA, WORKLOADS, Workload, make_qkv,  # noqa: E402
-                                           make_varlen_qkv, sweep_workload)
+from exact_attention_56_amd.inputs import (VARLEN_GQA, WORKLOADS, Workload, make_alibi_slopes,  # noqa: E402
+                                           make_qkv, make_varlen_qkv, sweep_workload)
 
 METRIC = "attention fwd TFLOPS (bf16, 1 MI355X) at hd128 seqlen 2k-16k; % of MFMA peak"
 # MI355X published dense peaks: 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU, and HBM3E 8 TB/s.
@@ -183,6 +184,29 @@ def sweep(dev, reps: int, warmup: int):
     return res
 
 
+def configs_bench(dev, reps: int, warmup: int):
+    """The long causal local workload (headdim 64, window (1024, 0), ALiBi) and the
+    headdim-256 16k workload.  TFLOP/s on the algorithmic count (visible pairs only)
+    and, beside it, on the 4*B*H*Sq*Sk*d (halved when causal) convention."""
+    res = {}
+    for name in ("local_alibi_s8192", "hd256_s16384"):
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
+        slopes = make_alibi_slopes(w.nheads).to(dev) if w.alibi else None
+        case = FwdCase(w, q, k, v, slopes)
+        for _ in range(warmup):
+            case.launch()
+        mean_ms, min_ms = time_events(case.launch, reps)
+        tf = case.flops / (mean_ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "convention_tflops": round(convention_flops(w) / (mean_ms * 1e-3) / 1e12, 1),
+                     "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4),
+                     "algorithmic_gflop": round(case.flops / 1e9, 2),
+                     "shape": [w.batch, w.nheads, w.seqlen_q, w.seqlen_k, w.headdim]}
+        del q, k, v, case
+    return res
+
+
 def decode_bench(dev, reps: int, warmup: int):
     w = WORKLOADS["decode_s32768"]
     q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
@@ -320,6 +344,16 @@ def backward_bench(dev, reps: int, warmup: int):
     return res
 
 
+# extra workloads: name -> (function, timed repetitions, warm-up launches)
+EXTRAS = {"sweep_noncausal": (sweep, 20, 10),
+          "configs": (configs_bench, 10, 3),
+          "decode": (decode_bench, 20, 3),
+          "varlen_gqa": (varlen_bench, 10, 3),
+          "backward": (backward_bench, 10, 5),
+          "kvcache_paged": (kvcache_bench, 20, 5),
+          "fp16_fwd": (fp16_bench, 20, 10)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,10 +362,15 @@ def main():
                     help="untimed steps first (about 0.2 s: lets the GPU reach its steady clock)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the seqlen sweep and the decode workload")
+    ap.add_argument("--no-extra", action="store_true", help="skip every extra workload")
+    ap.add_argument("--extra", default=",".join(EXTRAS),
+                    help="comma-separated extra workloads to run (default: all of " + ", ".join(EXTRAS) + ")")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    unknown = [n for n in args.extra.split(",") if n not in EXTRAS]
+    if unknown:
+        ap.error(f"unknown extra workload(s) {unknown}; choose from {list(EXTRAS)}")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -414,12 +453,10 @@ def main():
                      "kernel": "fa::fwd_kernel<128,4,false,false,__bf16>", "per_launch": per_case},
     }
     if not args.no_extra:
-        result["extra"] = {"sweep_noncausal": sweep(dev, reps=20, warmup=10),
-                           "decode": decode_bench(dev, reps=20, warmup=3),
-                           "varlen_gqa": varlen_bench(dev, reps=10, warmup=3),
-                           "backward": backward_bench(dev, reps=10, warmup=5),
-                           "kvcache_paged": kvcache_bench(dev, reps=20, warmup=5),
-                           "fp16_fwd": fp16_bench(dev, reps=20, warmup=10)}
+        result["extra"] = {}
+        for name in args.extra.split(","):
+            fn, reps, warmup = EXTRAS[name]
+            result["extra"][name] = fn(dev, reps=reps, warmup=warmup)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

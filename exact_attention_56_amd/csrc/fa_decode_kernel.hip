@@ -283,35 +283,32 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_group_kernel(FwdParams p) 
   }
 }
 
-// Maximum / sum of x over the 256 threads of a workgroup (every thread gets it).
-__device__ __forceinline__ float block_max(float x, float* sm) {
+// Maximum / sum of x over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  __syncthreads();  // sm is free (a previous reduction has been read)
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  return x;
 }
-__device__ __forceinline__ float block_sum(float x, float* sm) {
+__device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return (sm[0] + sm[1]) + (sm[2] + sm[3]);
+  return x;
 }
 
-// One workgroup per output row.  The split weights exp(lse_s - L) come from two
-// block reductions (maximum, then sum) over the splits; the weighted sum of the
-// partial rows runs 256 / (HD/4) splits at a time, HD/4 threads per split with one
-// 16-byte load each, and the split groups are added through LDS at the end.
+// One workgroup per output row.  The reads of a row's partials are issued before
+// anything waits: each thread loads up to CPB partial chunks (16 bytes of one split's
+// row; HD/4 threads cover a row, 256/(HD/4) splits side by side), and every wave
+// reads the splits' lse values itself and reduces them (maximum, then the sum of
+// the weights exp(lse_s - max)) with lane exchanges, so the weights need no barrier.
+// The split groups are added through LDS at the end.  A split whose lse is -inf
+// (no visible key) gets weight 0 and its partial row is ignored, whatever it holds.
 template <int HD, typename E>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int TPS = HD / 4;     // threads per partial row (4 floats each)
-  constexpr int SPP = 256 / TPS;  // partial rows read per pass
-  __shared__ float sm_red[4];
+  constexpr int SPP = 256 / TPS;  // partial rows side by side
+  constexpr int CPB = 8;          // partial chunks in flight per thread
   __shared__ __attribute__((aligned(16))) float sm_acc[SPP][HD];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const long rows = (long)p.batch * p.nheads * p.seqlen_q;
   const long row = blockIdx.x;  // (b*H + h)*Sq + i
   const int i = (int)(row % p.seqlen_q);
@@ -322,23 +319,37 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const float* lp = p.lse_partial + row;
   const float* op = p.out_partial + row * HD;
   const long lstride = rows, ostride = rows * HD;
+  const int sg = tid / TPS, c = tid % TPS;
 
+  f32x4 v[CPB];
+#pragma unroll
+  for (int k = 0; k < CPB; ++k) {
+    const int s = sg + SPP * k;
+    v[k] = s < ns ? *(const f32x4*)(op + s * ostride + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float mx = -INFINITY;
-  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, lp[s * lstride]);
-  const float M = block_max(mx, sm_red);
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lp[s * lstride]);
+  const float M = wave_max(mx);
   const float M_use = (M == -INFINITY) ? 0.f : M;
   float sum = 0.f;
-  for (int s = tid; s < ns; s += 256) sum += fast_exp2((lp[s * lstride] - M_use) * kLog2e);  // 0: empty split
-  const float L = block_sum(sum, sm_red);
+  for (int s = lane; s < ns; s += 64) sum += fast_exp2((lp[s * lstride] - M_use) * kLog2e);  // 0: empty split
+  const float L = wave_sum(sum);
 
-  const int sg = tid / TPS, c = tid % TPS;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = sg; s < ns; s += SPP) {
-    const float wgt = fast_exp2((lp[s * lstride] - M_use) * kLog2e);
-    if (wgt != 0.f) {  // an empty split's partial row is never read
-      const f32x4 v = *(const f32x4*)(op + s * ostride + 4 * c);
-      acc += wgt * v;
+  for (int s0 = 0;; s0 += SPP * CPB) {
+#pragma unroll
+    for (int k = 0; k < CPB; ++k) {
+      const int s = s0 + sg + SPP * k;
+      if (s < ns) {
+        const float wgt = fast_exp2((lp[s * lstride] - M_use) * kLog2e);
+        if (wgt != 0.f) acc += wgt * v[k];
+      }
+    }
+    if (s0 + SPP * CPB >= ns) break;
+#pragma unroll
+    for (int k = 0; k < CPB; ++k) {
+      const int s = s0 + SPP * CPB + sg + SPP * k;
+      v[k] = s < ns ? *(const f32x4*)(op + s * ostride + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   *(f32x4*)&sm_acc[sg][4 * c] = acc;
