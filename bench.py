@@ -110,6 +110,21 @@ class FwdCase:
                (self.w.window_left, self.w.window_right), self.slopes)
 
 
+def warm_up(fn, launches: int, min_seconds: float = 0.15):
+    """Untimed launches of fn(): at least `launches`, and more until `min_seconds` of
+    wall time have passed.  Each extra workload draws fresh tensors; its first launches
+    over them ran up to 10% slow even with the GPU already warm, so every workload
+    gets about the same settling time whatever its launch length."""
+    for _ in range(launches):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(fn, reps: int):
     """Mean and min duration (ms) of fn() over reps, HIP events on the current stream."""
     stream = torch.cuda.current_stream()
@@ -173,8 +188,7 @@ def sweep(dev, reps: int, warmup: int):
         w = sweep_workload(s)
         q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
         case = FwdCase(w, q, k, v)
-        for _ in range(warmup):
-            case.launch()
+        warm_up(case.launch, warmup)
         mean_ms, min_ms = time_events(case.launch, reps)
         tf = case.flops / (mean_ms * 1e-3) / 1e12
         res[w.name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -194,8 +208,7 @@ def configs_bench(dev, reps: int, warmup: int):
         q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
         slopes = make_alibi_slopes(w.nheads).to(dev) if w.alibi else None
         case = FwdCase(w, q, k, v, slopes)
-        for _ in range(warmup):
-            case.launch()
+        warm_up(case.launch, warmup)
         mean_ms, min_ms = time_events(case.launch, reps)
         tf = case.flops / (mean_ms * 1e-3) / 1e12
         res[name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -223,8 +236,7 @@ def decode_bench(dev, reps: int, warmup: int):
         partial()
         fa.combine(op, lp, out, lse)
 
-    for _ in range(warmup):
-        both()
+    warm_up(both, warmup)
     p_mean, p_min = time_events(partial, reps)
     b_mean, _ = time_events(both, reps)
     kv_bytes = 2 * k.numel() * 2
@@ -249,8 +261,7 @@ def varlen_bench(dev, reps: int, warmup: int):
     def launch():
         fa.fwd_varlen(q, k, v, out, lse, cu, cu, mx, mx, w.softmax_scale, w.causal)
 
-    for _ in range(warmup):
-        launch()
+    warm_up(launch, warmup)
     mean_ms, min_ms = time_events(launch, reps)
     # causal square sequences: S (S + 1) / 2 visible pairs, 4 * headdim flop per pair and head
     flops = sum(s * (s + 1) // 2 for s in w.lengths) * w.nheads * 4 * w.headdim
@@ -271,8 +282,7 @@ def fp16_bench(dev, reps: int, warmup: int):
         q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev,
                            dtype=torch.float16)
         case = FwdCase(w, q, k, v)
-        for _ in range(warmup):
-            case.launch()
+        warm_up(case.launch, warmup)
         mean_ms, min_ms = time_events(case.launch, reps)
         tf = case.flops / (mean_ms * 1e-3) / 1e12
         res[name] = {"tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -305,8 +315,7 @@ def kvcache_bench(dev, reps: int, warmup: int):
     def launch():
         fa.fwd_kvcache(q, kc, vc, lens, out, lse, op, lp, table, knew, vnew, cos, sin, w.softmax_scale, True)
 
-    for _ in range(warmup):
-        launch()
+    warm_up(launch, warmup)
     mean_ms, min_ms = time_events(launch, reps)
     nbytes = 2 * b * w.seqlen_k * hk * d * 2 + q.numel() * 2 * 2 + 2 * knew.numel() * 2 + out.numel() * 2
     return {"workload": f"paged KV cache: batch {b}, {h} query heads over {hk} K/V heads x {d}, {cached} cached + 1 "
@@ -332,8 +341,7 @@ def backward_bench(dev, reps: int, warmup: int):
         def launch():
             fa.bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, w.softmax_scale, w.causal)
 
-        for _ in range(warmup):
-            launch()
+        warm_up(launch, warmup)
         mean_ms, min_ms = time_events(launch, reps)
         flops = 2.5 * algorithmic_flops(w)
         tf = flops / (mean_ms * 1e-3) / 1e12
