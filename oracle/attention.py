@@ -246,6 +246,50 @@ def attention_backward(q, k, v, dout, softmax_scale: float, causal: bool = False
     return dq, dk, dv
 
 
+def attention_backward_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, softmax_scale: float,
+                              causal: bool = False, window_left: int = -1, window_right: int = -1,
+                              alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Exact gradients for a packed batch of sequences with grouped K/V heads, fp64.
+
+    [FA-overview §算法 / 反向传播] on each sequence's own rows ([FA-overview
+    §代码解读：FlashSelfAttention, §代码解读博客：FlashCrossAttention]: sequence b is rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and dout and rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1 of k and v, with its own lengths for the masks).  Per sequence and
+    query head h the formulas of attention_backward apply with K/V head h // (H / H_k); the
+    forward reads that K/V head once for every query head of its group, so its dk and dv are
+    the sums over the group.
+    q, dout [total_q, H, D], k/v [total_k, H_k, D] -> dq, dk, dv with the shapes of q, k, v.
+    """
+    qd, kd, vd, gd = as_f64(q), as_f64(k), as_f64(v), as_f64(dout)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).reshape(-1)]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).reshape(-1)]
+    nheads = qd.shape[1]
+    group = nheads // kd.shape[1]
+    slopes = slope_table(alibi_slopes, len(cq) - 1, nheads)
+    dq, dk, dv = np.zeros(qd.shape), np.zeros(kd.shape), np.zeros(vd.shape)
+    for b in range(len(cq) - 1):
+        q0, sq = cq[b], cq[b + 1] - cq[b]
+        k0, sk = ck[b], ck[b + 1] - ck[b]
+        if sq == 0 or sk == 0:  # no (query, key) pair: every gradient of the sequence stays 0
+            continue
+        rows = np.arange(sq)
+        keep = visible_mask(sq, sk, causal, window_left, window_right, rows)
+        for h in range(nheads):
+            hk = h // group
+            qh, gh = qd[q0:q0 + sq, h], gd[q0:q0 + sq, h]
+            kh, vh = kd[k0:k0 + sk, hk], vd[k0:k0 + sk, hk]
+            scores = softmax_scale * (qh @ kh.T)
+            if slopes is not None:
+                scores = scores + alibi_bias(float(slopes[b, h]), sq, sk, rows)
+            p, _ = softmax_rows(scores, keep)
+            dp = gh @ vh.T
+            ds = p * (dp - np.sum(p * dp, axis=1)[:, None])
+            dq[q0:q0 + sq, h] = softmax_scale * (ds @ kh)
+            dk[k0:k0 + sk, hk] += softmax_scale * (ds.T @ qh)
+            dv[k0:k0 + sk, hk] += p.T @ gh
+    return dq, dk, dv
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (round to nearest, ties to even), returned as fp64:
     the precision of the cache and of the operands the kernels multiply."""

@@ -576,6 +576,10 @@ def test_backward_autograd():
     pin_backward_autograd()
 
 
+def test_backward_varlen_gqa():
+    pin_backward_varlen_gqa()
+
+
 def test_backward_closed_forms():
     pin_backward_closed_forms()
 
@@ -600,6 +604,85 @@ def test_bf16_widening():
     pin_bf16_widening()
 
 
+def _torch_varlen_gqa_grads(q, k, v, dout, cq, ck, scale, causal, wl, wr, slopes):
+    """Independent fp64 formulation: per sequence, each K/V head repeated for the query
+    heads of its group, visibility written as index comparisons on the bottom-right
+    aligned positions, softmax over the visible keys (rows without one give 0), and
+    torch autograd for the gradients of sum(dout * out)."""
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    gt = torch.tensor(dout)
+    group = q.shape[1] // k.shape[1]
+    total = torch.zeros((), dtype=torch.float64)
+    for b in range(len(cq) - 1):
+        qs, gs = qt[cq[b]:cq[b + 1]], gt[cq[b]:cq[b + 1]]
+        ks = kt[ck[b]:ck[b + 1]].repeat_interleave(group, dim=1)
+        vs = vt[ck[b]:ck[b + 1]].repeat_interleave(group, dim=1)
+        sq, sk = qs.shape[0], ks.shape[0]
+        if sq == 0 or sk == 0:
+            continue
+        pos = torch.arange(sq)[:, None] + (sk - sq)
+        key = torch.arange(sk)[None, :]
+        vis = torch.ones(sq, sk, dtype=torch.bool)
+        if wl >= 0:
+            vis &= key >= pos - wl
+        right = 0 if causal else wr
+        if right >= 0:
+            vis &= key <= pos + right
+        s = torch.einsum("ihd,jhd->hij", qs, ks) * scale
+        if slopes is not None:
+            sl = torch.tensor(np.asarray(slopes, dtype=np.float64))
+            sl = sl[b] if sl.dim() == 2 else sl
+            s = s - sl[:, None, None] * (pos - key).abs().to(torch.float64)
+        empty = ~vis.any(dim=1)
+        s = s.masked_fill(~vis, float("-inf")).masked_fill(empty[:, None], 0.0)
+        pr = torch.softmax(s, dim=-1) * vis
+        out = torch.einsum("hij,jhd->ihd", pr, vs)
+        total = total + (out * gs).sum()
+    total.backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_backward_varlen_gqa():
+    """Packed batch with grouped K/V heads (an empty query sequence, an empty key
+    sequence, Sq > Sk and Sq < Sk sequences): the oracle's gradients equal torch
+    autograd of an independent dense formulation, in every mask mode, with per-head
+    and per-sequence ALiBi slopes; one tiny case also against central differences of
+    the (separately pinned) packed forward."""
+    nheads, nheads_k, headdim = 4, 2, 3
+    lens_q, lens_k = [3, 0, 5, 2, 4], [5, 2, 3, 0, 4]
+    cq, ck = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    q, dout = rand((cq[-1], nheads, headdim), 62), rand((cq[-1], nheads, headdim), 63)
+    k, v = rand((ck[-1], nheads_k, headdim), 64), rand((ck[-1], nheads_k, headdim), 65)
+    per_head = np.array([0.3, 0.1, 0.0, 0.2])
+    per_seq = np.array([[0.3, 0.1, 0.2, 0.05]] * 5) * np.arange(1, 6)[:, None] / 3
+    for causal, wl, wr, al in [(False, -1, -1, None), (True, -1, -1, None), (True, 2, 0, per_head),
+                               (False, 1, 2, per_seq), (False, -1, -1, per_head)]:
+        got = oracle.attention_backward_varlen(q, k, v, dout, cq, ck, 0.8, causal, wl, wr, al)
+        ref = _torch_varlen_gqa_grads(q, k, v, dout, cq, ck, 0.8, causal, wl, wr, al)
+        for g, r in zip(got, ref):
+            assert g.shape == r.shape
+            assert np.allclose(g, r, atol=1e-12), float(np.abs(g - r).max())
+
+    eps = 1e-6
+    lq, lk = [2, 3], [3, 2]
+    cq2, ck2 = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q2, g2 = rand((5, 2, 2), 66), rand((5, 2, 2), 67)
+    k2, v2 = rand((5, 1, 2), 68), rand((5, 1, 2), 69)
+    grads = oracle.attention_backward_varlen(q2, k2, v2, g2, cq2, ck2, 0.7, True, -1, -1, per_head[:2])
+    loss = lambda: float(np.sum(oracle.attention_varlen(q2, k2, v2, cq2, ck2, 0.7, True, -1, -1, per_head[:2])[0]
+                                * g2))
+    for x, g in ((q2, grads[0]), (k2, grads[1]), (v2, grads[2])):
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            up = loss()
+            x[idx] = old - eps
+            dn = loss()
+            x[idx] = old
+            fd = (up - dn) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-7 * (1 + abs(fd)), (idx, fd, g[idx])
+
+
 # --------------------------------------------------------------------------- planted mistakes
 
 
@@ -619,6 +702,7 @@ def _all_pins():
     pin_varlen_gqa()
     pin_backward_autograd()
     pin_backward_closed_forms()
+    pin_backward_varlen_gqa()
     pin_kvcache()
     pin_kvcache("fp16")
     pin_round_fp16()
@@ -739,6 +823,39 @@ def _bwd_variant(drop_delta=False, unscaled_dk=False, dv_from_dp=False):
     return bwd
 
 
+def _bwd_varlen_variant(overwrite_kv=False, heads_modulo=False):
+    def bwd(q, k, v, dout, cu_q, cu_k, softmax_scale, causal=False, window_left=-1, window_right=-1,
+            alibi_slopes=None):
+        qd, kd, vd, gd = oa.as_f64(q), oa.as_f64(k), oa.as_f64(v), oa.as_f64(dout)
+        nheads, nk = qd.shape[1], kd.shape[1]
+        slopes = oa.slope_table(alibi_slopes, len(cu_q) - 1, nheads)
+        dq, dk, dv = np.zeros(qd.shape), np.zeros(kd.shape), np.zeros(vd.shape)
+        for b in range(len(cu_q) - 1):
+            q0, sq, k0, sk = cu_q[b], cu_q[b + 1] - cu_q[b], cu_k[b], cu_k[b + 1] - cu_k[b]
+            if sq == 0 or sk == 0:
+                continue
+            rows = np.arange(sq)
+            keep = oa.visible_mask(sq, sk, causal, window_left, window_right, rows)
+            for h in range(nheads):
+                hk = h % nk if heads_modulo else h // (nheads // nk)
+                qh, gh, kh, vh = qd[q0:q0 + sq, h], gd[q0:q0 + sq, h], kd[k0:k0 + sk, hk], vd[k0:k0 + sk, hk]
+                sc = softmax_scale * (qh @ kh.T)
+                if slopes is not None:
+                    sc = sc + oa.alibi_bias(float(slopes[b, h]), sq, sk, rows)
+                p, _ = oa.softmax_rows(sc, keep)
+                dp = gh @ vh.T
+                ds = p * (dp - np.sum(p * dp, axis=1)[:, None])
+                dq[q0:q0 + sq, h] = softmax_scale * (ds @ kh)
+                if overwrite_kv:
+                    dk[k0:k0 + sk, hk] = softmax_scale * (ds.T @ qh)
+                    dv[k0:k0 + sk, hk] = p.T @ gh
+                else:
+                    dk[k0:k0 + sk, hk] += softmax_scale * (ds.T @ qh)
+                    dv[k0:k0 + sk, hk] += p.T @ gh
+        return dq, dk, dv
+    return bwd
+
+
 def _rotary_wrong_sign(x, positions, cos, sin, rotary_dim):
     return _ORIG_ROTARY(x, positions, cos, -sin, rotary_dim)
 
@@ -784,6 +901,8 @@ _ORIG_SLOPES = oa.slope_table
     ("attention_backward", _bwd_variant(drop_delta=True)),
     ("attention_backward", _bwd_variant(unscaled_dk=True)),
     ("attention_backward", _bwd_variant(dv_from_dp=True)),
+    ("attention_backward_varlen", _bwd_varlen_variant(overwrite_kv=True)),
+    ("attention_backward_varlen", _bwd_varlen_variant(heads_modulo=True)),
     ("rotary", _rotary_wrong_sign),
     ("slope_table", _slopes_first_row),
     ("round_fp16", _round_fp16_via_bf16),
