@@ -67,6 +67,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_kvcache.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i,
+                                  i, vp, i, i, vp]
+    lib.fa_bwd_varlen.restype = i
     lib.fa_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.fa_combine.restype = i
     lib.fa_status_str.argtypes = [i]
@@ -284,6 +287,53 @@ def attention_backward(q, k, v, out, lse, dout, softmax_scale=None, causal=False
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device)
     bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, softmax_scale, causal, window_size, alibi_slopes)
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None) -> None:
+    """fa_bwd_varlen: gradients of fwd_varlen into preallocated dq [total_q,H,D] and dk/dv
+    [total_k,H_k,D] (q's dtype); delta [H,total_q] fp32 is scratch.  out and lse must be the
+    forward's outputs for the same arguments; the cumulative lengths are read by the kernels
+    only (see fa_bwd_varlen in include/fa.h)."""
+    _dtype_code(q, "q")
+    _require(q, "q", q.dtype, 3)
+    for t, name, like in ((k, "k", k), (v, "v", k), (out, "out", q), (dout, "dout", q), (dq, "dq", q),
+                          (dk, "dk", k), (dv, "dv", k)):
+        _require(t, name, q.dtype, 3, q.device)
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+    total_q, h, d = q.shape
+    total_k, hk = k.shape[0], k.shape[1]
+    if k.shape[2] != d:
+        raise ValueError(f"k and v must be [total_k, H_k, {d}]")
+    if hk < 1 or h % hk != 0:
+        raise ValueError(f"K/V heads ({hk}) must divide query heads ({h})")
+    _require(lse, "lse", torch.float32, 2, q.device)
+    _require(delta, "delta", torch.float32, 2, q.device)
+    if tuple(lse.shape) != (h, total_q) or tuple(delta.shape) != (h, total_q):
+        raise ValueError("lse and delta must be [nheads, total_q]")
+    _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
+    _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, q.device)
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [batch + 1]")
+    batch = cu_seqlens_q.shape[0] - 1
+    slopes, per_batch = _alibi(alibi_slopes, batch, h, q.device)
+    _check(load_library().fa_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch,
+        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, h, hk, d, _scale(softmax_scale, d),
+        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype],
+        _stream_handle(q)))
+
+
+def attention_varlen_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None):
+    """Gradients (dq, dk, dv) of flash_attn_varlen_func's out for the upstream gradient dout."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               softmax_scale, causal, window_size, alibi_slopes)
     return dq, dk, dv
 
 

@@ -217,10 +217,69 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
   p.q_sign = f.q_sign;
   p.window_left = f.window_left;
   p.window_right = f.window_right;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.lse_head_stride = 0;
+  p.nheads_k = nheads;
   p.num_q_tiles = (seqlen_q + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
   p.num_k_tiles = (seqlen_k + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
   const long rows = (long)batch * seqlen_q * nheads;
   if ((long)batch * nheads * p.num_q_tiles > kMaxBlocks || (long)batch * nheads * p.num_k_tiles > kMaxBlocks ||
+      rows / 16 + 1 > kMaxBlocks)
+    return FA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return fa::launch_bwd(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int nheads, int nheads_k,
+                  int headdim, float softmax_scale, int causal, int window_left, int window_right,
+                  const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
+  if (!out || !lse || !dout || !dq || !dk || !dv || !delta || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_INVALID_ARG;
+  if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1 || total_k < 1 || batch < 1)
+    return FA_ERR_INVALID_ARG;
+  // As in fa_fwd_varlen: one padded sequence of the maximal lengths is validated in
+  // place of the device-resident per-sequence lengths.
+  fa::FwdParams f;
+  const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
+                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
+  if (st != FA_OK) return st;
+  if (headdim != 64 && headdim != 128) return FA_ERR_UNSUPPORTED;
+  if (elems4(total_q, nheads, headdim, 1) < 0 || elems4(total_k, nheads_k, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
+  fa::BwdParams p;
+  p.q = f.q;
+  p.k = f.k;
+  p.v = f.v;
+  p.out = (const uint16_t*)out;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.alibi = alibi_slopes;
+  p.alibi_bstride = f.alibi_bstride;
+  p.f16 = f.f16;
+  p.batch = batch;
+  p.seqlen_q = max_seqlen_q;
+  p.seqlen_k = max_seqlen_k;
+  p.nheads = nheads;
+  p.nheads_k = nheads_k;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.lse_head_stride = total_q;
+  p.scale = softmax_scale;
+  p.scale_log2 = f.scale_log2;
+  p.q_and = f.q_and;
+  p.q_sign = f.q_sign;
+  p.window_left = f.window_left;
+  p.window_right = f.window_right;
+  p.num_q_tiles = (max_seqlen_q + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
+  p.num_k_tiles = (max_seqlen_k + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
+  const long rows = (long)total_q * nheads;
+  if ((long)batch * nheads * p.num_q_tiles > kMaxBlocks || (long)batch * nheads_k * p.num_k_tiles > kMaxBlocks ||
       rows / 16 + 1 > kMaxBlocks)
     return FA_ERR_INVALID_ARG;
   (void)hipGetLastError();

@@ -1,18 +1,25 @@
 // fa_bwd.hip - instantiates the delta and dK/dV passes of the backward (headdim 64
 // and 128, bf16 and fp16) and launches the three passes in order on one stream:
-// delta, dK/dV, dQ.
+// delta, dK/dV, dQ (padded or packed batches, grouped K/V heads).
 #include "fa_bwd_kernel.h"
 
 namespace fa {
 
 template <int HD, typename E>
 static hipError_t launch_bwd_hd(const BwdParams& p, hipStream_t stream) {
-  const long rows = (long)p.batch * p.seqlen_q * p.nheads;
+  // delta runs over rows of [rows, H, D]; a packed batch is one sequence of total_q rows
+  // for it (its [H, total_q] output is then the [1, H, total_q] layout)
+  BwdParams pd = p;
+  if (p.cu_q != nullptr) {
+    pd.batch = 1;
+    pd.seqlen_q = (int)p.lse_head_stride;
+  }
+  const long rows = (long)pd.batch * pd.seqlen_q * pd.nheads;
   constexpr int rows_per_block = 4 * (64 / (HD / 8));
   hipLaunchKernelGGL((delta_kernel<HD, E>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
-                     0, stream, p, rows);
+                     0, stream, pd, rows);
   const bool alibi = p.alibi != nullptr;
-  const int kv_items = p.batch * p.nheads * p.num_k_tiles;
+  const int kv_items = p.batch * p.nheads_k * p.num_k_tiles;
   if (alibi)
     hipLaunchKernelGGL((dkdv_kernel<HD, true, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
   else

@@ -37,15 +37,22 @@ namespace fa {
 // Backward problem description, filled on the host.  Sizes are in elements.
 struct BwdParams {
   const uint16_t* q;      // bf16/fp16 [B, Sq, H, D]
-  const uint16_t* k;      // bf16/fp16 [B, Sk, H, D]
-  const uint16_t* v;      // bf16/fp16 [B, Sk, H, D]
+  const uint16_t* k;      // bf16/fp16 [B, Sk, H_k, D]
+  const uint16_t* v;      // bf16/fp16 [B, Sk, H_k, D]
   const uint16_t* out;    // bf16/fp16 [B, Sq, H, D]  forward output
   const uint16_t* dout;   // bf16/fp16 [B, Sq, H, D]  upstream gradient
   const float* lse;       // fp32 [B, H, Sq]     forward logsumexp (natural log)
   float* delta;           // fp32 [B, H, Sq]     D, written by delta_kernel
   uint16_t* dq;           // bf16/fp16 [B, Sq, H, D]
-  uint16_t* dk;           // bf16/fp16 [B, Sk, H, D]
-  uint16_t* dv;           // bf16/fp16 [B, Sk, H, D]
+  uint16_t* dk;           // bf16/fp16 [B, Sk, H_k, D]
+  uint16_t* dv;           // bf16/fp16 [B, Sk, H_k, D]
+  // Packed batch (cu_q != nullptr): sequence b owns q/dout/dq rows [cu_q[b], cu_q[b+1])
+  // and k/v/dk/dv rows [cu_k[b], cu_k[b+1]) of [total, heads, D] tensors; lse and delta
+  // are [H, total_q] (lse_head_stride = total_q); seqlen_q/seqlen_k are the maxima.
+  const int* cu_q;
+  const int* cu_k;
+  long lse_head_stride;
+  int nheads_k;           // K/V heads; query head h uses K/V head h / (nheads / nheads_k)
   const float* alibi;     // fp32 [H] or [B, H], or nullptr
   int alibi_bstride;      // 0: one slope per head for every batch; nheads: [B, H]
   int f16;                // 1: every 16-bit tensor is fp16, 0: bf16
@@ -211,6 +218,31 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows) {
 #endif
 }
 
+// Rows of sequence b: the first q and k row and the lengths; padded batches use the
+// common lengths.  The first lse/delta element of (b, h) is lse_row(p, b, h, q_start, Sq).
+struct SeqRows {
+  long q_start, k_start;
+  int Sq, Sk;
+};
+__device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b) {
+  SeqRows r;
+  if (p.cu_q != nullptr) {
+    r.q_start = p.cu_q[b];
+    r.Sq = p.cu_q[b + 1] - (int)r.q_start;
+    r.k_start = p.cu_k[b];
+    r.Sk = p.cu_k[b + 1] - (int)r.k_start;
+  } else {
+    r.Sq = p.seqlen_q;
+    r.Sk = p.seqlen_k;
+    r.q_start = (long)b * r.Sq;
+    r.k_start = (long)b * r.Sk;
+  }
+  return r;
+}
+__device__ __forceinline__ long lse_row(const BwdParams& p, int b, int h, const SeqRows& r) {
+  return p.cu_q != nullptr ? (long)h * p.lse_head_stride + r.q_start : ((long)b * p.nheads + h) * r.Sq;
+}
+
 // Bias in log2 units of query i and key j (ALiBi), or 0.
 __device__ __forceinline__ float alibi_log2(float slope_log2, int pos_i, int key) {
   return -slope_log2 * fabsf((float)(pos_i - key));
@@ -255,10 +287,13 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
     h = w / p.batch;
   }
 
-  const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
+  const SeqRows sr = seq_rows(p, b);
+  const int Sq = sr.Sq, Sk = sr.Sk, off = Sk - Sq;
+  if (qt * BWD_ROWS >= Sq) return;  // the whole workgroup: a packed sequence shorter than the tile
   const int wl = p.window_left, wr = p.window_right;
-  const long rs = (long)p.nheads * HD;
-  const long qoff = (long)b * Sq * rs + (long)h * HD, koff = (long)b * Sk * rs + (long)h * HD;
+  const long rs = (long)p.nheads * HD, rsk = (long)p.nheads_k * HD;
+  const int hk = h / (p.nheads / p.nheads_k);
+  const long qoff = sr.q_start * rs + (long)h * HD, koff = sr.k_start * rsk + (long)hk * HD;
 
   const int i0 = qt * BWD_ROWS;
   const int i_last = min(i0 + BWD_ROWS, Sq) - 1;
@@ -281,7 +316,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   // L in log2 units (an empty row gets +inf, so that every P of it is 0) and D
   float lrow2 = INFINITY, drow = 0.f;
   if (my_q < Sq) {
-    const long li = ((long)b * p.nheads + h) * Sq + my_q;
+    const long li = lse_row(p, b, h, sr) + my_q;
     const float l = p.lse[li];
     lrow2 = l == -INFINITY ? INFINITY : l * kLog2e;
     drow = p.delta[li];
@@ -299,8 +334,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   st.bbase = p.v + koff;
   st.lo = 0;
   st.hi = Sk;
-  st.row_stride = (int)rs;
-  st.row_bytes = (int)rs * 2;
+  st.row_stride = (int)rsk;
+  st.row_bytes = (int)rsk * 2;
   st.init(wave, lane);
 
   if (t_begin < t_end) st.load(lds, lds + 2 * Stream::ABYTES, t_begin);
@@ -366,8 +401,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 }
 
 // ---------------------------------------------------------------------------------
-// dkdv_kernel: one workgroup per (batch, head, 128 keys); wave w owns keys
-// j0 + 32 w + 0..31.  Per 32-query tile t:
+// dkdv_kernel: one workgroup per (batch, K/V head, 128 keys); wave w owns keys
+// j0 + 32 w + 0..31.  For each query head that reads the K/V head, per query tile t:
 //   S = Q K^T, dP = dO V^T        (lane = key; Q, dO rows from LDS, K, V in registers)
 //   P = exp2(S c + bias - L'), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by transpose reads; P, dS as B operands)
@@ -389,26 +424,29 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  // Causal mask or right window: earlier key tiles are seen by more queries; they
-  // run first within each group of (batch, head) pairs, as in dq_kernel.
-  int kt_idx, b, h;
+  // Work items are (batch, K/V head, key tile).  Causal mask or right window: earlier
+  // key tiles are seen by more queries; they run first within each group of (batch,
+  // K/V head) pairs, as in dq_kernel.
+  int kt_idx, b, hk;
   if (p.window_right >= 0) {
-    const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_k_tiles, p.batch * p.nheads, kt_idx);
+    const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_k_tiles, p.batch * p.nheads_k, kt_idx);
     b = bh % p.batch;
-    h = bh / p.batch;
+    hk = bh / p.batch;
   } else {
     int w = xcd_remap(blockIdx.x, items);
     kt_idx = w % p.num_k_tiles;
     w /= p.num_k_tiles;
     b = w % p.batch;
-    h = w / p.batch;
+    hk = w / p.batch;
   }
 
-  const int Sq = p.seqlen_q, Sk = p.seqlen_k, off = Sk - Sq;
+  const SeqRows sr = seq_rows(p, b);
+  const int Sq = sr.Sq, Sk = sr.Sk, off = Sk - Sq;
+  if (kt_idx * BWD_ROWS >= Sk) return;  // the whole workgroup: a packed sequence shorter than the tile
   const int wl = p.window_left, wr = p.window_right;
-  const long rs = (long)p.nheads * HD;
-  const long qoff = (long)b * Sq * rs + (long)h * HD, koff = (long)b * Sk * rs + (long)h * HD;
-  const long loff = ((long)b * p.nheads + h) * Sq;
+  const long rs = (long)p.nheads * HD, rsk = (long)p.nheads_k * HD;
+  const long koff = sr.k_start * rsk + (long)hk * HD;
+  const int group = p.nheads / p.nheads_k;
 
   const int j0 = kt_idx * BWD_ROWS;
   const int j_last = min(j0 + BWD_ROWS, Sk) - 1;
@@ -424,12 +462,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   x8<E> kf[HD / 16], vf[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
-    kf[kk] = row_fragment<E>(p.k + koff, rs, my_k, Sk, kk, half, p.q_and, p.q_sign);
-    vf[kk] = row_fragment<E>(p.v + koff, rs, my_k, Sk, kk, half, 0xffffffffu, 0u);
+    kf[kk] = row_fragment<E>(p.k + koff, rsk, my_k, Sk, kk, half, p.q_and, p.q_sign);
+    vf[kk] = row_fragment<E>(p.v + koff, rsk, my_k, Sk, kk, half, 0xffffffffu, 0u);
   }
   const float c = p.scale_log2;
-  float slope2 = 0.f;
-  if constexpr (ALIBI) slope2 = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
   // visible queries of this key: c_i in [my_k - wr, my_k + wl]
   const int qlo = wr < 0 ? 0 : max(0, my_k - wr - off);
   const int qhi = wl < 0 ? Sq - 1 : min(Sq - 1, my_k + wl - off);
@@ -438,97 +474,107 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) dk[db] = dv[db] = f32x16{};
 
-  Stream st;
-  st.abase = p.q + qoff;
-  st.bbase = p.dout + qoff;
-  st.lo = 0;
-  st.hi = Sq;
-  st.row_stride = (int)rs;
-  st.row_bytes = (int)rs * 2;
-  st.init(wave, lane);
-  // L and D of a tile: wave 0 loads L, wave 1 loads D (4 bytes per lane, rows past
-  // the end read as zeros; L is scaled and -inf handled when read)
-  auto load_ld = [&](lds_u8* dst, int t) {
-    if (wave < 2) {
-      const int r0 = t * DKV_TILE;
-      const float* src = (wave == 0 ? p.lse : p.delta) + loff + r0;
-      const int n = max(0, min(DKV_TILE, Sq - r0)) * 4;
-      const auto rsr = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, dst + LDBYTES * wave, 4, 4 * lane, 0, 0, 0);
-    }
-  };
+  // The query heads that read this K/V head, one after another: dK and dV sum their
+  // contributions in the same accumulators.
+  for (int h = hk * group; h < (hk + 1) * group; ++h) {
+    const long qoff = sr.q_start * rs + (long)h * HD;
+    const long loff = lse_row(p, b, h, sr);
+    float slope2 = 0.f;
+    if constexpr (ALIBI) slope2 = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;
+    if (h != hk * group) __syncthreads();  // every wave is done with the previous head's tiles
 
-  if (t_begin < t_end) {
-    st.load(lds, lds + GOFF, t_begin);
-    load_ld(lds + LOFF, t_begin);
-  }
-  for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) & 1;
-    wait_tile_loads<0>();
-    __syncthreads();
-    if (t + 1 < t_end) {
-      lds_u8* nb = lds + (cur ^ 1) * BUF;
-      st.load(nb, nb + GOFF, t + 1);
-      load_ld(nb + LOFF, t + 1);
-    }
-    const lds_u8* qt = lds + cur * BUF;
-    const lds_u8* gt = qt + GOFF;
-    const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
+    Stream st;
+    st.abase = p.q + qoff;
+    st.bbase = p.dout + qoff;
+    st.lo = 0;
+    st.hi = Sq;
+    st.row_stride = (int)rs;
+    st.row_bytes = (int)rs * 2;
+    st.init(wave, lane);
+    // L and D of a tile: wave 0 loads L, wave 1 loads D (4 bytes per lane, rows past
+    // the end read as zeros; L is scaled and -inf handled when read)
+    auto load_ld = [&](lds_u8* dst, int t) {
+      if (wave < 2) {
+        const int r0 = t * DKV_TILE;
+        const float* src = (wave == 0 ? p.lse : p.delta) + loff + r0;
+        const int n = max(0, min(DKV_TILE, Sq - r0)) * 4;
+        const auto rsr = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, dst + LDBYTES * wave, 4, 4 * lane, 0, 0, 0);
+      }
+    };
 
-    f32x16 s[DKV_QB], dp[DKV_QB];
-#pragma unroll
-    for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk)
-#pragma unroll
-      for (int qb = 0; qb < DKV_QB; ++qb) {
-        s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
-        dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
+    if (t_begin < t_end) {
+      st.load(lds, lds + GOFF, t_begin);
+      load_ld(lds + LOFF, t_begin);
+    }
+    for (int t = t_begin; t < t_end; ++t) {
+      const int cur = (t - t_begin) & 1;
+      wait_tile_loads<0>();
+      __syncthreads();
+      if (t + 1 < t_end) {
+        lds_u8* nb = lds + (cur ^ 1) * BUF;
+        st.load(nb, nb + GOFF, t + 1);
+        load_ld(nb + LOFF, t + 1);
+      }
+      const lds_u8* qt = lds + cur * BUF;
+      const lds_u8* gt = qt + GOFF;
+      const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
+
+      f32x16 s[DKV_QB], dp[DKV_QB];
+  #pragma unroll
+      for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
+  #pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk)
+  #pragma unroll
+        for (int qb = 0; qb < DKV_QB; ++qb) {
+          s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
+          dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
+        }
+
+      // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
+      const int i0 = t * DKV_TILE;
+      // every (query of the tile, key of the block) pair visible, no query past the end
+      const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
+                        (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
+      x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
+  #pragma unroll
+      for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+        const int qb = cc >> 1, ci = cc & 1;
+        const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+        const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+        const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+        const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+        f32x16 pt, dt;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l = e < 4 ? l_a[e] : l_b[e - 4];
+          const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+          const int qi = i0 + qrow + e;
+          float x = fmaf(s[qb][8 * ci + e], c, -l * kLog2e);
+          if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+          float pv = (l == -INFINITY) ? 0.f : fast_exp2(x);
+          if (!full) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+          pt[e] = pv;
+          dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+        }
+        pf[cc] = pack_rows<E>(pt, 0);
+        dsf[cc] = pack_rows<E>(dt, 0);
       }
 
-    // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
-    const int i0 = t * DKV_TILE;
-    // every (query of the tile, key of the block) pair visible, no query past the end
-    const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
-                      (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
-    x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
-#pragma unroll
-    for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
-      const int qb = cc >> 1, ci = cc & 1;
-      const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
-      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-      const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
-      const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
-      const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
-      const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
-      f32x16 pt, dt;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float l = e < 4 ? l_a[e] : l_b[e - 4];
-        const float dd = e < 4 ? d_a[e] : d_b[e - 4];
-        const int qi = i0 + qrow + e;
-        float x = fmaf(s[qb][8 * ci + e], c, -l * kLog2e);
-        if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
-        float pv = (l == -INFINITY) ? 0.f : fast_exp2(x);
-        if (!full) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
-        pt[e] = pv;
-        dt[e] = pv * (dp[qb][8 * ci + e] - dd);
-      }
-      pf[cc] = pack_rows<E>(pt, 0);
-      dsf[cc] = pack_rows<E>(dt, 0);
+  #pragma unroll
+      for (int cc = 0; cc < 2 * DKV_QB; ++cc)
+  #pragma unroll
+        for (int db = 0; db < HD / 32; ++db) {
+          dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
+          dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
+        }
     }
-
-#pragma unroll
-    for (int cc = 0; cc < 2 * DKV_QB; ++cc)
-#pragma unroll
-      for (int db = 0; db < HD / 32; ++db) {
-        dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
-        dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
-      }
-  }
+  }  // query heads of the group
   if (my_k < Sk) {
-    store_rows<HD, E>(p.dk + koff, rs, my_k, dk, p.scale, half);
-    store_rows<HD, E>(p.dv + koff, rs, my_k, dv, 1.f, half);
+    store_rows<HD, E>(p.dk + koff, rsk, my_k, dk, p.scale, half);
+    store_rows<HD, E>(p.dv + koff, rsk, my_k, dv, 1.f, half);
   }
 #endif
 }

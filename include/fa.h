@@ -230,6 +230,33 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            float softmax_scale, int causal, int window_left, int window_right,
            const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
 
+/*
+ * fa_bwd_varlen - gradients of fa_fwd_varlen: the backward of fa_bwd over a packed
+ * batch of sequences with grouped K/V heads [FA-overview, "算法 / 反向传播",
+ * "并行性 / 反向传播"; the packed layout and the K/V head groups as for fa_fwd_varlen
+ * ("代码解读：FlashSelfAttention", "代码解读博客：FlashCrossAttention")].
+ *   q, out, dout, dq [total_q, nheads, headdim]   dtype (device; dq written)
+ *   k, v, dk, dv     [total_k, nheads_k, headdim] dtype (device; dk, dv written)
+ *   lse              [nheads, total_q] fp32 (device, read): fa_fwd_varlen's output
+ *   delta            [nheads, total_q] fp32 (device): caller-owned scratch, written with D
+ *   cu_seqlens_q/k, batch, max_seqlen_q/k, nheads_k and the mask arguments as for
+ *   fa_fwd_varlen (and the forward's values); total_k = cu_seqlens_k[batch].
+ * A K/V head's dk and dv sum the contributions of every query head of its group
+ * (the forward reads it once per query head); the sums are formed in one workgroup,
+ * in a fixed order, so results are bitwise reproducible.  Rows of a sequence past
+ * max_seqlen_q (or keys past max_seqlen_k) are left unwritten; the cu_seqlens arrays
+ * are read on the device only and must describe rows inside the tensors.  headdim
+ * must be 64 or 128.  Errors as for fa_bwd, plus FA_ERR_INVALID_ARG for a NULL
+ * cu_seqlens pointer, total_q < 1, total_k < 1, nheads_k < 1 or nheads_k not dividing
+ * nheads.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* delta,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int max_seqlen_q,
+                  int max_seqlen_k, int total_q, int total_k, int nheads, int nheads_k, int headdim,
+                  float softmax_scale, int causal, int window_left, int window_right,
+                  const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
+
 /* fa_status_str - static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

@@ -29,8 +29,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_combine", "fa_fwd", "fa_fwd_kvcache", "fa_fwd_splitkv",
-                                    "fa_fwd_varlen", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_varlen", "fa_combine", "fa_fwd", "fa_fwd_kvcache",
+                                    "fa_fwd_splitkv", "fa_fwd_varlen", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -134,6 +134,25 @@ def bwd_args(**over):
 ])
 def test_bwd_rejects_invalid(lib, over, code):
     assert lib.fa_bwd(*bwd_args(**over)) == code
+
+
+def bwd_varlen_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE,
+             cu_q=FAKE, cu_k=FAKE, batch=2, max_sq=8, max_sk=8, total_q=10, total_k=12, nheads=4, nheads_k=2,
+             headdim=128, scale=0.125, causal=0, wl=-1, wr=-1, alibi=None, per_batch=0, dtype=0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu_q=None), -1), (dict(cu_k=None), -1), (dict(q=None), -1), (dict(lse=None), -1), (dict(dk=None), -1),
+    (dict(delta=None), -1), (dict(nheads_k=0), -1), (dict(nheads_k=3), -1), (dict(nheads=2, nheads_k=4), -1),
+    (dict(total_q=0), -1), (dict(total_k=0), -1), (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(wl=-3), -1),
+    (dict(scale=math.inf), -1), (dict(headdim=256), -2), (dict(headdim=80), -2), (dict(dtype=2), -1),
+    (dict(per_batch=3), -1),
+])
+def test_bwd_varlen_rejects_invalid(lib, over, code):
+    assert lib.fa_bwd_varlen(*bwd_varlen_args(**over)) == code
 
 
 @pytest.mark.parametrize("args,code", [

@@ -1,0 +1,121 @@
+"""GPU parity of the packed-batch backward with grouped K/V heads (fa_bwd_varlen through
+the C ABI) against the exact fp64 gradient of the oracle.
+
+The GPU chain is the library's own: fa_fwd_varlen gives out and lse, fa_bwd_varlen the
+gradients.  Bound as for fa_bwd: for each of dq, dk, dv, max|err| <= 2e-2 * max|ref|
+(norm-wise relative), and rows the mask leaves out of every pair are exactly zero (rows
+with no visible key in dq, keys no query of their sequence sees in dk and dv).  A K/V head's
+gradient sums its whole query-head group.  Uniform lengths with one K/V head per query head
+must reproduce fa_bwd bit for bit (the same kernels and arithmetic).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_56_amd as fa
+import oracle
+from exact_attention_56_amd.inputs import make_alibi_slopes
+from tests.parity import to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GRAD_REL = 2e-2
+
+CASES = [
+    # lens_q, lens_k (None: the same), H, H_k, D, causal, wl, wr, alibi (None / "head" / "seq"), dtype
+    ((130, 0, 257, 64), None, 4, 2, 128, True, -1, -1, None, torch.bfloat16),
+    ((100, 300, 1), (333, 129, 70), 6, 3, 64, False, -1, -1, "head", torch.bfloat16),
+    ((257, 129), (129, 257), 2, 1, 128, True, -1, -1, "seq", torch.bfloat16),
+    ((200, 513), None, 2, 2, 128, True, 40, 0, "head", torch.bfloat16),
+    ((128, 300), None, 8, 2, 128, True, -1, -1, None, torch.float16),
+    ((50, 60), (0, 70), 4, 4, 64, False, 10, 10, None, torch.bfloat16),
+    ((64, 1, 191), None, 8, 2, 64, False, -1, -1, "seq", torch.float16),
+]
+
+
+def case_id(c):
+    lq, lk, h, hk, d, causal, wl, wr, al, dt = c
+    lk = lq if lk is None else lk
+    return (f"q{'-'.join(map(str, lq))}_k{'-'.join(map(str, lk))}_h{h}kv{hk}_d{d}{'_causal' if causal else ''}"
+            f"_w{wl},{wr}_alibi-{al}_{'fp16' if dt == torch.float16 else 'bf16'}")
+
+
+def visibility(lq, lk, causal, wl, wr):
+    """Per sequence: rows with no visible key and keys no row sees (the pages' mask)."""
+    empty_rows, unseen_keys = [], []
+    for sq, sk in zip(lq, lk):
+        keep = oracle.visible_mask(sq, sk, causal, wl, wr) if sq and sk else np.zeros((sq, sk), bool)
+        empty_rows.append(~keep.any(axis=1) if sk else np.ones(sq, bool))
+        unseen_keys.append(~keep.any(axis=0) if sq else np.ones(sk, bool))
+    return np.concatenate(empty_rows), np.concatenate(unseen_keys)
+
+
+def check_grad(got, ref, name, zero_rows):
+    g, r = to_np(got), np.asarray(ref, np.float64)
+    assert g.shape == r.shape, f"{name}: shape {g.shape} vs {r.shape}"
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values (unwritten or NaN)"
+    err, scale = float(np.abs(g - r).max()), float(np.abs(r).max())
+    if scale == 0.0:
+        assert err == 0.0, f"{name}: expected all zero, max |got| = {err:.3e}"
+    else:
+        assert err <= GRAD_REL * scale, f"{name}: max err {err:.3e} > {GRAD_REL} * max|ref| {scale:.3e}"
+    z = g[zero_rows]
+    assert np.all(z == 0.0), f"{name}: {(z != 0).sum()} elements of masked-out rows must be exactly 0"
+    return err / scale if scale else 0.0
+
+
+def draw(shape, g, dtype):
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[case_id(c) for c in CASES])
+def test_bwd_varlen_matches_oracle(case):
+    lq, lk, h, hk, d, causal, wl, wr, al, dt = case
+    lk = lq if lk is None else lk
+    print(f"[case] bwd_varlen {case_id(case)}", file=sys.stderr, flush=True)
+    g = torch.Generator().manual_seed(sum(lq) * 7 + sum(lk) + d)
+    tq, tk = sum(lq), sum(lk)
+    q, k, v = draw((tq, h, d), g, dt), draw((tk, hk, d), g, dt), draw((tk, hk, d), g, dt)
+    dout = draw((tq, h, d), g, dt)
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32)
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32)
+    slopes = None if al is None else make_alibi_slopes(h, len(lq) if al == "seq" else None)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    sd = None if slopes is None else slopes.to(DEV)
+    out, lse = fa.flash_attn_varlen_func(qd, kd, vd, cq.to(DEV), ck.to(DEV), max(lq), max(lk), scale, causal,
+                                         (wl, wr), sd)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+    delta = torch.full((h, tq), float("nan"), dtype=torch.float32, device=DEV)
+    fa.bwd_varlen(qd, kd, vd, out, lse, gd, dq, dk, dv, delta, cq.to(DEV), ck.to(DEV), max(lq), max(lk), scale,
+                  causal, (wl, wr), sd)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward_varlen(q, k, v, dout, cq.numpy(), ck.numpy(), scale, causal, wl, wr,
+                                                  slopes)
+    empty_rows, unseen_keys = visibility(lq, lk, causal, wl, wr)
+    rel = [check_grad(dq.cpu(), rq, "dq", empty_rows), check_grad(dk.cpu(), rk, "dk", unseen_keys),
+           check_grad(dv.cpu(), rv, "dv", unseen_keys)]
+    print(f"[case] relative errors dq {rel[0]:.2e} dk {rel[1]:.2e} dv {rel[2]:.2e}", file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_uniform_matches_padded(causal):
+    b, s, h, d = 3, 200, 2, 128
+    print(f"[case] bwd_varlen uniform vs padded causal={causal}", file=sys.stderr, flush=True)
+    g = torch.Generator().manual_seed(91 + causal)
+    q, k, v, dout = (draw((b, s, h, d), g, torch.bfloat16).to(DEV) for _ in range(4))
+    out, lse = fa.flash_attn_func(q, k, v, causal=causal)
+    ref = fa.attention_backward(q, k, v, out, lse, dout, causal=causal)
+    cu = torch.arange(0, (b + 1) * s, s, dtype=torch.int32, device=DEV)
+    flat = lambda t: t.reshape(b * s, h, d)
+    out_v, lse_v = fa.flash_attn_varlen_func(flat(q), flat(k), flat(v), cu, cu, s, s, causal=causal)
+    got = fa.attention_varlen_backward(flat(q), flat(k), flat(v), out_v, lse_v, flat(dout), cu, cu, s, s,
+                                       causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out_v.view(torch.int16), flat(out).view(torch.int16))
+    for a, r in zip(got, ref):
+        assert torch.equal(a.view(torch.int16), flat(r).view(torch.int16))
