@@ -17,7 +17,8 @@ Printed: ONE JSON line with the contract fields plus
                 long causal local ALiBi workload and the headdim-256 16k workload, the
                 split-KV decode workload in HBM GB/s, a packed batch of causal
                 sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), the
-                backward (fa_bwd) on the benchmark shape, a paged-KV-cache decode
+                backward (fa_bwd) on the benchmark shape and (fa_bwd_varlen) on the packed
+                grouped-head batch, a paged-KV-cache decode
                 step (fa_fwd_kvcache), and the benchmark shape with fp16 tensors.
 """
 
@@ -352,12 +353,38 @@ def backward_bench(dev, reps: int, warmup: int):
     return res
 
 
+def backward_varlen_bench(dev, reps: int, warmup: int):
+    """fa_bwd_varlen on the packed grouped-head workload (the causal sequences of
+    varlen_gqa, 32 query heads over 8 K/V heads x 128).  Algorithmic FLOPs: 10 * headdim
+    per visible pair and query head (2.5x the forward's)."""
+    w = VARLEN_GQA
+    q, k, v, cu = make_varlen_qkv(w, device=dev)
+    mx = max(w.lengths)
+    out, lse = fa.flash_attn_varlen_func(q, k, v, cu, cu, mx, mx, w.softmax_scale, w.causal)
+    dout = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(w.nheads, q.shape[0], dtype=torch.float32, device=dev)
+
+    def launch():
+        fa.bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, delta, cu, cu, mx, mx, w.softmax_scale, w.causal)
+
+    warm_up(launch, warmup)
+    mean_ms, min_ms = time_events(launch, reps)
+    flops = 2.5 * sum(s * (s + 1) // 2 for s in w.lengths) * w.nheads * 4 * w.headdim
+    tf = flops / (mean_ms * 1e-3) / 1e12
+    return {"workload": f"{w.name} backward: {len(w.lengths)} sequences ({sum(w.lengths)} tokens), {w.nheads} query "
+                        f"heads over {w.nheads_k} K/V heads x {w.headdim}, causal",
+            "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "mean_ms": round(mean_ms, 4), "min_ms": round(min_ms, 4), "algorithmic_gflop": round(flops / 1e9, 2)}
+
+
 # extra workloads: name -> (function, timed repetitions, warm-up launches)
 EXTRAS = {"sweep_noncausal": (sweep, 20, 10),
           "configs": (configs_bench, 10, 3),
           "decode": (decode_bench, 20, 3),
           "varlen_gqa": (varlen_bench, 10, 3),
           "backward": (backward_bench, 10, 5),
+          "backward_varlen_gqa": (backward_varlen_bench, 10, 3),
           "kvcache_paged": (kvcache_bench, 20, 5),
           "fp16_fwd": (fp16_bench, 20, 10)}
 
