@@ -269,12 +269,15 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  // Causal mask or right window: later query tiles see more keys.  Each XCD's
-  // range then runs in groups of up to four (batch, head) pairs, query tile slowest
-  // and heaviest first inside a group (as in the forward); otherwise tiles run
-  // fastest within the XCD-contiguous ranges of xcd_remap.
+  // Padded batch with a causal mask or right window: later query tiles see more keys.
+  // Each XCD's range then runs in groups of up to four (batch, head) pairs, query tile
+  // slowest and heaviest first inside a group (as in the forward).  Otherwise tiles run
+  // fastest within the XCD-contiguous ranges of xcd_remap, head slowest: on a packed
+  // batch each XCD then takes a slice of the heads over every sequence (equal work
+  // whatever the lengths; grouping sequences instead left the XCDs unequal and ran at
+  // 58% of this order's speed), heaviest tile of each sequence first under a mask.
   int qt, b, h;
-  if (p.window_right >= 0) {
+  if (p.window_right >= 0 && p.cu_q == nullptr) {
     const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_q_tiles, p.batch * p.nheads, qt);
     qt = p.num_q_tiles - 1 - qt;
     b = bh % p.batch;
@@ -285,6 +288,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
     w /= p.num_q_tiles;
     b = w % p.batch;
     h = w / p.batch;
+    if (p.window_right >= 0) qt = p.num_q_tiles - 1 - qt;  // packed: heaviest tile of a sequence first
   }
 
   const SeqRows sr = seq_rows(p, b);
@@ -424,11 +428,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  // Work items are (batch, K/V head, key tile).  Causal mask or right window: earlier
-  // key tiles are seen by more queries; they run first within each group of (batch,
-  // K/V head) pairs, as in dq_kernel.
+  // Work items are (batch, K/V head, key tile).  Padded batch with a causal mask or
+  // right window: earlier key tiles are seen by more queries; they run first within
+  // each group of (batch, K/V head) pairs, as in dq_kernel.  Otherwise (and for packed
+  // batches) key tile fastest, K/V head slowest, as in dq_kernel.
   int kt_idx, b, hk;
-  if (p.window_right >= 0) {
+  if (p.window_right >= 0 && p.cu_q == nullptr) {
     const int bh = heavy_first_item(xcd_remap(blockIdx.x, items), p.num_k_tiles, p.batch * p.nheads_k, kt_idx);
     b = bh % p.batch;
     hk = bh / p.batch;
