@@ -327,11 +327,11 @@ def kvcache_bench(dev, reps: int, warmup: int):
 
 
 def backward_bench(dev, reps: int, warmup: int):
-    """fa_bwd on the benchmark shape, non-causal and causal.  Algorithmic FLOPs: the five
-    products of the backward (S, dP, dV, dQ, dK) are 10 * headdim per visible pair, 2.5x
-    the forward's count."""
+    """fa_bwd on the benchmark shape, non-causal and causal, and on the headdim-256 16k
+    workload.  Algorithmic FLOPs: the five products of the backward (S, dP, dV, dQ, dK)
+    are 10 * headdim per visible pair, 2.5x the forward's count."""
     res = {}
-    for name in ("bench_s2048", "bench_s2048_causal"):
+    for name in ("bench_s2048", "bench_s2048_causal", "hd256_s16384"):
         w = WORKLOADS[name]
         q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed, device=dev)
         dout = torch.randn_like(q)

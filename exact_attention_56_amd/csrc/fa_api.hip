@@ -192,7 +192,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
                          window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
   if (st != FA_OK) return st;
-  if (headdim != 64 && headdim != 128) return FA_ERR_UNSUPPORTED;
+  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
   fa::BwdParams p;
   p.q = f.q;
   p.k = f.k;
@@ -246,7 +246,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
   const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
                          window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
   if (st != FA_OK) return st;
-  if (headdim != 64 && headdim != 128) return FA_ERR_UNSUPPORTED;
+  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
   if (elems4(total_q, nheads, headdim, 1) < 0 || elems4(total_k, nheads_k, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
   p.q = f.q;

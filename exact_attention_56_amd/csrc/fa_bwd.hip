@@ -1,5 +1,6 @@
-// fa_bwd.hip - instantiates the delta and dK/dV passes of the backward (headdim 64
-// and 128, bf16 and fp16) and launches the three passes in order on one stream:
+// fa_bwd.hip - instantiates the delta and dK/dV passes of the backward (headdim 64,
+// 128 and 256, bf16 and fp16; the dQ pass too at 256) and launches the three passes in
+// order on one stream:
 // delta, dK/dV, dQ (padded or packed batches, grouped K/V heads).
 #include "fa_bwd_kernel.h"
 
@@ -26,6 +27,7 @@ static hipError_t launch_bwd_hd(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((dkdv_kernel<HD, false, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (HD == 256) return launch_dq_hd<256, E>(p, stream);  // accumulators in AGPRs: compiled here
   return HD == 64 ? launch_dq_d64(p, stream) : launch_dq_d128(p, stream);
 }
 
@@ -34,6 +36,7 @@ static hipError_t launch_bwd_e(const BwdParams& p, int headdim, hipStream_t stre
   switch (headdim) {
     case 64: return launch_bwd_hd<64, E>(p, stream);
     case 128: return launch_bwd_hd<128, E>(p, stream);
+    case 256: return launch_bwd_hd<256, E>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -71,7 +71,8 @@ constexpr int BWD_ROWS = 128;    // rows (queries or keys) a workgroup owns: 32 
 constexpr int DQ_TILE = 64;      // keys per streamed tile (dq kernel)
 // Queries per streamed tile (dkdv kernel).  Headdim 128 takes 64 (two independent
 // 32-query blocks per wave: the kernel runs one wave per SIMD there, so it has the
-// registers); headdim 64 takes 32, which keeps it at two waves per SIMD.
+// registers); headdim 64 takes 32, which keeps it at two waves per SIMD; headdim 256
+// takes 32 (one wave per SIMD: K and V of 32 keys fill 128 registers, dK and dV 256).
 #ifndef FA_DKV_TILE128
 #define FA_DKV_TILE128 64
 #endif

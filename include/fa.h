@@ -221,7 +221,7 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
  * Rows with no visible key (lse = -inf) get dq = 0 and add nothing to dk, dv.  Keys no
  * query sees get dk = dv = 0.  Every output element is written exactly once (no
  * atomics): results are bitwise reproducible.  The ALiBi slopes are constants here
- * (no gradient).  headdim must be 64 or 128 (256: FA_ERR_UNSUPPORTED).  Errors as for
+ * (no gradient).  headdim 64, 128 or 256.  Errors as for
  * fa_fwd, plus FA_ERR_INVALID_ARG for a NULL out, lse, dout, dq, dk, dv or delta.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -246,7 +246,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
  * in a fixed order, so results are bitwise reproducible.  Rows of a sequence past
  * max_seqlen_q (or keys past max_seqlen_k) are left unwritten; the cu_seqlens arrays
  * are read on the device only and must describe rows inside the tensors.  headdim
- * must be 64 or 128.  Errors as for fa_bwd, plus FA_ERR_INVALID_ARG for a NULL
+ * 64, 128 or 256.  Errors as for fa_bwd, plus FA_ERR_INVALID_ARG for a NULL
  * cu_seqlens pointer, total_q < 1, total_k < 1, nheads_k < 1 or nheads_k not dividing
  * nheads.
  */

@@ -129,7 +129,7 @@ def bwd_args(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(out=None), -1), (dict(lse=None), -1), (dict(dout=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
     (dict(dv=None), -1), (dict(delta=None), -1), (dict(q=None), -1), (dict(batch=0), -1), (dict(seqlen_k=0), -1),
-    (dict(wl=-2), -1), (dict(scale=math.nan), -1), (dict(headdim=256), -2), (dict(headdim=96), -2),
+    (dict(wl=-2), -1), (dict(scale=math.nan), -1), (dict(headdim=32), -2), (dict(headdim=96), -2),
     (dict(dtype=2), -1), (dict(per_batch=4), -1),
 ])
 def test_bwd_rejects_invalid(lib, over, code):
@@ -148,7 +148,7 @@ def bwd_varlen_args(**over):
     (dict(cu_q=None), -1), (dict(cu_k=None), -1), (dict(q=None), -1), (dict(lse=None), -1), (dict(dk=None), -1),
     (dict(delta=None), -1), (dict(nheads_k=0), -1), (dict(nheads_k=3), -1), (dict(nheads=2, nheads_k=4), -1),
     (dict(total_q=0), -1), (dict(total_k=0), -1), (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(wl=-3), -1),
-    (dict(scale=math.inf), -1), (dict(headdim=256), -2), (dict(headdim=80), -2), (dict(dtype=2), -1),
+    (dict(scale=math.inf), -1), (dict(headdim=512), -2), (dict(headdim=80), -2), (dict(dtype=2), -1),
     (dict(per_batch=3), -1),
 ])
 def test_bwd_varlen_rejects_invalid(lib, over, code):

@@ -38,6 +38,10 @@ BWD_CASES = [
     (1, 2, 160, 160, 128, True, -1, -1, False, 0.0),
     (1, 2, 513, 515, 128, False, -1, -1, False, None),
     (1, 1, 1, 70, 128, True, -1, -1, False, None),
+    (1, 2, 200, 300, 256, False, -1, -1, False, None),
+    (1, 2, 257, 129, 256, True, -1, -1, True, None),
+    (2, 1, 130, 130, 256, True, 30, 0, False, None),
+    (1, 1, 1024, 1024, 256, False, -1, -1, False, None),
 ]
 
 

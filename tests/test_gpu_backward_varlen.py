@@ -34,6 +34,8 @@ CASES = [
     ((128, 300), None, 8, 2, 128, True, -1, -1, None, torch.float16),
     ((50, 60), (0, 70), 4, 4, 64, False, 10, 10, None, torch.bfloat16),
     ((64, 1, 191), None, 8, 2, 64, False, -1, -1, "seq", torch.float16),
+    ((100, 257), None, 4, 2, 256, True, -1, -1, "head", torch.bfloat16),
+    ((65, 300), (129, 200), 2, 1, 256, False, -1, -1, None, torch.float16),
 ]
 
 
