@@ -187,7 +187,8 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
  *       (device, written; out also holds the rotated queries between the two passes).
  *   out_partial, lse_partial: caller-owned scratch of at least max_splits splits in the
  *       fa_fwd_splitkv layout.  num_splits = 0 picks the split count (about 2048
- *       workgroups, at least 256 keys per split), else 1..max_splits.
+ *       workgroups when a workgroup serves one or two queries of a K/V head, about 512
+ *       when it serves four or eight; at least 256 keys per split), else 1..max_splits.
  * Sequence b attends to its cache_seqlens[b] + seqlen_new keys; the causal/window
  * alignment is bottom-right within them.  Query head h reads K/V head
  * h / (nheads / nheads_k).  Device-side values (cache_seqlens, block_table, rotary
