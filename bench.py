@@ -18,8 +18,8 @@ Printed: ONE JSON line with the contract fields plus
                 split-KV decode workload in HBM GB/s, a packed batch of causal
                 sequences of mixed lengths with grouped K/V heads (fa_fwd_varlen), the
                 backward (fa_bwd) on the benchmark shape and (fa_bwd_varlen) on the packed
-                grouped-head batch, a paged-KV-cache decode
-                step (fa_fwd_kvcache), and the benchmark shape with fp16 tensors.
+                grouped-head batch, paged-KV-cache decode steps (fa_fwd_kvcache; 4 and
+                1 K/V heads), and the benchmark shape with fp16 tensors.
 """
 
 from __future__ import annotations
@@ -291,13 +291,13 @@ def fp16_bench(dev, reps: int, warmup: int):
     return res
 
 
-def kvcache_bench(dev, reps: int, warmup: int):
+def kvcache_bench(dev, reps: int, warmup: int, hk: int = 4):
     """fa_fwd_kvcache on the decode workload's sizes with a paged cache: batch 8, 16 query
-    heads over 4 K/V heads x 128, 32767 cached keys + 1 appended (rotary on q and the new
-    key), 256-row blocks in shuffled order, automatic split count.  HBM bytes: the K/V rows
-    read plus q, the appended row, partials and outputs."""
+    heads over 4 K/V heads x 128 (hk), 32767 cached keys + 1 appended (rotary on q and the
+    new key), 256-row blocks in shuffled order, automatic split count.  HBM bytes: the K/V
+    rows read plus q, the appended row, partials and outputs."""
     w = WORKLOADS["decode_s32768"]
-    b, h, hk, d, page = w.batch, w.nheads, 4, w.headdim, 256
+    b, h, d, page = w.batch, w.nheads, w.headdim, 256
     cached = w.seqlen_k - 1
     blocks = w.seqlen_k // page
     g = torch.Generator(device=dev).manual_seed(9)
@@ -386,6 +386,7 @@ EXTRAS = {"sweep_noncausal": (sweep, 20, 10),
           "backward": (backward_bench, 10, 5),
           "backward_varlen_gqa": (backward_varlen_bench, 10, 3),
           "kvcache_paged": (kvcache_bench, 20, 5),
+          "kvcache_paged_mqa": (lambda dev, reps, warmup: kvcache_bench(dev, reps, warmup, hk=1), 20, 5),
           "fp16_fwd": (fp16_bench, 20, 10)}
 
 

@@ -325,9 +325,9 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
   int ns = num_splits;
   if (ns == 0) {
     const int nq = nheads / nheads_k * seqlen_q;
-    const int per_block = fa::decode_queries_per_block(nq);
+    const int per_block = fa::decode_uses_mfma(headdim, nq) ? 128 : fa::decode_queries_per_block(nq);
     const long rows = (long)batch * nheads_k * ((nq + per_block - 1) / per_block);
-    const long target = per_block >= 4 ? 512 : 2048;
+    const long target = nq >= 3 ? 512 : 2048;
     ns = (int)std::min<long>(max_splits, std::max<long>(1, (target + rows - 1) / rows));
     ns = (int)std::min<long long>(ns, std::max<long long>(1, capacity / 256));
   }

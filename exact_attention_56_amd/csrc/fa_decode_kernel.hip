@@ -17,7 +17,7 @@
 //
 // Combine kernel: out = sum_s exp(lse_s - L) out_s with L = ln sum_s exp(lse_s), one
 // workgroup per row.
-#include "fa_common.h"
+#include "fa_fwd_kernel.h"  // decode_uses_mfma, launch_fwd_decode_d64/d128 (compiled with their own flags)
 
 namespace fa {
 
@@ -462,6 +462,14 @@ static hipError_t launch_kvcache_hd(const FwdParams& p, const uint16_t* k_new, c
   if (e != hipSuccess) return e;
   FwdParams d = p;
   if (cos != nullptr) d.q = qrot;  // the decode kernel reads the rotated queries
+  if constexpr (HD != 256) {
+    // more than four queries per K/V head: every K/V tile feeds matrix-core products for
+    // all of them (the vector-ALU kernel's work per key grows with their number)
+    if (decode_uses_mfma(HD, p.nheads / p.nheads_k * p.seqlen_q)) {
+      d.split_len = (p.split_len + BC - 1) / BC * BC;
+      return HD == 64 ? launch_fwd_decode_d64(d, stream) : launch_fwd_decode_d128(d, stream);
+    }
+  }
   return launch_decode_kvc<HD, true, E>(d, stream);
 }
 

@@ -43,6 +43,8 @@
 //    LDS as zeros without branches; only tiles crossing a mask boundary run the
 //    per-element visibility test.
 #pragma once
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -152,6 +154,40 @@ struct KVStream {
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)voff[i], 0, 0, 0);
+  }
+};
+
+// KV-cache decode: the same stream over a cache whose rows are reached through a block
+// table (btab == nullptr: a contiguous cache, rows in order).  Key j of the sequence is
+// row (btab[j >> page_shift] << page_shift) + (j & (page_size - 1)); tiles start on
+// multiples of BC <= page_size, so a tile never crosses a block.
+template <int HD, int NW>
+struct PagedKVStream : KVStream<HD, NW> {
+  using T = Tile<HD, NW>;
+  const int* btab;
+  int page_shift;
+  bool active;  // wave-uniform: this wave holds at least one existing row
+
+  __device__ __forceinline__ long tile_row(int j0) const {
+    if (btab == nullptr) return j0;
+    // past the last key nothing is read: any block will do (and the table may end there)
+    return j0 < this->key_hi ? ((long)btab[j0 >> page_shift] << page_shift) + (j0 & ((1 << page_shift) - 1)) : 0;
+  }
+  __device__ __forceinline__ void load_k(lds_u8* dst, int t) const {
+    if (!this->loads_k) return;
+    const int j0 = this->key_lo + t * BC;
+    const auto rs = tile_rsrc(this->kbase + tile_row(j0) * this->row_stride, this->key_hi - j0, this->row_bytes);
+#pragma unroll
+    for (int i = 0; i < T::KPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->koff[i], 0, 0, 0);
+  }
+  __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
+    if (!this->loads_v) return;
+    const int j0 = this->key_lo + t * BC;
+    const auto rs = tile_rsrc(this->vbase + tile_row(j0) * this->row_stride, this->key_hi - j0, this->row_bytes);
+#pragma unroll
+    for (int i = 0; i < T::VPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->voff[i], 0, 0, 0);
   }
 };
 
@@ -321,9 +357,9 @@ struct LdsBufs {
 // One tile step: P(t) from s_cur, S(t+1) into s_nxt, O += V(t) P(t), loads of
 // K(t+2) and V(t+1) into the free buffers, reference-maximum update.  Ends with
 // the tile barrier.
-template <int HD, int NW, bool ALIBI, typename E>
+template <int HD, int NW, bool ALIBI, typename E, typename KV>
 __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
-                                          int t_begin, const KVStream<HD, NW>& kv, const LdsBufs& lb, int half,
+                                          int t_begin, const KV& kv, const LdsBufs& lb, int half,
                                           float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
                                           int i_last, int off) {
   using T = Tile<HD, NW>;
@@ -335,6 +371,14 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   const int b0 = rel % NB, b1 = (rel + 1) % NB, bm1 = (rel + NB - 1) % NB;
   kv.load_k(lb.k[b0], t + NB);
   kv.load_v(lb.v[bm1], t + NB - 1);
+  if constexpr (!std::is_same_v<KV, KVStream<HD, NW>>) {
+    // decode form: a wave none of whose rows exists only streams tiles for the others
+    if (!kv.active) {
+      wait_tile_loads<NB == 2 ? 0 : T::LOADS_PER_STEP>();
+      __syncthreads();
+      return;
+    }
+  }
 
   // S(t+1) = K(t+1) Q^T
   qk_tile<HD, E>(s_nxt, lb.kl[b1], st.qf);
@@ -469,8 +513,13 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
 }
 
 // One work item: (batch, head, query tile[, key split]) number `item` of `items`.
-template <int HD, int NW, bool ALIBI, bool SPLIT, typename E>
+// DEC (KV-cache decode, split mode only): the block's rows are the Sq * G queries that
+// share K/V head h (G = nheads / nheads_k query heads, row r = query i * G + head g),
+// read from a KV cache (Sk = cache_seqlens[b] + seqlen_new keys, paged through the block
+// table or contiguous); every K/V tile loaded then serves all of them.
+template <int HD, int NW, bool ALIBI, bool SPLIT, typename E, bool DEC = false>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int item, int items) {
+  static_assert(!DEC || SPLIT, "the decode form writes split partials");
   using T = Tile<HD, NW>;
   constexpr int BR = 32 * NW;  // query rows per workgroup
   const int tid = threadIdx.x;
@@ -511,7 +560,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   // batch lists each sequence's first row in cu_q / cu_k.
   long q_start, k_start;
   int Sq, Sk;
-  if (p.cu_q != nullptr) {
+  if (DEC) {
+    Sq = p.seqlen_q;
+    Sk = p.cache_seqlens[b] + p.seqlen_new;
+    q_start = (long)b * Sq;
+    k_start = p.block_table != nullptr ? 0 : (long)b * p.page_size;  // contiguous: page_size = capacity
+  } else if (p.cu_q != nullptr) {
     q_start = p.cu_q[b];
     Sq = p.cu_q[b + 1] - q_start;
     k_start = p.cu_k[b];
@@ -530,16 +584,22 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   }
   const long row_stride = (long)p.nheads * HD;     // q and out
   const long kv_stride = (long)p.nheads_k * HD;    // k and v
-  const int hk = h / (p.nheads / p.nheads_k);
+  const int G = p.nheads / p.nheads_k;
+  const int hk = DEC ? h : h / G;                  // the decode form's items are K/V heads
   const uint16_t* __restrict__ qbase = p.q + q_start * row_stride + (long)h * HD;
 
-  KVStream<HD, NW> kv;
+  std::conditional_t<DEC, PagedKVStream<HD, NW>, KVStream<HD, NW>> kv;
   kv.kbase = p.k + k_start * kv_stride + (long)hk * HD;
   kv.vbase = p.v + k_start * kv_stride + (long)hk * HD;
   kv.key_lo = key_lo;
   kv.key_hi = key_hi;
   kv.row_stride = (int)kv_stride;
   kv.row_bytes = (int)kv_stride * 2;
+  if constexpr (DEC) {
+    kv.btab = p.block_table != nullptr ? p.block_table + (long)b * p.max_blocks : nullptr;
+    kv.page_shift = p.page_shift;
+    kv.active = qt * BR + wave * 32 < Sq * G;
+  }
   kv.init(wave, lane);
 
   LdsBufs lb;
@@ -552,8 +612,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     lb.vl[i] = lb.v[i] + vt_lane_offset<HD>(lane);
   }
 
-  const int i0 = qt * BR;
-  const int i_last = min(i0 + BR, Sq) - 1;
+  // Positions (query index i) of the block's first and last row; the decode form's
+  // rows r = i * G + g of rows_total = Sq * G hold G heads per position.
+  const int rows_total = DEC ? Sq * G : Sq;
+  const int r0 = qt * BR;
+  const int i0 = DEC ? r0 / G : r0;
+  const int i_last = DEC ? (min(r0 + BR, rows_total) - 1) / G : min(r0 + BR, Sq) - 1;
   const int off = Sk - Sq;  // query i sits at key position i + off
   const int wl = p.window_left, wr = p.window_right;
 
@@ -569,12 +633,17 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 
   // ---- Q fragments: B operand of S^T = K Q^T, held for the whole loop ----------
   FwdState<HD, E> st;
-  const int my_q = i0 + wave * 32 + lrow;
+  const int my_r = r0 + wave * 32 + lrow;         // this lane's row of the block
+  const int my_q = DEC ? my_r / G : my_r;         // its query index
+  const int my_h = DEC ? hk * G + my_r % G : h;   // and its query head
+  const bool my_valid = my_r < rows_total;
   const int my_pos = my_q + off;
+  const uint16_t* __restrict__ my_qrow =
+      DEC ? p.q + (((long)b * Sq + my_q) * p.nheads + my_h) * HD : qbase + (long)my_q * row_stride;
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_q < Sq) raw = *(const u32x4*)(qbase + (long)my_q * row_stride + 16 * kk + 8 * half);
+    if (my_valid) raw = *(const u32x4*)(my_qrow + 16 * kk + 8 * half);
     raw = (raw & p.q_and) ^ p.q_sign;
     st.qf[kk] = __builtin_bit_cast(x8<E>, raw);
   }
@@ -585,7 +654,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   st.b_cur = 0.f;
   const float c = p.scale_log2;
   float slope = 0.f;
-  if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + h] * kLog2e;  // bias in log2 units
+  if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + my_h] * kLog2e;  // bias in log2 units
   // multiplier turning the stored scores into log2 units
   const float cs = ALIBI ? 1.f : c;
 
@@ -621,7 +690,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const float l_tot = sum_with_other_half(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
-  if (my_q >= Sq) return;  // this lane's row is past the end: nothing to write
+  if (!my_valid) return;  // this lane's row is past the end: nothing to write
 
   if constexpr (!SPLIT) {
     uint16_t* obase = (uint16_t*)p.out + (q_start + my_q) * row_stride + (long)h * HD;
@@ -641,7 +710,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
       p.lse[li] = lse_v;
     }
   } else {
-    const long rowid = (((long)split * p.batch + b) * p.nheads + h) * Sq + my_q;
+    const long rowid = (((long)split * p.batch + b) * p.nheads + my_h) * Sq + my_q;
     float* obase = (float*)p.out + rowid * HD;
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db)
@@ -663,6 +732,16 @@ template <int HD, int NW, bool ALIBI, bool SPLIT, typename E>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p, int items) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD, NW>::LDS_BYTES];
   fwd_item<HD, NW, ALIBI, SPLIT, E>(p, smem, blockIdx.x, items);
+}
+
+// KV-cache decode with grouped K/V heads on the matrix cores: one workgroup per (batch,
+// K/V head, key split, block of 128 rows of the Sq * G queries that share the K/V head),
+// split partials as fa_fwd_splitkv writes them.
+template <int HD, bool ALIBI, typename E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_decode_kernel(FwdParams p,
+                                                                                                int items) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD, 4>::LDS_BYTES];
+  fwd_item<HD, 4, ALIBI, true, E, true>(p, smem, blockIdx.x, items);
 }
 
 template <int HD, int NW, bool ALIBI, bool SPLIT>
@@ -707,5 +786,33 @@ hipError_t launch_fwd_hd(const FwdParams& p, bool split, hipStream_t stream) {
 hipError_t launch_fwd_d64(const FwdParams& p, bool split, hipStream_t stream);
 hipError_t launch_fwd_d128(const FwdParams& p, bool split, hipStream_t stream);
 hipError_t launch_fwd_d256(const FwdParams& p, bool split, hipStream_t stream);
+
+// The matrix-core decode form (fwd_decode_kernel) for a KV-cache step whose K/V heads
+// each serve nq_total = (nheads / nheads_k) * seqlen_q > 4 queries, headdim 64 or 128.
+// Up to four queries the vector-ALU kernel streams the cache faster (paged 32k-key
+// caches, batch 8: 5.45 against 4.65 TB/s at four queries per K/V head); from eight on
+// it falls behind (3.0 against 4.8 TB/s at eight, 1.5 against 3.6 at sixteen).  The
+// caller passes split_len as a multiple of BC (so a tile never crosses a cache block)
+// and the split partials as out / lse.
+inline bool decode_uses_mfma(int headdim, int nq_total) { return headdim != 256 && nq_total > 4; }
+
+template <int HD>
+hipError_t launch_fwd_decode_hd(const FwdParams& p, hipStream_t stream) {
+  FwdParams d = p;
+  d.reverse_q = 0;
+  d.num_q_tiles = ((p.nheads / p.nheads_k) * p.seqlen_q + 127) / 128;
+  const long nblocks = (long)d.batch * d.nheads_k * d.num_splits * d.num_q_tiles;
+  const dim3 grid((unsigned)nblocks);
+  if (p.f16) {
+    if (p.alibi) hipLaunchKernelGGL((fwd_decode_kernel<HD, true, _Float16>), grid, dim3(256), 0, stream, d, (int)nblocks);
+    else hipLaunchKernelGGL((fwd_decode_kernel<HD, false, _Float16>), grid, dim3(256), 0, stream, d, (int)nblocks);
+  } else {
+    if (p.alibi) hipLaunchKernelGGL((fwd_decode_kernel<HD, true, __bf16>), grid, dim3(256), 0, stream, d, (int)nblocks);
+    else hipLaunchKernelGGL((fwd_decode_kernel<HD, false, __bf16>), grid, dim3(256), 0, stream, d, (int)nblocks);
+  }
+  return hipGetLastError();
+}
+hipError_t launch_fwd_decode_d64(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_decode_d128(const FwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -33,6 +33,9 @@ KVC_CASES = [
     (1, 8, 2, 2, 64, None, 1000, (900,), 8, 64, True, 100, True, 7),
     (4, 1, 16, 16, 128, 256, 4, (1023, 1, 500, 768), 1, 128, True, -1, False, 0),
     (2, 1, 12, 4, 128, 64, 4, (150, 77), 1, 0, True, -1, True, 0),
+    (2, 1, 8, 1, 128, 64, 6, (300, 17), 1, 128, True, -1, False, 0),
+    (1, 4, 64, 1, 64, 128, 4, (400,), 2, 0, True, -1, True, 0),
+    (2, 2, 16, 2, 128, None, 700, (650, 3), 1, 0, False, 30, False, 5),
 ]
 
 
