@@ -120,11 +120,13 @@ struct PairStream {
     const auto ra = rsrc(abase, t);
 #pragma unroll
     for (int i = 0; i < PWA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dsta + 1024 * (lw + BWD_NW * i), 16, (int)aoff[i], 0, 0, 0);
+      if (lw + BWD_NW * i < LA)  // loads wholly past the tile are skipped (wave-uniform)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dsta + 1024 * (lw + BWD_NW * i), 16, (int)aoff[i], 0, 0, 0);
     const auto rb = rsrc(bbase, t);
 #pragma unroll
     for (int i = 0; i < PWB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dstb + 1024 * (lw + BWD_NW * i), 16, (int)boff[i], 0, 0, 0);
+      if (lw + BWD_NW * i < LB)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dstb + 1024 * (lw + BWD_NW * i), 16, (int)boff[i], 0, 0, 0);
   }
 };
 

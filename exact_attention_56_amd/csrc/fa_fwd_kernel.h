@@ -68,13 +68,15 @@ struct Tile {
   static constexpr int VCH = CPR + 2;        // 16-byte slots per V row in LDS
   static constexpr int KPITCH = KCH * 16;    // bytes
   static constexpr int VPITCH = VCH * 16;
-  // 64-lane (1 KiB) direct loads per tile: the tile needs KCH (VCH) of them; the
-  // count is rounded up to a multiple of the 4 waves so every wave issues the same
-  // loads without a branch, and the buffer has room for the extra (all-zero) ones.
-  static constexpr int KPW = (KCH + 3) / 4;  // K loads per loading wave (4 waves load K)
-  static constexpr int VPW = (VCH + 3) / 4;  // V loads per loading wave (4 waves load V)
-  static constexpr int KBYTES = 4096 * KPW;  // one K buffer (>= BC * KPITCH)
-  static constexpr int VBYTES = 4096 * VPW;  // one V buffer (>= BC * VPITCH)
+  // 64-lane (1 KiB) direct loads per tile: the tile needs KCH (VCH) of them, load u
+  // issued by loading wave u % 4.  A wave skips the loads that would lie wholly past
+  // the tile (a wave-uniform test): issuing them as all-zero loads, so that every
+  // wave issued the same number, cost measurably (20 instead of 17 K loads per tile
+  // at headdim 128).
+  static constexpr int KPW = (KCH + 3) / 4;  // most K loads a loading wave issues (4 waves load K)
+  static constexpr int VPW = (VCH + 3) / 4;  // most V loads a loading wave issues (4 waves load V)
+  static constexpr int KBYTES = 1024 * KCH;  // one K buffer (>= BC * KPITCH)
+  static constexpr int VBYTES = 1024 * VCH;  // one V buffer (>= BC * VPITCH)
   // Ring of NBUF K and NBUF V buffers: K runs NBUF tiles ahead of the step that
   // reads it and V NBUF-1, so a tile's loads have NBUF-1 steps to land.  Headdim 64
   // measured slower with three buffers, so every headdim keeps two.
@@ -83,9 +85,11 @@ struct Tile {
 #endif
   static constexpr int NBUF = HD == 256 ? 2 : FA_NBUF;
   static constexpr int LDS_BYTES = NBUF * (KBYTES + VBYTES);
-  // loads one wave issues per step (its vmcnt after a step's loads)
+  // most loads a wave issues per step (the size of the scheduling group), and the
+  // fewest: a wait until at most MIN_LOADS_PER_STEP of its loads are in flight
+  // leaves every earlier step's loads landed
   static constexpr int LOADS_PER_STEP = NW == 4 ? KPW + VPW : KPW;
-  static_assert(NW == 4 || KPW == VPW, "K- and V-loading waves issue equally many loads");
+  static constexpr int MIN_LOADS_PER_STEP = NW == 4 ? KCH / 4 + VCH / 4 : (KCH < VCH ? KCH : VCH) / 4;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -145,7 +149,8 @@ struct KVStream {
     const auto rs = tile_rsrc(kbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)koff[i], 0, 0, 0);
+      if (lw + 4 * i < T::KCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)koff[i], 0, 0, 0);
   }
   __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
     if (!loads_v) return;
@@ -153,7 +158,8 @@ struct KVStream {
     const auto rs = tile_rsrc(vbase + (long)j0 * row_stride, key_hi - j0, row_bytes);
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)voff[i], 0, 0, 0);
+      if (lw + 4 * i < T::VCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)voff[i], 0, 0, 0);
   }
 };
 
@@ -179,7 +185,8 @@ struct PagedKVStream : KVStream<HD, NW> {
     const auto rs = tile_rsrc(this->kbase + tile_row(j0) * this->row_stride, this->key_hi - j0, this->row_bytes);
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->koff[i], 0, 0, 0);
+      if (this->lw + 4 * i < T::KCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->koff[i], 0, 0, 0);
   }
   __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
     if (!this->loads_v) return;
@@ -187,7 +194,8 @@ struct PagedKVStream : KVStream<HD, NW> {
     const auto rs = tile_rsrc(this->vbase + tile_row(j0) * this->row_stride, this->key_hi - j0, this->row_bytes);
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->voff[i], 0, 0, 0);
+      if (this->lw + 4 * i < T::VCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (this->lw + 4 * i), 16, (int)this->voff[i], 0, 0, 0);
   }
 };
 
@@ -374,7 +382,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   if constexpr (!std::is_same_v<KV, KVStream<HD, NW>>) {
     // decode form: a wave none of whose rows exists only streams tiles for the others
     if (!kv.active) {
-      wait_tile_loads<NB == 2 ? 0 : T::LOADS_PER_STEP>();
+      wait_tile_loads<NB == 2 ? 0 : T::MIN_LOADS_PER_STEP>();
       __syncthreads();
       return;
     }
@@ -508,7 +516,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
     st.m_run = m_new;
   }
   // K(t+2) and V(t+1) (loaded NB-2 steps ago) are in LDS before anyone passes the barrier
-  wait_tile_loads<NB == 2 ? 0 : T::LOADS_PER_STEP>();
+  wait_tile_loads<NB == 2 ? 0 : T::MIN_LOADS_PER_STEP>();
   __syncthreads();
 }
 
