@@ -704,10 +704,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   }
 
   // two tiles per trip so S(t) and S(t+1) swap roles without register copies.  Where
-  // the registers allow it (headdim 128, and 64 without ALiBi, outside the decode
-  // form) the item's last tile takes the short LAST step: +1-3.5% on 2k-4k launches;
-  // elsewhere its extra code cost a wave per SIMD or spilled.
-  constexpr bool SHORT_LAST = !DEC && (HD == 128 || (HD == 64 && !ALIBI));
+  // the registers allow it (headdim 128, and 64 except the split ALiBi form, outside
+  // the decode form) the item's last tile takes the short LAST step: +1-3.5% on 2k-4k
+  // launches; elsewhere its extra code spilled in the loop.
+  constexpr bool SHORT_LAST = !DEC && (HD == 128 || (HD == 64 && (!ALIBI || !SPLIT)));
   if constexpr (SHORT_LAST) {
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
@@ -780,8 +780,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
 // One workgroup per work item.  (A grid of only the resident workgroups looping
 // over items with a static stride was measured slower: the causal items' unequal
 // lengths then leave CUs idle.)
+// Headdim 64 asks for three waves per SIMD: the register allocator then fits the ALiBi
+// kernel's short last step into 168 registers (12 bytes per lane spilled) instead of
+// giving up the third wave.
 template <int HD, int NW, bool ALIBI, bool SPLIT, typename E>
-__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p, int items) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 3 : 1))) void fwd_kernel(
+    FwdParams p, int items) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<HD, NW>::LDS_BYTES];
   fwd_item<HD, NW, ALIBI, SPLIT, E>(p, smem, blockIdx.x, items);
 }
