@@ -479,17 +479,24 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
       __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
     }
   } else if constexpr (FA_SCHED == 1) {
-#ifndef FA_V1
-#define FA_V1 3
+#ifndef FA_V1_256
+#define FA_V1_256 4
 #endif
-#ifndef FA_V2
-#define FA_V2 5
+#ifndef FA_V2_256
+#define FA_V2_256 5
 #endif
+#ifndef FA_PF_256
+#define FA_PF_256 12
+#endif
+    // vector instructions placed after each product of the S(t+1) phase (V1) and of the
+    // P V phase (V2); headdim 256 (one wave per SIMD, 32 products per phase) measured
+    // +11% with four instead of three after each S product, which leaves room for all of
+    // tile t's exponentials inside the first phase
+    constexpr int FA_V1 = HD == 256 ? FA_V1_256 : 3;  // headdim 64: 3-14 all within 1%
+    constexpr int FA_V2 = HD == 256 ? FA_V2_256 : 5;
     // LDS operand reads issued ahead of the first product: at headdim 256 only one
     // wave runs per SIMD, so a deeper queue hides more LDS latency.
-#ifndef FA_PF
-    constexpr int FA_PF = HD == 256 ? 12 : 2;
-#endif
+    constexpr int FA_PF = HD == 256 ? FA_PF_256 : 2;
 #ifndef FA_VI
 #define FA_VI 0
 #endif
