@@ -58,8 +58,10 @@ constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: re
 
 // LDS tiles.  A K row keeps its HD/8 16-byte chunks plus one pad slot (16 lanes
 // reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); a V row
-// keeps two pad slots (the 4 rows one transpose read touches land on disjoint
-// 8-bank groups).  Pad slots are filled with zeros by out-of-range loads.
+// keeps two pad slots (the 4 rows that 16 lanes of a transpose read touch land on
+// disjoint 8-bank groups; the two 16-lane groups of one 32-lane half still overlap,
+// a 2-way conflict that a 4-slot pad removes at a measured net loss, its extra loads
+// costing more).  Pad slots are filled with zeros by out-of-range loads.
 template <int HD, int NW>
 struct Tile {
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
