@@ -44,11 +44,16 @@ long long elems4(long long a, long long b, long long c, long long d) {
   return r;
 }
 
+// 16-bit tensors start on a 16-byte boundary (the kernels move 16 bytes per lane);
+// a NULL optional pointer passes.
+bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
+
 // Shared validation of the entry points.  Fills p on success.
 int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q, int seqlen_k,
             int nheads, int headdim, float softmax_scale, int causal, int window_left, int window_right,
             const float* alibi_slopes, int alibi_per_batch, int dtype, fa::FwdParams* p) {
   if (!q || !k || !v) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_INVALID_ARG;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
   if (alibi_per_batch != 0 && alibi_per_batch != 1) return FA_ERR_INVALID_ARG;
   if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || nheads < 1 || headdim < 1) return FA_ERR_INVALID_ARG;
@@ -118,7 +123,7 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen_q,
            int seqlen_k, int nheads, int headdim, float softmax_scale, int causal, int window_left,
            int window_right, const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse) return FA_ERR_INVALID_ARG;
+  if (!out || !lse || !aligned16(out)) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
                          window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
@@ -134,7 +139,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_parti
                    int batch, int seqlen_q, int seqlen_k, int nheads, int headdim, float softmax_scale,
                    int causal, int window_left, int window_right, const float* alibi_slopes,
                    int alibi_per_batch, int dtype, int num_splits, hipStream_t stream) {
-  if (!out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
+  if (!out_partial || !lse_partial || !aligned16(out_partial)) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
                          window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
@@ -161,7 +166,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float*
                   const int* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int nheads,
                   int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
                   const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (!out || !lse || !cu_seqlens_q || !cu_seqlens_k || !aligned16(out)) return FA_ERR_INVALID_ARG;
   if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1) return FA_ERR_INVALID_ARG;
   // The per-sequence lengths live on the device; the maxima size the grid and the
   // window normalisation.  One padded "batch" of max_seqlen rows is validated in
@@ -188,6 +193,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            int headdim, float softmax_scale, int causal, int window_left, int window_right,
            const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
   fa::FwdParams f;  // the forward's validation and window normalisation
   const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
                          window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
@@ -237,6 +244,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
                   int headdim, float softmax_scale, int causal, int window_left, int window_right,
                   const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_INVALID_ARG;
   if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1 || total_k < 1 || batch < 1)
     return FA_ERR_INVALID_ARG;
@@ -294,6 +303,7 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
                    const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
                    hipStream_t stream) {
   if (!cache_seqlens || !out || !lse || !out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(out_partial) || !aligned16(k_new) || !aligned16(v_new)) return FA_ERR_INVALID_ARG;
   if (seqlen_q < 1 || seqlen_q > kDecodeMaxRows || seqlen_new < 0 || page_size < 1 || max_splits < 1)
     return FA_ERR_INVALID_ARG;
   if (nheads < 1 || nheads_k < 1 || nheads % nheads_k != 0) return FA_ERR_INVALID_ARG;
@@ -364,6 +374,7 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,
                int seqlen_q, int nheads, int headdim, int num_splits, int dtype, hipStream_t stream) {
   if (!out_partial || !lse_partial || !out || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(out_partial) || !aligned16(out)) return FA_ERR_INVALID_ARG;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
   if (batch < 1 || seqlen_q < 1 || nheads < 1 || headdim < 1 || num_splits < 1) return FA_ERR_INVALID_ARG;
   if (seqlen_q > kMaxSeqlen) return FA_ERR_INVALID_ARG;

@@ -30,6 +30,9 @@
  *     (the gradients of fa_bwd and the KV cache included): FA_BF16 or FA_FP16.  The
  *     arithmetic is the same for both: fp32 accumulation, the probabilities rounded
  *     to dtype for the P V product, the output rounded to dtype (nearest even).
+ *     Every such tensor (q, k, v, out, the cache and appended rows, dout, dq, dk, dv),
+ *     and the fp32 split partials out_partial, starts on a 16-byte boundary: the
+ *     kernels move 16 bytes per lane.
  *   - lse: fp32, contiguous [batch, nheads, seqlen_q], natural logarithm of
  *     sum_j exp(softmax_scale * q_i . k_j + bias_ij) over the visible keys.
  *   - Visibility (bottom-right alignment): query i sits at key position
@@ -55,7 +58,8 @@
  *
  * Errors (return value)
  *   FA_OK (0) on success.  On any error nothing is launched and no output is touched:
- *   FA_ERR_INVALID_ARG (-1): a NULL required pointer, a size < 1, a window side < -1,
+ *   FA_ERR_INVALID_ARG (-1): a NULL required pointer, a 16-bit tensor pointer that is
+ *                            not 16-byte aligned, a size < 1, a window side < -1,
  *                            num_splits outside [1, seqlen_k], a non-finite softmax_scale,
  *                            a dtype other than FA_BF16 / FA_FP16, alibi_per_batch
  *                            other than 0 / 1, or a problem whose element count

@@ -63,6 +63,8 @@ def fwd_args(**over):
     (dict(scale=math.nan), -1), (dict(headdim=96), -2), (dict(headdim=32), -2), (dict(headdim=512), -2),
     (dict(seqlen_q=(1 << 30) + 1), -1), (dict(dtype=2), -1), (dict(dtype=-1), -1), (dict(per_batch=2), -1),
     (dict(per_batch=-1, alibi=FAKE), -1),
+    # 16-bit tensors start on a 16-byte boundary
+    (dict(q=FAKE + 8), -1), (dict(k=FAKE + 2), -1), (dict(v=FAKE + 4), -1), (dict(out=FAKE + 8), -1),
 ])
 def test_fwd_rejects_invalid(lib, over, code):
     assert lib.fa_fwd(*fwd_args(**over)) == code
@@ -71,6 +73,7 @@ def test_fwd_rejects_invalid(lib, over, code):
 @pytest.mark.parametrize("over,ns,code", [
     (dict(), 0, -1), (dict(), 5, -1), (dict(), -1, -1), (dict(out=None), 2, -1),
     (dict(headdim=80), 2, -2), (dict(scale=math.nan), 2, -1), (dict(dtype=3), 2, -1), (dict(per_batch=5), 2, -1),
+    (dict(q=FAKE + 8), 2, -1), (dict(out=FAKE + 4), 2, -1),
 ])
 def test_splitkv_rejects_invalid(lib, over, ns, code):
     a = fwd_args(**over)
@@ -91,7 +94,7 @@ def varlen_args(**over):
     (dict(nheads_k=0), -1), (dict(nheads_k=3), -1), (dict(nheads=2, nheads_k=4), -1), (dict(total_q=0), -1),
     (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(max_sk=-1), -1), (dict(wl=-3), -1),
     (dict(scale=math.inf), -1), (dict(headdim=80), -2), (dict(nheads=1 << 16, nheads_k=1 << 16), -2),
-    (dict(dtype=2), -1), (dict(per_batch=3), -1),
+    (dict(dtype=2), -1), (dict(per_batch=3), -1), (dict(out=FAKE + 8), -1), (dict(k=FAKE + 2), -1),
 ])
 def test_varlen_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_varlen(*varlen_args(**over)) == code
@@ -112,7 +115,7 @@ def kvc_args(**over):
     (dict(max_blocks=0), -1), (dict(nheads_k=3), -1), (dict(cos=FAKE), -1), (dict(cos=FAKE, sin=FAKE, rd=3), -1),
     (dict(cos=FAKE, sin=FAKE, rd=256), -1), (dict(num_splits=17), -1), (dict(num_splits=-1), -1),
     (dict(max_splits=0), -1), (dict(headdim=80), -2), (dict(table=None, page=0), -1), (dict(dtype=7), -1),
-    (dict(per_batch=2), -1),
+    (dict(per_batch=2), -1), (dict(out=FAKE + 8), -1), (dict(op=FAKE + 8), -1), (dict(kc=FAKE + 8), -1),
 ])
 def test_kvcache_rejects_invalid(lib, over, code):
     assert lib.fa_fwd_kvcache(*kvc_args(**over)) == code
@@ -130,7 +133,7 @@ def bwd_args(**over):
     (dict(out=None), -1), (dict(lse=None), -1), (dict(dout=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
     (dict(dv=None), -1), (dict(delta=None), -1), (dict(q=None), -1), (dict(batch=0), -1), (dict(seqlen_k=0), -1),
     (dict(wl=-2), -1), (dict(scale=math.nan), -1), (dict(headdim=32), -2), (dict(headdim=96), -2),
-    (dict(dtype=2), -1), (dict(per_batch=4), -1),
+    (dict(dtype=2), -1), (dict(per_batch=4), -1), (dict(dq=FAKE + 8), -1), (dict(dout=FAKE + 2), -1),
 ])
 def test_bwd_rejects_invalid(lib, over, code):
     assert lib.fa_bwd(*bwd_args(**over)) == code
@@ -150,6 +153,7 @@ def bwd_varlen_args(**over):
     (dict(total_q=0), -1), (dict(total_k=0), -1), (dict(batch=0), -1), (dict(max_sq=0), -1), (dict(wl=-3), -1),
     (dict(scale=math.inf), -1), (dict(headdim=512), -2), (dict(headdim=80), -2), (dict(dtype=2), -1),
     (dict(per_batch=3), -1),
+    (dict(dv=FAKE + 8), -1), (dict(out=FAKE + 2), -1),
 ])
 def test_bwd_varlen_rejects_invalid(lib, over, code):
     assert lib.fa_bwd_varlen(*bwd_varlen_args(**over)) == code
@@ -161,6 +165,8 @@ def test_bwd_varlen_rejects_invalid(lib, over, code):
     ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 2, 0, None), -1),
     ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 100, 2, 0, None), -2),
     ((FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 2, None), -1),
+    ((FAKE + 8, FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 0, None), -1),
+    ((FAKE, FAKE, FAKE + 8, FAKE, 1, 1, 1, 64, 2, 0, None), -1),
 ])
 def test_combine_rejects_invalid(lib, args, code):
     assert lib.fa_combine(*args) == code
