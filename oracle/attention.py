@@ -291,11 +291,28 @@ def attention_backward_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, softmax
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round fp64 values to bf16 (round to nearest, ties to even), returned as fp64:
-    the precision of the cache and of the operands the kernels multiply."""
-    import torch  # local import: rounding through torch's own RNE conversion
+    """Round fp64 values to bf16 in one step (round to nearest, ties to even), returned
+    as fp64: the precision of the cache and of the operands the kernels multiply.
 
-    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    bf16 keeps fp32's 8 exponent bits and 7 stored mantissa bits.  A value of binary
+    exponent e (2^e <= |x| < 2^(e+1)) therefore sits on a grid of spacing 2^(e-7),
+    and below the smallest normal 2^-126 on the subnormal grid 2^-133.  The quotient
+    x / spacing is exact in fp64 (a power-of-two scaling), numpy's rint rounds it to
+    the nearest integer with ties to even, and the product is exact again.  A result
+    of magnitude 2^128 or more lies past the largest finite bf16 (2 - 2^-7) * 2^127,
+    so it becomes infinity; zeros, infinities and NaN pass through.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    _, e2 = np.frexp(xf)  # xf = m * 2^e2 with 0.5 <= |m| < 1, so e = e2 - 1
+    e = np.maximum(e2.astype(np.int64) - 1, -126)
+    spacing = np.ldexp(1.0, (e - 7).astype(np.int32))
+    r = np.rint(xf / spacing) * spacing
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, xf), r)
+    out[fin] = r
+    return out
 
 
 def round_fp16(x: np.ndarray) -> np.ndarray:
@@ -304,8 +321,6 @@ def round_fp16(x: np.ndarray) -> np.ndarray:
     with np.errstate(over="ignore"):  # overflow to inf is the IEEE result
         return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
-
-ROUNDING = {"bf16": round_bf16, "fp16": round_fp16}
 
 
 def rotary(x: np.ndarray, positions: np.ndarray, cos: np.ndarray, sin: np.ndarray, rotary_dim: int) -> np.ndarray:
@@ -357,7 +372,7 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, softmax_scale: float, 
     v_app = None if vn is None else np.zeros(vn.shape)
     heads = [h // group for h in range(nheads)]
     slopes = slope_table(alibi_slopes, batch, nheads)
-    rnd = ROUNDING[storage]
+    rnd = {"bf16": round_bf16, "fp16": round_fp16}[storage]  # looked up per call
     for b in range(batch):
         rows = []
         for j in range(lens[b]):  # the cached keys, through the block table

@@ -425,6 +425,39 @@ def pin_kvcache(storage="bf16"):
             assert np.allclose(l1[b][fin], lb[0][fin], atol=1e-12)
 
 
+def pin_round_bf16():
+    """Rounding to bf16 from first principles (8 exponent bits as in fp32, 7 stored
+    mantissa bits), worked out by hand: spacing 2^-7 on [1, 2), ties to the even
+    neighbour, a value just above a tie, a value whose rounding to fp32 first would
+    create a false tie (1 + 2^-8 + 2^-40 must go up), negatives, the largest finite
+    value (2 - 2^-7) * 2^127 with its overflow tie (2 - 2^-8) * 2^127 going to infinity,
+    the subnormal spacing 2^-133 and the normal/subnormal boundary, and 0.1 (mantissa
+    1.6 * 128 = 204.8 -> 205, i.e. 205 / 2048)."""
+    big = (2 - 2.0 ** -7) * 2.0 ** 127
+    tie_inf = (2 - 2.0 ** -8) * 2.0 ** 127
+    cases = [(1 + 2.0 ** -8, 1.0), (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6), (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7),
+             (1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -7), (1 + 2.0 ** -8 - 2.0 ** -30, 1.0),
+             (-(1 + 2.0 ** -8), -1.0), (-(1 + 3 * 2.0 ** -8), -(1 + 2.0 ** -6)), (-(1 + 2.0 ** -8 + 2.0 ** -30),
+                                                                               -(1 + 2.0 ** -7)),
+             (3.0 + 2.0 ** -7, 3.0), (3.0 + 3 * 2.0 ** -7, 3.0 + 2.0 ** -5),
+             (big, big), (tie_inf - 2.0 ** 100, big), (tie_inf, math.inf), (-tie_inf, -math.inf),
+             (2.0 ** -133, 2.0 ** -133), (2.0 ** -134, 0.0), (3 * 2.0 ** -134, 2.0 ** -132),
+             (2.0 ** -134 + 2.0 ** -160, 2.0 ** -133), (2.0 ** -126 - 2.0 ** -134, 2.0 ** -126),
+             (2.0 ** -126 - 3 * 2.0 ** -134, 2.0 ** -126 - 2.0 ** -132),
+             (0.1, 205.0 / 2048.0), (-0.1, -205.0 / 2048.0), (0.0, 0.0), (math.inf, math.inf)]
+    x = np.array([c[0] for c in cases])
+    got = oracle.round_bf16(x)
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(got, want), [(a, g, w) for a, g, w in zip(x, got, want) if g != w]
+    assert np.isnan(oracle.round_bf16(np.array([math.nan]))[0])
+    assert math.copysign(1.0, oracle.round_bf16(np.array([-0.0]))[0]) == -1.0
+    # every value already on the bf16 grid is a fixed point (all 2^16 bit patterns but NaN)
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    pat = bits.view(np.float32)
+    grid = pat[~np.isnan(pat)].astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(grid), grid)
+
+
 def pin_round_fp16():
     """Rounding to IEEE binary16 from first principles: spacing 2^-10 on [1, 2), ties to
     the even neighbour, largest finite value 65504 (a tie at 65520 goes to infinity),
@@ -596,6 +629,10 @@ def test_round_fp16():
     pin_round_fp16()
 
 
+def test_round_bf16():
+    pin_round_bf16()
+
+
 def test_per_batch_slopes():
     pin_per_batch_slopes()
 
@@ -706,6 +743,7 @@ def _all_pins():
     pin_kvcache()
     pin_kvcache("fp16")
     pin_round_fp16()
+    pin_round_bf16()
     pin_per_batch_slopes()
 
 
@@ -866,6 +904,35 @@ def _slopes_first_row(alibi_slopes, batch, nheads):
     return None if t is None else np.tile(t[0], (batch, 1))
 
 
+def _round_bf16_truncate(x):
+    # toward zero: keep the top 16 bits of the fp32 pattern
+    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _round_bf16_half_away(x):
+    # ties away from zero instead of to even
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e2 = np.frexp(x[fin])
+    sp = np.ldexp(1.0, (np.maximum(e2 - 1, -126) - 7).astype(np.int32))
+    q = x[fin] / sp
+    r = np.sign(q) * np.floor(np.abs(q) + 0.5) * sp
+    out[fin] = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x[fin]), r)
+    return out
+
+
+def _round_bf16_via_fp16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _round_bf16_via_fp32(x):
+    # two roundings (fp64 -> fp32 -> bf16) instead of one
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def _round_fp16_via_bf16(x):
     return oa.round_bf16(x)
 
@@ -907,6 +974,10 @@ _ORIG_SLOPES = oa.slope_table
     ("slope_table", _slopes_first_row),
     ("round_fp16", _round_fp16_via_bf16),
     ("round_fp16", _round_fp16_truncate),
+    ("round_bf16", _round_bf16_truncate),
+    ("round_bf16", _round_bf16_half_away),
+    ("round_bf16", _round_bf16_via_fp16),
+    ("round_bf16", _round_bf16_via_fp32),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, replacement):
     """Each planted oracle mistake must make at least one pin fail."""
