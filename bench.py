@@ -111,19 +111,21 @@ class FwdCase:
                (self.w.window_left, self.w.window_right), self.slopes)
 
 
-def warm_up(fn, launches: int, min_seconds: float = 0.15):
+def warm_up(fn, launches: int, min_seconds: float = 0.3) -> float:
     """Untimed launches of fn(): at least `launches`, and more until `min_seconds` of
-    wall time have passed.  Each extra workload draws fresh tensors; its first launches
-    over them ran up to 10% slow even with the GPU already warm, so every workload
-    gets about the same settling time whatever its launch length."""
+    wall time have passed; returns the seconds spent.  A fixed handful of launches
+    measured 10-20% slow while the clock ramps, and each extra workload draws fresh
+    tensors whose first launches ran slow even on a warm GPU, so every workload (the
+    headline step included) gets about the same settling time whatever its length."""
+    t0 = time.perf_counter()
     for _ in range(launches):
         fn()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     while time.perf_counter() - t0 < min_seconds:
         for _ in range(4):
             fn()
         torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def time_events(fn, reps: int):
@@ -139,36 +141,76 @@ def time_events(fn, reps: int):
     return sum(ts) / len(ts), min(ts)
 
 
-def cpu_baseline(cases, budget_s: float):
-    """The fp64 oracle on host cores over whole (batch, head) slices of the workload."""
-    import numpy as np
+CPU_WORKERS_MAX = 16  # the host-CPU share of one GPU on the measurement boxes
+
+
+def _cpu_worker_init():
+    """Each oracle worker runs single-threaded: the pool, not BLAS, spreads the work."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing: BLAS keeps its default
+        pass
+
+
+def _oracle_slice(task):
+    """One (batch, head) slice of a workload through the fp64 oracle."""
+    import oracle
+    q, k, v, scale, causal, wl, wr = task
+    oracle.attention_forward(q, k, v, scale, causal, wl, wr)
+    return True
+
+
+def start_cpu_pool():
+    """Worker processes for cpu_baseline, forked before this process touches the GPU
+    (the children inherit no GPU state).  Returns (pool, workers)."""
+    import multiprocessing
+    n = max(1, min(CPU_WORKERS_MAX, os.cpu_count() or 1))
+    return multiprocessing.get_context("fork").Pool(n, initializer=_cpu_worker_init), n
+
+
+def cpu_baseline(cases, budget_s: float, pool, workers: int):
+    """The fp64 oracle, as it stands, on the host cores: whole (batch, head) slices of
+    the workload, one per single-threaded worker process at a time, until every slice
+    is done or `budget_s` has passed (slices already started are finished and counted)."""
+    from collections import deque
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    done_flops, n_slices = 0.0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+    tasks = []
+    n_pairs = cases[0].w.batch * cases[0].w.nheads
+    for n in range(n_pairs):
         for case in cases:
             w = case.w
-            b, h = n_slices % w.batch, (n_slices // w.batch) % w.nheads
-            q = case.q_cpu[b:b + 1, :, h:h + 1]
-            k = case.k_cpu[b:b + 1, :, h:h + 1]
-            v = case.v_cpu[b:b + 1, :, h:h + 1]
-            oracle.attention_forward(q, k, v, w.softmax_scale, w.causal, w.window_left, w.window_right)
-            done_flops += case.flops / (w.batch * w.nheads)
-        n_slices += 1
-        if n_slices >= cases[0].w.batch * cases[0].w.nheads:
+            b, h = n % w.batch, (n // w.batch) % w.nheads
+            tasks.append((case, b, h))
+    pending = deque()
+    done_flops, done = 0.0, 0
+    t0 = time.perf_counter()
+    it = iter(tasks)
+    while True:
+        while len(pending) < 2 * workers and time.perf_counter() - t0 < budget_s:
+            nxt = next(it, None)
+            if nxt is None:
+                break
+            case, b, h = nxt
+            w = case.w
+            arg = (oracle.as_f64(case.q_cpu[b:b + 1, :, h:h + 1]), oracle.as_f64(case.k_cpu[b:b + 1, :, h:h + 1]),
+                   oracle.as_f64(case.v_cpu[b:b + 1, :, h:h + 1]), w.softmax_scale, w.causal, w.window_left,
+                   w.window_right)
+            pending.append((pool.apply_async(_oracle_slice, (arg,)), case.flops / (w.batch * w.nheads)))
+        if not pending:
             break
+        res, fl = pending.popleft()
+        res.get()
+        done_flops += fl
+        done += 1
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_slices} (batch, head) slices of each of: "
-                      + ", ".join(c.w.name for c in cases)
-                      + f" (full seqlen rows, fp64 NumPy), {dt:.1f} s; host has {os.cpu_count()} logical CPUs"
-                      + (f" ({cpu_model()})" if cpu_model() else "")}
+    names = ", ".join(c.w.name for c in cases)
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"{done} of the {len(tasks)} (batch, head) slices of {names} (full seqlen rows, fp64 NumPy), "
+                      f"{dt:.1f} s on {workers} single-threaded worker processes; host has {os.cpu_count()} "
+                      f"logical CPUs" + (f" ({cpu_model()})" if cpu_model() else "")}
 
 
 def cpu_model() -> str:
@@ -394,8 +436,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=400,
-                    help="untimed steps first (about 0.2 s: lets the GPU reach its steady clock)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps first (at least)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="and untimed steps until this much wall time has passed (the clock settles)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip every extra workload")
@@ -412,6 +455,8 @@ def main():
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(each GPU would run fa_fwd on its own batch/head share).", file=sys.stderr)
         sys.exit(2)
+    # the oracle's worker processes are forked before anything touches the GPU
+    pool, workers = (None, 0) if args.no_cpu_baseline else start_cpu_pool()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -431,9 +476,7 @@ def main():
         for c in cases:
             c.launch()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_s = warm_up(step, args.warmup, args.warmup_seconds)
 
     # timed region: exactly K steps, wall clock bracketed by synchronisation, with
     # HIP events around every forward launch on the launch stream
@@ -474,6 +517,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -501,7 +545,9 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = src.numel()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget, pool, workers)
+        pool.close()
+        pool.join()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

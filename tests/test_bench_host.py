@@ -39,3 +39,27 @@ def test_multi_gpu_refused():
     res = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                          cwd=bench.ROOT, timeout=300)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_cpu_baseline_pool_reports_its_workers():
+    """cpu_baseline runs whole (batch, head) slices on single-threaded worker processes
+    and reports how many it used; on a tiny workload every slice finishes."""
+    from exact_attention_56_amd.inputs import make_qkv
+
+    class Case:
+        pass
+
+    w = WORKLOADS["tiny"]
+    q, k, v = make_qkv(w.batch, w.seqlen_q, w.seqlen_k, w.nheads, w.headdim, w.seed)
+    c = Case()
+    c.w, c.flops, c.q_cpu, c.k_cpu, c.v_cpu = w, bench.algorithmic_flops(w), q, k, v
+    import multiprocessing
+    pool = multiprocessing.get_context("fork").Pool(2, initializer=bench._cpu_worker_init)
+    try:
+        res = bench.cpu_baseline([c], 30.0, pool, 2)
+    finally:
+        pool.close()
+        pool.join()
+    assert res["cores"] == 2 and res["kind"] == "oracle" and res["value"] > 0
+    assert res["sample"].startswith(f"{w.batch * w.nheads} of the {w.batch * w.nheads} ")
+    assert "2 single-threaded worker processes" in res["sample"]
