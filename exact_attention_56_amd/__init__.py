@@ -389,6 +389,14 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
     if rotary_cos is not None:
         _require(rotary_cos, "rotary_cos", torch.float32, 2, q.device)
         _require(rotary_sin, "rotary_sin", torch.float32, 2, q.device)
+        if rotary_sin.shape != rotary_cos.shape:
+            raise ValueError("rotary_cos and rotary_sin must have the same shape [positions, rotary_dim / 2]")
+        # one row per cache position: rows cache_seqlens[b] + i are read for every
+        # appended key and query, and the positions reach the capacity at most
+        capacity = page * max_blocks
+        if rotary_cos.shape[0] < capacity:
+            raise ValueError(f"rotary tables need a row for every cache position ({capacity}), "
+                             f"got {rotary_cos.shape[0]}")
         rd = 2 * rotary_cos.shape[1]
     slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
     _require(out, "out", q.dtype, 4, q.device)

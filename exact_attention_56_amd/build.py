@@ -34,6 +34,9 @@ SOURCES = [
     ("fa_decode_kernel.hip", []),
     ("fa_api.hip", []),
 ]
+# host-only C++ (argument validation and launch planning): compiled by the host compiler
+HOST_SOURCES = ["fa_validate.cpp"]
+CXX = os.environ.get("CXX", "g++")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 OFFLOAD_ARCH = "gfx950"
 
@@ -43,6 +46,11 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+# host compiler flags: the ROCm headers (fa.h names hipStream_t) in their AMD form
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+              f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def _run(cmd, verbose):
@@ -68,6 +76,10 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         objs.append(obj)
         jobs.append([HIPCC, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(obj_dir, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        jobs.append([CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB_PATH + ".tmp"

@@ -1,121 +1,25 @@
 // fa_api.hip - the extern "C" entry points declared in include/fa.h.
 //
-// Validates every argument before any HIP call (so an invalid call launches
-// nothing and touches no output), fills the kernel parameter block and launches
-// on the caller's stream.  No allocation, no synchronisation, no global state.
-#include <math.h>
-#include <stdint.h>
-
-#include <algorithm>
-
+// Each entry point first runs its plan (fa_validate.cpp): every argument and every
+// grid of the call is checked before any HIP call, so an invalid call launches
+// nothing and touches no output.  Then it launches on the caller's stream, checking
+// the runtime's status after each launch before the next.  No allocation, no
+// synchronisation, no global state.
 #include "fa.h"
 #include "fa_bwd_kernel.h"
+#include "fa_validate.h"
 
 namespace fa {
 hipError_t launch_fwd(const FwdParams& p, int headdim, bool split, hipStream_t stream);
-long fwd_num_blocks(const FwdParams& p, bool split);
 hipError_t launch_decode(const FwdParams& p, int headdim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int headdim, hipStream_t stream);
 hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new, const uint16_t* v_new,
                           uint16_t* k_cache, uint16_t* v_cache, const float* cos, const float* sin, int rd,
                           uint16_t* qrot, hipStream_t stream);
-int decode_step_keys(int headdim);
-int decode_queries_per_block(int nq_total);
 }  // namespace fa
 
 namespace {
-
-constexpr int kMaxSeqlen = 1 << 30;     // keeps every position/window sum inside int32
-constexpr long kMaxBlocks = 0x7fffffffL;  // grid x dimension
-constexpr int kDecodeMaxRows = 8;       // fa_fwd_splitkv: vector-ALU path up to this seqlen_q
-constexpr long long kMaxRowElems = 1 << 22;  // nheads * headdim
-constexpr int kQTile = fa::FWD_BLOCK_ROWS;  // query rows per matrix-core workgroup
-
-bool headdim_supported(int d) { return d == 64 || d == 128 || d == 256; }
-
-// Elements of a [a, b, c, d] tensor, or -1 when it does not fit in int64.
-long long elems4(long long a, long long b, long long c, long long d) {
-  long long r = 1;
-  const long long f[4] = {a, b, c, d};
-  for (long long x : f) {
-    if (x <= 0 || r > (long long)INT64_MAX / 2 / x) return -1;
-    r *= x;
-  }
-  return r;
-}
-
-// 16-bit tensors start on a 16-byte boundary (the kernels move 16 bytes per lane);
-// a NULL optional pointer passes.
-bool aligned16(const void* x) { return ((uintptr_t)x & 15) == 0; }
-
-// Shared validation of the entry points.  Fills p on success.
-int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q, int seqlen_k,
-            int nheads, int headdim, float softmax_scale, int causal, int window_left, int window_right,
-            const float* alibi_slopes, int alibi_per_batch, int dtype, fa::FwdParams* p) {
-  if (!q || !k || !v) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
-  if (alibi_per_batch != 0 && alibi_per_batch != 1) return FA_ERR_INVALID_ARG;
-  if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || nheads < 1 || headdim < 1) return FA_ERR_INVALID_ARG;
-  if (seqlen_q > kMaxSeqlen || seqlen_k > kMaxSeqlen) return FA_ERR_INVALID_ARG;
-  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
-  if (!isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
-  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
-  if (elems4(batch, seqlen_q, nheads, headdim) < 0 || elems4(batch, seqlen_k, nheads, headdim) < 0)
-    return FA_ERR_INVALID_ARG;
-  // The kernels address at most 128 key rows (nheads*headdim bf16 apart) from one
-  // buffer base with 32-bit offsets.
-  if ((long long)nheads * headdim > kMaxRowElems) return FA_ERR_UNSUPPORTED;
-
-  int wl = window_left;
-  int wr = causal ? 0 : window_right;
-  // A side at least as wide as the whole key range is the same as no bound:
-  // c_i - wl < 0 <= j for every row when wl >= Sk, and c_i + wr >= Sk - 1 >= j
-  // for every row when wr >= Sq.
-  if (wl >= seqlen_k) wl = -1;
-  if (wr >= seqlen_q) wr = -1;
-
-  p->q = (const uint16_t*)q;
-  p->k = (const uint16_t*)k;
-  p->v = (const uint16_t*)v;
-  p->alibi = alibi_slopes;
-  p->alibi_bstride = alibi_per_batch ? nheads : 0;
-  p->f16 = dtype == FA_FP16 ? 1 : 0;
-  p->batch = batch;
-  p->seqlen_q = seqlen_q;
-  p->seqlen_k = seqlen_k;
-  p->nheads = nheads;
-  p->nheads_k = nheads;
-  p->cu_q = nullptr;
-  p->cu_k = nullptr;
-  p->lse_head_stride = 0;
-  p->cache_seqlens = nullptr;
-  p->block_table = nullptr;
-  p->page_size = 0;
-  p->page_shift = 0;
-  p->max_blocks = 0;
-  p->seqlen_new = 0;
-  // The kernels fold the scale into Q's sign and a positive multiplier: a negative
-  // scale negates Q, a zero scale zeroes Q (every score is then exactly 0).
-  if (softmax_scale == 0.f) {
-    p->scale_log2 = 1.f;
-    p->q_and = 0u;
-    p->q_sign = 0u;
-  } else {
-    p->scale_log2 = fabsf(softmax_scale) * fa::kLog2e;
-    p->q_and = 0xffffffffu;
-    p->q_sign = signbit(softmax_scale) ? 0x80008000u : 0u;
-  }
-  p->window_left = wl;
-  p->window_right = wr;
-  p->num_q_tiles = (seqlen_q + kQTile - 1) / kQTile;
-  p->num_splits = 1;
-  p->split_len = seqlen_k;
-  // Causal (or a right window): later query tiles see more keys; start them first.
-  p->reverse_q = (wr >= 0) ? 1 : 0;
-  return FA_OK;
-}
-
+int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 }  // namespace
 
 extern "C" {
@@ -123,119 +27,52 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int seqlen_q,
            int seqlen_k, int nheads, int headdim, float softmax_scale, int causal, int window_left,
            int window_right, const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse || !aligned16(out)) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
-  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
+  const int st = fa::plan_fwd(q, k, v, out, lse, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
+                              window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
-  p.out = out;
-  p.lse = lse;
-  if (fa::fwd_num_blocks(p, false) > kMaxBlocks) return FA_ERR_INVALID_ARG;
   (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
-  return fa::launch_fwd(p, headdim, false, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_fwd(p, headdim, false, stream));
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* out_partial, float* lse_partial,
                    int batch, int seqlen_q, int seqlen_k, int nheads, int headdim, float softmax_scale,
                    int causal, int window_left, int window_right, const float* alibi_slopes,
                    int alibi_per_batch, int dtype, int num_splits, hipStream_t stream) {
-  if (!out_partial || !lse_partial || !aligned16(out_partial)) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
-  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
+  int vector_path = 0;
+  const int st = fa::plan_fwd_splitkv(q, k, v, out_partial, lse_partial, batch, seqlen_q, seqlen_k, nheads, headdim,
+                                      softmax_scale, causal, window_left, window_right, alibi_slopes,
+                                      alibi_per_batch, dtype, num_splits, &p, &vector_path);
   if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > seqlen_k) return FA_ERR_INVALID_ARG;
-  if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
-  p.out = out_partial;
-  p.lse = lse_partial;
-  p.num_splits = num_splits;
-  p.split_len = (seqlen_k + num_splits - 1) / num_splits;
   (void)hipGetLastError();
-  hipError_t e;
-  if (seqlen_q <= kDecodeMaxRows) {
-    if ((long)batch * nheads * num_splits * seqlen_q > kMaxBlocks) return FA_ERR_INVALID_ARG;
-    e = fa::launch_decode(p, headdim, stream);
-  } else {
-    if (fa::fwd_num_blocks(p, true) > kMaxBlocks) return FA_ERR_INVALID_ARG;
-    e = fa::launch_fwd(p, headdim, true, stream);
-  }
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(vector_path ? fa::launch_decode(p, headdim, stream) : fa::launch_fwd(p, headdim, true, stream));
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_seqlens_q,
                   const int* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int nheads,
                   int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
                   const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse || !cu_seqlens_q || !cu_seqlens_k || !aligned16(out)) return FA_ERR_INVALID_ARG;
-  if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1) return FA_ERR_INVALID_ARG;
-  // The per-sequence lengths live on the device; the maxima size the grid and the
-  // window normalisation.  One padded "batch" of max_seqlen rows is validated in
-  // their place (every sequence is at most that long).
   fa::FwdParams p;
-  const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
+  const int st = fa::plan_fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q,
+                                     max_seqlen_k, total_q, nheads, nheads_k, headdim, softmax_scale, causal,
+                                     window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
   if (st != FA_OK) return st;
-  if (batch < 1 || elems4(total_q, nheads, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
-  p.batch = batch;
-  p.nheads_k = nheads_k;
-  p.cu_q = cu_seqlens_q;
-  p.cu_k = cu_seqlens_k;
-  p.lse_head_stride = total_q;
-  p.out = out;
-  p.lse = lse;
-  if (fa::fwd_num_blocks(p, false) > kMaxBlocks) return FA_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  return fa::launch_fwd(p, headdim, false, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_fwd(p, headdim, false, stream));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* delta, int batch, int seqlen_q, int seqlen_k, int nheads,
            int headdim, float softmax_scale, int causal, int window_left, int window_right,
            const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
-  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_INVALID_ARG;
-  fa::FwdParams f;  // the forward's validation and window normalisation
-  const int st = prepare(q, k, v, batch, seqlen_q, seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
-  if (st != FA_OK) return st;
-  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
   fa::BwdParams p;
-  p.q = f.q;
-  p.k = f.k;
-  p.v = f.v;
-  p.out = (const uint16_t*)out;
-  p.dout = (const uint16_t*)dout;
-  p.lse = lse;
-  p.delta = delta;
-  p.dq = (uint16_t*)dq;
-  p.dk = (uint16_t*)dk;
-  p.dv = (uint16_t*)dv;
-  p.alibi = alibi_slopes;
-  p.alibi_bstride = f.alibi_bstride;
-  p.f16 = f.f16;
-  p.batch = batch;
-  p.seqlen_q = seqlen_q;
-  p.seqlen_k = seqlen_k;
-  p.nheads = nheads;
-  p.scale = softmax_scale;
-  p.scale_log2 = f.scale_log2;
-  p.q_and = f.q_and;
-  p.q_sign = f.q_sign;
-  p.window_left = f.window_left;
-  p.window_right = f.window_right;
-  p.cu_q = nullptr;
-  p.cu_k = nullptr;
-  p.lse_head_stride = 0;
-  p.nheads_k = nheads;
-  p.num_q_tiles = (seqlen_q + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
-  p.num_k_tiles = (seqlen_k + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
-  const long rows = (long)batch * seqlen_q * nheads;
-  if ((long)batch * nheads * p.num_q_tiles > kMaxBlocks || (long)batch * nheads * p.num_k_tiles > kMaxBlocks ||
-      rows / 16 + 1 > kMaxBlocks)
-    return FA_ERR_INVALID_ARG;
+  const int st = fa::plan_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, batch, seqlen_q, seqlen_k, nheads, headdim,
+                              softmax_scale, causal, window_left, window_right, alibi_slopes, alibi_per_batch, dtype,
+                              &p);
+  if (st != FA_OK) return st;
   (void)hipGetLastError();
-  return fa::launch_bwd(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_bwd(p, headdim, stream));
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
@@ -243,56 +80,14 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
                   int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int nheads, int nheads_k,
                   int headdim, float softmax_scale, int causal, int window_left, int window_right,
                   const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream) {
-  if (!out || !lse || !dout || !dq || !dk || !dv || !delta || !cu_seqlens_q || !cu_seqlens_k)
-    return FA_ERR_INVALID_ARG;
-  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_INVALID_ARG;
-  if (nheads_k < 1 || nheads < 1 || nheads % nheads_k != 0 || total_q < 1 || total_k < 1 || batch < 1)
-    return FA_ERR_INVALID_ARG;
-  // As in fa_fwd_varlen: one padded sequence of the maximal lengths is validated in
-  // place of the device-resident per-sequence lengths.
-  fa::FwdParams f;
-  const int st = prepare(q, k, v, 1, max_seqlen_q, max_seqlen_k, nheads, headdim, softmax_scale, causal,
-                         window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &f);
-  if (st != FA_OK) return st;
-  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
-  if (elems4(total_q, nheads, headdim, 1) < 0 || elems4(total_k, nheads_k, headdim, 1) < 0) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
-  p.q = f.q;
-  p.k = f.k;
-  p.v = f.v;
-  p.out = (const uint16_t*)out;
-  p.dout = (const uint16_t*)dout;
-  p.lse = lse;
-  p.delta = delta;
-  p.dq = (uint16_t*)dq;
-  p.dk = (uint16_t*)dk;
-  p.dv = (uint16_t*)dv;
-  p.alibi = alibi_slopes;
-  p.alibi_bstride = f.alibi_bstride;
-  p.f16 = f.f16;
-  p.batch = batch;
-  p.seqlen_q = max_seqlen_q;
-  p.seqlen_k = max_seqlen_k;
-  p.nheads = nheads;
-  p.nheads_k = nheads_k;
-  p.cu_q = cu_seqlens_q;
-  p.cu_k = cu_seqlens_k;
-  p.lse_head_stride = total_q;
-  p.scale = softmax_scale;
-  p.scale_log2 = f.scale_log2;
-  p.q_and = f.q_and;
-  p.q_sign = f.q_sign;
-  p.window_left = f.window_left;
-  p.window_right = f.window_right;
-  p.num_q_tiles = (max_seqlen_q + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
-  p.num_k_tiles = (max_seqlen_k + fa::BWD_ROWS - 1) / fa::BWD_ROWS;
-  const long rows = (long)total_q * nheads;
-  if ((long)batch * nheads * p.num_q_tiles > kMaxBlocks || (long)batch * nheads_k * p.num_k_tiles > kMaxBlocks ||
-      rows / 16 + 1 > kMaxBlocks)
-    return FA_ERR_INVALID_ARG;
+  const int st = fa::plan_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, batch,
+                                     max_seqlen_q, max_seqlen_k, total_q, total_k, nheads, nheads_k, headdim,
+                                     softmax_scale, causal, window_left, window_right, alibi_slopes, alibi_per_batch,
+                                     dtype, &p);
+  if (st != FA_OK) return st;
   (void)hipGetLastError();
-  return fa::launch_bwd(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_bwd(p, headdim, stream));
 }
 
 int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens, const int* block_table,
@@ -302,98 +97,29 @@ int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache
                    int nheads_k, int headdim, float softmax_scale, int causal, int window_left, int window_right,
                    const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
                    hipStream_t stream) {
-  if (!cache_seqlens || !out || !lse || !out_partial || !lse_partial) return FA_ERR_INVALID_ARG;
-  if (!aligned16(out) || !aligned16(out_partial) || !aligned16(k_new) || !aligned16(v_new)) return FA_ERR_INVALID_ARG;
-  if (seqlen_q < 1 || seqlen_q > kDecodeMaxRows || seqlen_new < 0 || page_size < 1 || max_splits < 1)
-    return FA_ERR_INVALID_ARG;
-  if (nheads < 1 || nheads_k < 1 || nheads % nheads_k != 0) return FA_ERR_INVALID_ARG;
-  if (seqlen_new > 0 && (!k_new || !v_new)) return FA_ERR_INVALID_ARG;
-  if ((rotary_cos == nullptr) != (rotary_sin == nullptr)) return FA_ERR_INVALID_ARG;
-  if (rotary_cos && (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > headdim)) return FA_ERR_INVALID_ARG;
-  if (num_splits < 0 || num_splits > max_splits) return FA_ERR_INVALID_ARG;
-  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
-  int shift = 0;
-  long long capacity = page_size;
-  if (block_table) {
-    // a decode step never crosses a block: blocks are a power of two of at least 64 rows
-    if ((page_size & (page_size - 1)) != 0 || page_size < 64 || page_size % fa::decode_step_keys(headdim) != 0 ||
-        max_blocks_per_seq < 1)
-      return FA_ERR_INVALID_ARG;
-    while ((1 << shift) < page_size) ++shift;
-    capacity = (long long)page_size * max_blocks_per_seq;
-  }
-  if (capacity > kMaxSeqlen) return FA_ERR_INVALID_ARG;
   fa::FwdParams p;
-  const int st = prepare(q, k_cache, v_cache, batch, seqlen_q, (int)capacity, nheads, headdim, softmax_scale,
-                         causal, window_left, window_right, alibi_slopes, alibi_per_batch, dtype, &p);
+  fa::CombineParams c;
+  const int st = fa::plan_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table, page_size, max_blocks_per_seq,
+                                      k_new, v_new, seqlen_new, rotary_cos, rotary_sin, rotary_dim, out, lse,
+                                      out_partial, lse_partial, max_splits, batch, seqlen_q, nheads, nheads_k,
+                                      headdim, softmax_scale, causal, window_left, window_right, alibi_slopes,
+                                      alibi_per_batch, dtype, num_splits, &p, &c);
   if (st != FA_OK) return st;
-  // automatic split count, at least 256 keys per split.  A workgroup serves up to eight
-  // queries of one K/V head.  Workgroups of one or two queries are short: about 2048 of
-  // them (eight per CU) keep HBM busy.  Workgroups of four or eight queries do four to
-  // eight times the work per key: about 512 measured best (paged 32k-key caches, batch 8:
-  // +7% at four queries, +35-40% at eight, against 2048).
-  int ns = num_splits;
-  if (ns == 0) {
-    const int nq = nheads / nheads_k * seqlen_q;
-    const int per_block = fa::decode_uses_mfma(headdim, nq) ? 128 : fa::decode_queries_per_block(nq);
-    const long rows = (long)batch * nheads_k * ((nq + per_block - 1) / per_block);
-    const long target = nq >= 3 ? 512 : 2048;
-    ns = (int)std::min<long>(max_splits, std::max<long>(1, (target + rows - 1) / rows));
-    ns = (int)std::min<long long>(ns, std::max<long long>(1, capacity / 256));
-  }
-  if (elems4(ns, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
-  if ((long)batch * nheads * ns * seqlen_q > kMaxBlocks) return FA_ERR_INVALID_ARG;
-  p.nheads_k = nheads_k;
-  p.cache_seqlens = cache_seqlens;
-  p.block_table = block_table;
-  p.page_size = page_size;
-  p.page_shift = shift;
-  p.max_blocks = block_table ? max_blocks_per_seq : 1;
-  p.seqlen_new = seqlen_new;
-  p.out = out_partial;
-  p.lse = lse_partial;
-  p.num_splits = ns;
-  p.split_len = (int)((capacity + ns - 1) / ns);
   (void)hipGetLastError();
   if (fa::launch_kvcache(p, headdim, (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
                          (uint16_t*)v_cache, rotary_cos, rotary_sin, rotary_dim, (uint16_t*)out, stream) != hipSuccess)
     return FA_ERR_LAUNCH;
-  fa::CombineParams c;
-  c.out_partial = out_partial;
-  c.lse_partial = lse_partial;
-  c.out = (uint16_t*)out;
-  c.lse = lse;
-  c.batch = batch;
-  c.seqlen_q = seqlen_q;
-  c.nheads = nheads;
-  c.num_splits = ns;
-  c.f16 = p.f16;
-  return fa::launch_combine(c, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_combine(c, headdim, stream));
 }
 
 int fa_combine(const float* out_partial, const float* lse_partial, void* out, float* lse, int batch,
                int seqlen_q, int nheads, int headdim, int num_splits, int dtype, hipStream_t stream) {
-  if (!out_partial || !lse_partial || !out || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(out_partial) || !aligned16(out)) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_INVALID_ARG;
-  if (batch < 1 || seqlen_q < 1 || nheads < 1 || headdim < 1 || num_splits < 1) return FA_ERR_INVALID_ARG;
-  if (seqlen_q > kMaxSeqlen) return FA_ERR_INVALID_ARG;
-  if (!headdim_supported(headdim)) return FA_ERR_UNSUPPORTED;
-  if (elems4(num_splits, batch, (long long)nheads * seqlen_q, headdim) < 0) return FA_ERR_INVALID_ARG;
-  const long rows = (long)batch * nheads * seqlen_q;
-  if (rows > kMaxBlocks) return FA_ERR_INVALID_ARG;  // one workgroup per row
   fa::CombineParams p;
-  p.out_partial = out_partial;
-  p.lse_partial = lse_partial;
-  p.out = (uint16_t*)out;
-  p.lse = lse;
-  p.batch = batch;
-  p.seqlen_q = seqlen_q;
-  p.nheads = nheads;
-  p.num_splits = num_splits;
-  p.f16 = dtype == FA_FP16 ? 1 : 0;
+  const int st = fa::plan_combine(out_partial, lse_partial, out, lse, batch, seqlen_q, nheads, headdim, num_splits,
+                                  dtype, &p);
+  if (st != FA_OK) return st;
   (void)hipGetLastError();
-  return fa::launch_combine(p, headdim, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_combine(p, headdim, stream));
 }
 
 const char* fa_status_str(int status) {

@@ -16,9 +16,12 @@ static hipError_t launch_bwd_hd(const BwdParams& p, hipStream_t stream) {
     pd.seqlen_q = (int)p.lse_head_stride;
   }
   const long rows = (long)pd.batch * pd.seqlen_q * pd.nheads;
-  constexpr int rows_per_block = 4 * (64 / (HD / 8));
+  const int rows_per_block = delta_rows_per_block(HD);
   hipLaunchKernelGGL((delta_kernel<HD, E>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
                      0, stream, pd, rows);
+  // dK/dV must not run on a delta that was never written
+  const hipError_t ed = hipGetLastError();
+  if (ed != hipSuccess) return ed;
   const bool alibi = p.alibi != nullptr;
   const int kv_items = p.batch * p.nheads_k * p.num_k_tiles;
   if (alibi)

@@ -34,40 +34,7 @@
 
 namespace fa {
 
-// Backward problem description, filled on the host.  Sizes are in elements.
-struct BwdParams {
-  const uint16_t* q;      // bf16/fp16 [B, Sq, H, D]
-  const uint16_t* k;      // bf16/fp16 [B, Sk, H_k, D]
-  const uint16_t* v;      // bf16/fp16 [B, Sk, H_k, D]
-  const uint16_t* out;    // bf16/fp16 [B, Sq, H, D]  forward output
-  const uint16_t* dout;   // bf16/fp16 [B, Sq, H, D]  upstream gradient
-  const float* lse;       // fp32 [B, H, Sq]     forward logsumexp (natural log)
-  float* delta;           // fp32 [B, H, Sq]     D, written by delta_kernel
-  uint16_t* dq;           // bf16/fp16 [B, Sq, H, D]
-  uint16_t* dk;           // bf16/fp16 [B, Sk, H_k, D]
-  uint16_t* dv;           // bf16/fp16 [B, Sk, H_k, D]
-  // Packed batch (cu_q != nullptr): sequence b owns q/dout/dq rows [cu_q[b], cu_q[b+1])
-  // and k/v/dk/dv rows [cu_k[b], cu_k[b+1]) of [total, heads, D] tensors; lse and delta
-  // are [H, total_q] (lse_head_stride = total_q); seqlen_q/seqlen_k are the maxima.
-  const int* cu_q;
-  const int* cu_k;
-  long lse_head_stride;
-  int nheads_k;           // K/V heads; query head h uses K/V head h / (nheads / nheads_k)
-  const float* alibi;     // fp32 [H] or [B, H], or nullptr
-  int alibi_bstride;      // 0: one slope per head for every batch; nheads: [B, H]
-  int f16;                // 1: every 16-bit tensor is fp16, 0: bf16
-  int batch, seqlen_q, seqlen_k, nheads;
-  float scale;            // softmax_scale as given
-  float scale_log2;       // |scale| * log2(e), or 1 when scale == 0
-  uint32_t q_and;         // 0 when scale == 0 (the scores are then the bias alone)
-  uint32_t q_sign;        // 0x80008000 when scale < 0, else 0
-  int window_left, window_right;  // -1 = unbounded; window_right already 0 when causal
-  int num_q_tiles;        // ceil(Sq / 128): dq workgroups per (batch, head)
-  int num_k_tiles;        // ceil(Sk / 128): dkdv workgroups per (batch, head)
-};
-
 constexpr int BWD_NW = 4;        // waves per workgroup
-constexpr int BWD_ROWS = 128;    // rows (queries or keys) a workgroup owns: 32 per wave
 constexpr int DQ_TILE = 64;      // keys per streamed tile (dq kernel)
 // Queries per streamed tile (dkdv kernel).  Headdim 128 takes 64 (two independent
 // 32-query blocks per wave: the kernel runs one wave per SIMD there, so it has the

@@ -1,9 +1,12 @@
-// fa_common.h - device types, parameter blocks and small helpers shared by the
-// gfx950 attention kernels.  Internal to the library (not part of the C ABI).
+// fa_common.h - device types and small helpers shared by the gfx950 attention
+// kernels (the parameter blocks are in fa_params.h).  Internal to the library (not
+// part of the C ABI).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "fa_params.h"
 
 namespace fa {
 
@@ -24,56 +27,8 @@ using x8 = E __attribute__((ext_vector_type(8)));
 template <typename E>
 using x2 = E __attribute__((ext_vector_type(2)));
 
-// Matrix-core forward: query rows per workgroup of the default four-wave launch
-// (the eight-wave launch recounts its 256-row tiles itself).
-constexpr int FWD_BLOCK_ROWS = 128;
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// Forward problem description, filled on the host.  Sizes are in elements.
-struct FwdParams {
-  const uint16_t* q;      // bf16 [B, Sq, H, D]
-  const uint16_t* k;      // bf16 [B, Sk, H, D]
-  const uint16_t* v;      // bf16 [B, Sk, H, D]
-  void* out;              // bf16 [B, Sq, H, D]  or fp32 [S, B, H, Sq, D] (split mode)
-  float* lse;             // fp32 [B, H, Sq]     or fp32 [S, B, H, Sq]    (split mode)
-  const float* alibi;     // fp32 ALiBi slopes [H] or [B, H], or nullptr
-  int alibi_bstride;      // 0: one slope per head for every batch; nheads: [B, H]
-  int f16;                // 1: q/k/v/out are fp16, 0: bf16
-  int batch, seqlen_q, seqlen_k, nheads;  // varlen: seqlen_q/k are the maximum lengths
-  int nheads_k;           // K/V heads; query head h reads K/V head h / (nheads / nheads_k)
-  const int* cu_q;        // varlen: [batch + 1] first q/out row of each sequence, or nullptr
-  const int* cu_k;        // varlen: [batch + 1] first k/v row of each sequence, or nullptr
-  long lse_head_stride;   // varlen: total_q, lse being [nheads, total_q]
-  float scale_log2;       // |softmax_scale| * log2(e), or 1 when softmax_scale == 0
-  uint32_t q_and;         // 0 when softmax_scale == 0 (Q is zeroed on load), else all ones
-  uint32_t q_sign;        // 0x80008000 when softmax_scale < 0 (Q is negated on load), else 0
-  int window_left;        // -1 = unbounded
-  int window_right;       // -1 = unbounded; already 0 when causal
-  int num_q_tiles;        // ceil(Sq / 128)
-  int num_splits;         // 1 for the plain forward
-  int split_len;          // keys per split (ceil(Sk / num_splits))
-  int reverse_q;          // 1: visit the heaviest query tiles first (causal)
-  // KV-cache decode (fa_fwd_kvcache); cache_seqlens is nullptr otherwise
-  const int* cache_seqlens;  // [batch] rows already in the cache
-  const int* block_table;    // [batch, max_blocks] physical block of each logical block, or
-                             // nullptr: contiguous cache, block b holds sequence b
-  int page_size;             // rows per block (the per-sequence capacity when contiguous)
-  int page_shift;            // log2(page_size) when paged
-  int max_blocks;            // row length of block_table
-  int seqlen_new;            // rows appended to every sequence before the attention
-};
-
-// Combine description.
-struct CombineParams {
-  const float* out_partial;  // [S, B, H, Sq, D]
-  const float* lse_partial;  // [S, B, H, Sq]
-  uint16_t* out;             // bf16 or fp16 [B, Sq, H, D]
-  float* lse;                // [B, H, Sq]
-  int batch, seqlen_q, nheads, num_splits;
-  int f16;                   // 1: out is fp16, 0: bf16
-};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -21,14 +21,10 @@
 
 namespace fa {
 
-constexpr int DEC_THREADS = 256;
-#ifndef FA_DEC_UNROLL
-#define FA_DEC_UNROLL 8
-#endif
+constexpr int DEC_THREADS = BLOCK_THREADS;
 #ifndef FA_DEC_CPOL
 #define FA_DEC_CPOL 2
 #endif
-constexpr int DEC_UNROLL = FA_DEC_UNROLL;  // key rows per lane per step
 constexpr int DEC_CPOL = FA_DEC_CPOL;      // KV loads are non-temporal (read once, streamed)
 
 // Helpers of the grouped kernel.  Dot product of 8 packed 16-bit values (two 16-byte
@@ -429,9 +425,6 @@ static void launch_group(const FwdParams& p, hipStream_t stream) {
                      stream, p);
 }
 
-// Queries one decode workgroup serves when a K/V head has nq_total of them.
-int decode_queries_per_block(int nq_total) { return nq_total <= 1 ? 1 : nq_total <= 2 ? 2 : nq_total <= 4 ? 4 : 8; }
-
 template <int HD, bool ALIBI, bool KVC, typename E>
 static void launch_group_nq(const FwdParams& p, hipStream_t stream) {
   switch (decode_queries_per_block(p.nheads / p.nheads_k * p.seqlen_q)) {
@@ -493,10 +486,6 @@ hipError_t launch_kvcache(const FwdParams& p, int headdim, const uint16_t* k_new
   return p.f16 ? launch_kvcache_e<_Float16>(p, headdim, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream)
                : launch_kvcache_e<__bf16>(p, headdim, k_new, v_new, k_cache, v_cache, cos, sin, rd, qrot, stream);
 }
-
-// Key rows one decode step covers per wave (blocks of a paged cache must hold a whole
-// number of them): DEC_UNROLL * 64 / (headdim / 8).
-int decode_step_keys(int headdim) { return DEC_UNROLL * 64 / (headdim / 8); }
 
 template <typename E>
 static hipError_t launch_decode_e(const FwdParams& p, int headdim, hipStream_t stream) {

@@ -830,11 +830,6 @@ hipError_t launch_fwd_instance(const FwdParams& p, long nblocks, hipStream_t str
   return hipGetLastError();
 }
 
-// Eight waves per workgroup for headdim 128 with neither causal mask nor window and
-// at least 4096 query rows; four otherwise.
-inline int fwd_waves(const FwdParams& p, int hd, bool split) {
-  return (hd == 128 && !split && p.window_left < 0 && p.window_right < 0 && p.seqlen_q >= 4096) ? 8 : 4;
-}
 
 // One translation unit per head dimension instantiates these (separate files let
 // each get its own register-allocation flags).  The caller sets num_q_tiles for
@@ -843,7 +838,7 @@ template <int HD>
 hipError_t launch_fwd_hd(const FwdParams& p, bool split, hipStream_t stream) {
   const bool alibi = p.alibi != nullptr;
   if constexpr (HD == 128) {
-    if (fwd_waves(p, HD, split) == 8) {
+    if (fwd_waves(HD, split, p.window_left, p.window_right, p.seqlen_q) == 8) {
       FwdParams p8 = p;
       p8.num_q_tiles = (p.seqlen_q + 255) / 256;
       const long nblocks = (long)p8.batch * p8.nheads * p8.num_q_tiles;
@@ -863,13 +858,12 @@ hipError_t launch_fwd_d128(const FwdParams& p, bool split, hipStream_t stream);
 hipError_t launch_fwd_d256(const FwdParams& p, bool split, hipStream_t stream);
 
 // The matrix-core decode form (fwd_decode_kernel) for a KV-cache step whose K/V heads
-// each serve nq_total = (nheads / nheads_k) * seqlen_q > 4 queries, headdim 64 or 128.
-// Up to four queries the vector-ALU kernel streams the cache faster (paged 32k-key
-// caches, batch 8: 5.45 against 4.65 TB/s at four queries per K/V head); from eight on
-// it falls behind (3.0 against 4.8 TB/s at eight, 1.5 against 3.6 at sixteen).  The
-// caller passes split_len as a multiple of BC (so a tile never crosses a cache block)
-// and the split partials as out / lse.
-inline bool decode_uses_mfma(int headdim, int nq_total) { return headdim != 256 && nq_total > 4; }
+// each serve nq_total = (nheads / nheads_k) * seqlen_q > 4 queries, headdim 64 or 128
+// (decode_uses_mfma).  Up to four queries the vector-ALU kernel streams the cache
+// faster (paged 32k-key caches, batch 8: 5.45 against 4.65 TB/s at four queries per
+// K/V head); from eight on it falls behind (3.0 against 4.8 TB/s at eight, 1.5 against
+// 3.6 at sixteen).  The caller passes split_len as a multiple of BC (so a tile never
+// crosses a cache block) and the split partials as out / lse.
 
 template <int HD>
 hipError_t launch_fwd_decode_hd(const FwdParams& p, hipStream_t stream) {

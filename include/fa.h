@@ -62,8 +62,12 @@
  *                            not 16-byte aligned, a size < 1, a window side < -1,
  *                            num_splits outside [1, seqlen_k], a non-finite softmax_scale,
  *                            a dtype other than FA_BF16 / FA_FP16, alibi_per_batch
- *                            other than 0 / 1, or a problem whose element count
- *                            overflows 64-bit indexing;
+ *                            other than 0 / 1, a problem whose element count
+ *                            overflows 64-bit indexing, or a call one of whose
+ *                            kernel grids would exceed the runtime's 2^32 - 1
+ *                            work-items (2^24 - 1 workgroups of 256 threads; the
+ *                            eight-wave headdim-128 forward 2^23 - 1 of 512); every
+ *                            grid of a call is checked before its first launch;
  *   FA_ERR_UNSUPPORTED (-2): headdim not in {64, 128, 256}, or nheads * headdim > 2^22;
  *   FA_ERR_LAUNCH      (-3): the HIP runtime reported an error for the launch.
  *   No exception crosses the ABI and nothing is printed.
@@ -183,7 +187,9 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
  *   k_new, v_new [batch, seqlen_new, nheads_k, headdim] dtype (device, read) or NULL when
  *       seqlen_new = 0: appended at rows cache_seqlens[b] .. + seqlen_new - 1 (written into
  *       the cache before the attention reads it).
- *   rotary_cos, rotary_sin [positions, rotary_dim / 2] fp32 (device, read) or both NULL:
+ *   rotary_cos, rotary_sin [positions, rotary_dim / 2] fp32 (device, read) or both NULL,
+ *       with a row for every cache position (positions >= the capacity: page_size *
+ *       max_blocks_per_seq, or page_size for a contiguous cache):
  *       query row i and new key row i are rotated at position cache_seqlens[b] + i, pairs
  *       (x_d, x_{d + rotary_dim/2}) for d < rotary_dim / 2 (rotary_dim even, <= headdim);
  *       the rotated keys are stored in the cache, rounded to dtype.
@@ -198,7 +204,8 @@ int fa_combine(const float* out_partial, const float* lse_partial, void* out, fl
  * h / (nheads / nheads_k).  Device-side values (cache_seqlens, block_table, rotary
  * positions) cannot be checked on the host: they must stay inside the buffers.
  * Errors as for fa_fwd, plus FA_ERR_INVALID_ARG for NULL required pointers, seqlen_q
- * outside [1, 8], an invalid page_size, rotary_dim, num_splits or head grouping.
+ * outside [1, 8], an invalid page_size, rotary_dim, num_splits or head grouping, or
+ * seqlen_new larger than the capacity.
  */
 int fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
                    const int* block_table, int page_size, int max_blocks_per_seq,

@@ -181,3 +181,32 @@ def test_binding_requires_gpu_tensors():
         fa.flash_attn_func(q.float(), q, q)
     with pytest.raises(TypeError):  # one element type for q, k and v
         fa.flash_attn_func(q, q.half(), q)
+
+
+# Grids: a launch's work-item count (workgroups x threads) must fit in 32 bits, so
+# 2^24 workgroups of 256 threads (or 2^23 of the eight-wave forward's 512) are one past
+# the limit.  Each call below needs exactly one grid past it and is rejected before any
+# HIP call.
+@pytest.mark.parametrize("entry,over", [
+    ("fwd", dict(batch=1 << 17, seqlen_q=128, seqlen_k=128, nheads=128, headdim=64)),  # 2^24 four-wave groups
+    ("fwd", dict(batch=493448, seqlen_q=4224, seqlen_k=4224, nheads=1, headdim=128)),  # 8388616 eight-wave groups
+    ("combine", dict(seqlen_q=1 << 24)),                                             # one workgroup per row
+    ("bwd", dict(seqlen_q=(1 << 24) * 8, seqlen_k=64, nheads=1, headdim=256)),       # delta: 8 rows per group
+    ("bwd", dict(seqlen_q=(1 << 24) * 16, seqlen_k=64, nheads=1, headdim=128)),      # delta: 16 rows per group
+    ("bwd", dict(seqlen_q=(1 << 24) * 32, seqlen_k=64, nheads=1, headdim=64)),       # delta: 32 rows per group
+    ("kvcache", dict(batch=1 << 21, nheads=8, nheads_k=8, num_splits=1, table=None, page=256)),  # combine rows
+    ("splitkv", dict(batch=1 << 16, seqlen_q=1, seqlen_k=64, nheads=16, headdim=64)),  # decode workgroups (16 splits)
+])
+def test_grid_just_past_limit_rejected(lib, entry, over):
+    if entry == "fwd":
+        assert lib.fa_fwd(*fwd_args(**over)) == -1
+    elif entry == "splitkv":
+        a = fwd_args(**over)
+        a.insert(17, 16)
+        assert lib.fa_fwd_splitkv(*a) == -1
+    elif entry == "combine":
+        assert lib.fa_combine(FAKE, FAKE, FAKE, FAKE, 1, over["seqlen_q"], 1, 64, 2, 0, None) == -1
+    elif entry == "bwd":
+        assert lib.fa_bwd(*bwd_args(**over)) == -1
+    else:
+        assert lib.fa_fwd_kvcache(*kvc_args(**over)) == -1

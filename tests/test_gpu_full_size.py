@@ -15,7 +15,7 @@ import torch
 
 import exact_attention_56_amd as fa
 import oracle
-from exact_attention_56_amd.inputs import WORKLOADS, workload_inputs
+from exact_attention_56_amd.inputs import VARLEN_GQA, WORKLOADS, make_varlen_qkv, sweep_workload, workload_inputs
 from tests.parity import check_lse, check_out
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -37,9 +37,14 @@ def sample_rows(w, seed):
     return sorted(samples)
 
 
-@pytest.mark.parametrize("name", [n for n in WORKLOADS])
+# the benchmark's seqlen sweep (16 heads x 128, batch 16384 / seqlen, non-causal): from
+# 4096 query rows these run the eight-wave headdim-128 launch
+SWEEP = {f"sweep_s{s}": sweep_workload(s) for s in (4096, 8192, 16384)}
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS] + list(SWEEP))
 def test_full_size_sampled(name):
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if name in WORKLOADS else SWEEP[name]
     print(f"[case] full size {name}: {w}", file=sys.stderr, flush=True)
     q, k, v, slopes = workload_inputs(w)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -70,9 +75,20 @@ def test_full_size_sampled(name):
     check_out(got_out, ref_out)
 
 
-@pytest.mark.parametrize("name", ["bench_s2048", "bench_s2048_causal", "local_alibi_s8192"])
-def test_full_size_backward_heads(name):
-    """fa_bwd at the full workload size; two whole (batch, head) slices are compared with
+BWD_HEADS = {"bench_s2048": [(0, 0), (7, 15)], "bench_s2048_causal": [(0, 0), (7, 15)],
+             "local_alibi_s8192": [(0, 0), (1, 31)]}
+
+
+def _bwd_cases():
+    cases = [(n, heads) for n, heads in BWD_HEADS.items()]
+    # headdim 256 at 16k: one head per case (about 12 s of fp64 oracle work each)
+    cases += [("hd256_s16384", [(0, 0)]), ("hd256_s16384", [(0, 7)])]
+    return cases
+
+
+@pytest.mark.parametrize("name,heads", _bwd_cases(), ids=lambda x: str(x).replace(" ", ""))
+def test_full_size_backward_heads(name, heads):
+    """fa_bwd at the full workload size; whole (batch, head) slices are compared with
     the exact oracle gradient of that head alone (heads are independent problems)."""
     from tests.test_gpu_backward import GRAD_REL
     w = WORKLOADS[name]
@@ -87,7 +103,7 @@ def test_full_size_backward_heads(name):
     torch.cuda.synchronize()
     for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         assert bool(torch.isfinite(t).all()), f"{nm}: non-finite or unwritten values"
-    for b, h in [(0, 0), (w.batch - 1, w.nheads - 1)]:
+    for b, h in heads:
         sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
         hs = None if slopes is None else slopes[h:h + 1]
         rq, rk, rv = oracle.attention_backward(q[sl], k[sl], v[sl], dout[sl], w.softmax_scale, w.causal,
@@ -98,3 +114,64 @@ def test_full_size_backward_heads(name):
             bound = GRAD_REL * float(np.abs(ref).max())
             print(f"[case]   head ({b},{h}) {nm}: max err {err:.3e}, bound {bound:.3e}", file=sys.stderr, flush=True)
             assert err <= bound, f"{nm} of head ({b},{h}): max err {err:.3e} > {bound:.3e}"
+
+
+# sequences of the packed grouped-head workload whose rows are compared in full: the
+# shortest, a middle one and the longest (each an attention problem of its own)
+def _varlen_pick(lengths):
+    order = sorted(range(len(lengths)), key=lambda i: lengths[i])
+    return [order[0], order[len(order) // 2], order[-1]]
+
+
+def test_full_size_varlen_gqa():
+    """fa_fwd_varlen on the whole packed grouped-head workload (16 causal sequences,
+    27 290 tokens, 32 query heads over 8 K/V heads x 128), as the benchmark launches it;
+    every row of three sequences is compared with the oracle run on that sequence alone."""
+    w = VARLEN_GQA
+    print(f"[case] full-size varlen forward {w.name}", file=sys.stderr, flush=True)
+    q, k, v, cu = make_varlen_qkv(w)
+    mx = max(w.lengths)
+    qd, kd, vd, cud = q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.nheads, q.shape[0]), float("nan"), device=DEV)
+    fa.fwd_varlen(qd, kd, vd, out, lse, cud, cud, mx, mx, w.softmax_scale, w.causal)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()), "unwritten or non-finite output"
+    out_c, lse_c = out.cpu(), lse.cpu()
+    for b in _varlen_pick(w.lengths):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        print(f"[case]   sequence {b}: {s1 - s0} tokens", file=sys.stderr, flush=True)
+        ro, rl = oracle.attention_varlen(q[s0:s1], k[s0:s1], v[s0:s1], [0, s1 - s0], [0, s1 - s0], w.softmax_scale,
+                                         w.causal)
+        check_lse(lse_c[:, s0:s1], rl)
+        check_out(out_c[s0:s1], ro)
+
+
+def test_full_size_backward_varlen_gqa():
+    """fa_bwd_varlen on the whole packed grouped-head workload, as the benchmark launches
+    it; the gradients of three whole sequences (dk, dv summed over each K/V head's group)
+    are compared with the oracle gradient of that sequence alone."""
+    from tests.test_gpu_backward import GRAD_REL
+    w = VARLEN_GQA
+    print(f"[case] full-size varlen backward {w.name}", file=sys.stderr, flush=True)
+    q, k, v, cu = make_varlen_qkv(w)
+    mx = max(w.lengths)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed + 100)).to(torch.bfloat16)
+    qd, kd, vd, gd, cud = q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), cu.to(DEV)
+    out, lse = fa.flash_attn_varlen_func(qd, kd, vd, cud, cud, mx, mx, w.softmax_scale, w.causal)
+    dq, dk, dv = fa.attention_varlen_backward(qd, kd, vd, out, lse, gd, cud, cud, mx, mx, w.softmax_scale, w.causal)
+    torch.cuda.synchronize()
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert bool(torch.isfinite(t).all()), f"{nm}: non-finite or unwritten values"
+    got = {"dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+    for b in _varlen_pick(w.lengths):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        ref = oracle.attention_backward_varlen(q[s0:s1], k[s0:s1], v[s0:s1], dout[s0:s1], [0, s1 - s0],
+                                               [0, s1 - s0], w.softmax_scale, w.causal)
+        for r, nm in zip(ref, ("dq", "dk", "dv")):
+            g = got[nm][s0:s1].double().numpy()
+            err = float(np.abs(g - r).max())
+            bound = GRAD_REL * float(np.abs(r).max())
+            print(f"[case]   sequence {b} ({s1 - s0} tokens) {nm}: max err {err:.3e}, bound {bound:.3e}",
+                  file=sys.stderr, flush=True)
+            assert err <= bound, f"{nm} of sequence {b}: max err {err:.3e} > {bound:.3e}"
