@@ -19,6 +19,7 @@ Functions
   combine(out_partial, lse_partial, out, lse)
   decode(q, k_cache, v_cache, num_splits=16, ...) -> (out, lse)
   kvcache_decode(q, k_cache, v_cache, cache_seqlens, ...) -> (out, lse)   KV-cache decode step
+  fwd_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse, ...)  the same step, no allocation
   bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, ...)   gradients into preallocated tensors
   attention_backward(q, k, v, out, lse, dout, ...) -> (dq, dk, dv)
 """
@@ -65,6 +66,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, i, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i,
                                    i, f, i, i, i, vp, i, i, i, vp]
     lib.fa_fwd_kvcache.restype = i
+    lib.fa_fwd_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, i, vp, vp, i, vp, vp, i, i, i, i, i, f,
+                                           i, i, i, vp, i, i, i, vp]
+    lib.fa_fwd_kvcache_noalloc.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i,
@@ -354,11 +358,10 @@ def kvcache_decode(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=N
     return out, lse
 
 
-def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_partial, block_table=None, k_new=None,
-                v_new=None, rotary_cos=None, rotary_sin=None, softmax_scale=None, causal=False, window_size=(-1, -1),
-                alibi_slopes=None, num_splits=0) -> None:
-    """fa_fwd_kvcache with preallocated out [B,Sq,H,D], lse [B,H,Sq] and split scratch
-    out_partial [S,B,H,Sq,D] / lse_partial [S,B,H,Sq] (fp32; S = max_splits)."""
+def _kvcache_common(q, k_cache, v_cache, cache_seqlens, out, lse, block_table, k_new, v_new, rotary_cos,
+                    rotary_sin, alibi_slopes):
+    """Checks shared by the KV-cache entry points; returns (b, sq, h, d, hk, page,
+    max_blocks, snew, rd, slopes, per_batch)."""
     _dtype_code(q, "q")
     _require(q, "q", q.dtype, 4)
     _require(k_cache, "k_cache", q.dtype, 4, q.device)
@@ -401,16 +404,40 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_p
     slopes, per_batch = _alibi(alibi_slopes, b, h, q.device)
     _require(out, "out", q.dtype, 4, q.device)
     _require(lse, "lse", torch.float32, 3, q.device)
+    if out.shape != q.shape or tuple(lse.shape) != (b, h, sq):
+        raise ValueError("out/lse do not match q")
+    return b, sq, h, d, hk, page, max_blocks, snew, rd, slopes, per_batch
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, out, lse, out_partial, lse_partial, block_table=None, k_new=None,
+                v_new=None, rotary_cos=None, rotary_sin=None, softmax_scale=None, causal=False, window_size=(-1, -1),
+                alibi_slopes=None, num_splits=0) -> None:
+    """fa_fwd_kvcache with preallocated out [B,Sq,H,D], lse [B,H,Sq] and split scratch
+    out_partial [S,B,H,Sq,D] / lse_partial [S,B,H,Sq] (fp32; S = max_splits)."""
+    b, sq, h, d, hk, page, max_blocks, snew, rd, slopes, per_batch = _kvcache_common(
+        q, k_cache, v_cache, cache_seqlens, out, lse, block_table, k_new, v_new, rotary_cos, rotary_sin, alibi_slopes)
     _require(out_partial, "out_partial", torch.float32, 5, q.device)
     _require(lse_partial, "lse_partial", torch.float32, 4, q.device)
     max_splits = out_partial.shape[0]
-    if out.shape != q.shape or tuple(lse.shape) != (b, h, sq) or tuple(out_partial.shape[1:]) != (b, h, sq, d) or \
-            tuple(lse_partial.shape) != (max_splits, b, h, sq):
-        raise ValueError("out/lse/partials do not match q")
-    op, lp = out_partial, lse_partial
+    if tuple(out_partial.shape[1:]) != (b, h, sq, d) or tuple(lse_partial.shape) != (max_splits, b, h, sq):
+        raise ValueError("the partials do not match q")
     _check(load_library().fa_fwd_kvcache(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(), _ptr(block_table), page,
         max_blocks, _ptr(k_new), _ptr(v_new), snew, _ptr(rotary_cos), _ptr(rotary_sin), rd, out.data_ptr(),
-        lse.data_ptr(), op.data_ptr(), lp.data_ptr(), int(max_splits), b, sq, h, hk, d, _scale(softmax_scale, d),
-        int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype],
-        int(num_splits), _stream_handle(q)))
+        lse.data_ptr(), out_partial.data_ptr(), lse_partial.data_ptr(), int(max_splits), b, sq, h, hk, d,
+        _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(slopes), per_batch,
+        _DTYPES[q.dtype], int(num_splits), _stream_handle(q)))
+
+
+def fwd_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse, block_table=None, k_new=None, v_new=None,
+                        rotary_cos=None, rotary_sin=None, softmax_scale=None, causal=False, window_size=(-1, -1),
+                        alibi_slopes=None, num_splits=0) -> None:
+    """fa_fwd_kvcache_noalloc: fwd_kvcache with the split partials in the library's own
+    device buffer (no allocation by the call; overlapping calls on one GPU race)."""
+    b, sq, h, d, hk, page, max_blocks, snew, rd, slopes, per_batch = _kvcache_common(
+        q, k_cache, v_cache, cache_seqlens, out, lse, block_table, k_new, v_new, rotary_cos, rotary_sin, alibi_slopes)
+    _check(load_library().fa_fwd_kvcache_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_seqlens.data_ptr(), _ptr(block_table), page,
+        max_blocks, _ptr(k_new), _ptr(v_new), snew, _ptr(rotary_cos), _ptr(rotary_sin), rd, out.data_ptr(),
+        lse.data_ptr(), b, sq, h, hk, d, _scale(softmax_scale, d), int(bool(causal)), int(window_size[0]),
+        int(window_size[1]), _ptr(slopes), per_batch, _DTYPES[q.dtype], int(num_splits), _stream_handle(q)))

@@ -33,6 +33,7 @@ SOURCES = [
     ("fa_bwd.hip", []),
     ("fa_decode_kernel.hip", []),
     ("fa_api.hip", []),
+    ("fa_noalloc.hip", []),
 ]
 # host-only C++ (argument validation and launch planning): compiled by the host compiler
 HOST_SOURCES = ["fa_validate.cpp"]

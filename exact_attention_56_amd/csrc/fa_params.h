@@ -122,6 +122,10 @@ inline int decode_step_keys(int headdim) { return DEC_UNROLL * 64 / (headdim / 8
 // per row.
 inline int delta_rows_per_block(int headdim) { return 4 * (64 / (headdim / 8)); }
 
+// Size of the device buffer that holds the split partials of fa_fwd_kvcache_noalloc
+// (one per GPU, for the life of the process).
+#define FA_NOALLOC_SCRATCH_BYTES (16LL << 20)
+
 // A grid's work-item count (workgroups x threads) must fit in 32 bits on this runtime.
 inline long long max_grid_blocks(int threads) { return 0xffffffffLL / threads; }
 

@@ -2,6 +2,7 @@
 // (declared in fa_validate.h).  Plain C++: no HIP calls, no device memory touched.
 #include "fa_validate.h"
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -321,6 +322,14 @@ int plan_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cac
   c->num_splits = ns;
   c->f16 = p->f16;
   return FA_OK;
+}
+
+int scratch_max_splits(int batch, int nheads, int seqlen_q, int headdim, long long bytes) {
+  if (batch < 1 || nheads < 1 || seqlen_q < 1 || headdim < 1 || bytes < 1) return 0;
+  const long long row_bytes = 4LL * headdim + 4;  // one partial row and its lse
+  const long long rows = elems4(batch, nheads, seqlen_q, 1);
+  if (rows < 0 || rows > bytes / row_bytes) return 0;
+  return (int)std::min<long long>(INT_MAX, bytes / (rows * row_bytes));
 }
 
 int plan_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,

@@ -42,6 +42,10 @@ int plan_fwd_kvcache(const void* q, void* k_cache, void* v_cache, const int* cac
                      const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits, FwdParams* p,
                      CombineParams* c);
 
+// Most splits whose partials (fp32 out [S, B, H, Sq, D] followed by lse [S, B, H, Sq])
+// fit in `bytes`; 0 when not even one split fits or a size is not positive.
+int scratch_max_splits(int batch, int nheads, int seqlen_q, int headdim, long long bytes);
+
 int plan_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, float* delta, int batch, int seqlen_q, int seqlen_k, int nheads,
              int headdim, float softmax_scale, int causal, int window_left, int window_right,

@@ -269,6 +269,32 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
                   float softmax_scale, int causal, int window_left, int window_right,
                   const float* alibi_slopes, int alibi_per_batch, int dtype, hipStream_t stream);
 
+/*
+ * fa_fwd_kvcache_noalloc - fa_fwd_kvcache for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and results, without out_partial,
+ * lse_partial and max_splits.  The split partials live in a device buffer the
+ * library holds, 16 MiB per GPU (FA_NOALLOC_SCRATCH_BYTES), for the life of the
+ * process; the call itself allocates nothing.  At most
+ *     floor(16 MiB / (batch * nheads * seqlen_q * (4 * headdim + 4)))
+ * splits fit (e.g. 254 for batch 8, 16 heads, one query row, headdim 128):
+ * num_splits = 0 caps the automatic count there, a larger explicit num_splits, or a
+ * step whose single split does not fit, returns FA_ERR_INVALID_ARG.  The buffer of a
+ * GPU is looked up on the first call that runs there (on the device of `stream`).
+ * All calls on one GPU share it: calls that overlap in time on one GPU (on two
+ * streams, or from two host threads) race, and must be ordered by the caller.
+ * FA_ERR_LAUNCH also reports a failed lookup of the buffer.
+ */
+int fa_fwd_kvcache_noalloc(const void* q, void* k_cache, void* v_cache, const int* cache_seqlens,
+                           const int* block_table, int page_size, int max_blocks_per_seq,
+                           const void* k_new, const void* v_new, int seqlen_new,
+                           const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                           void* out, float* lse,
+                           int batch, int seqlen_q, int nheads, int nheads_k, int headdim,
+                           float softmax_scale, int causal, int window_left, int window_right,
+                           const float* alibi_slopes, int alibi_per_batch, int dtype, int num_splits,
+                           hipStream_t stream);
+
 /* fa_status_str - static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

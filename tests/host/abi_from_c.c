@@ -110,6 +110,14 @@ int main(void) {
   EXPECT(fa_fwd_kvcache(P, P, P, I, NULL, 256, 1, NULL, NULL, 0, NULL, NULL, 0, P, F, F, F, 16, 1 << 21, 1, 8, 8,
                         64, 0.1f, 1, -1, -1, NULL, 0, FA_BF16, 1, s), FA_ERR_INVALID_ARG);
 
+  /* fa_fwd_kvcache_noalloc: 2032 splits of batch 2 x 8 heads x headdim 128 fit its buffer */
+  EXPECT(fa_fwd_kvcache_noalloc(P, P, P, NULL, I, 256, 4, NULL, NULL, 0, NULL, NULL, 0, P, F, 2, 1, 8, 2, 128, 0.1f,
+                                1, -1, -1, NULL, 0, FA_BF16, 0, s), FA_ERR_INVALID_ARG);
+  EXPECT(fa_fwd_kvcache_noalloc(P, P, P, I, I, 256, 4, NULL, NULL, 0, NULL, NULL, 0, P, F, 2, 1, 8, 2, 128, 0.1f,
+                                1, -1, -1, NULL, 0, FA_BF16, 2033, s), FA_ERR_INVALID_ARG);
+  EXPECT(fa_fwd_kvcache_noalloc(P, P, P, I, I, 256, 4, NULL, NULL, 0, NULL, NULL, 0, P, F, 1 << 20, 1, 8, 2, 128,
+                                0.1f, 1, -1, -1, NULL, 0, FA_BF16, 1, s), FA_ERR_INVALID_ARG);
+
   /* fa_bwd */
   EXPECT(fa_bwd(P, P, P, P, F, P, P, P, P, NULL, 1, 4, 4, 2, 128, 0.125f, 0, -1, -1, NULL, 0, FA_BF16, s),
          FA_ERR_INVALID_ARG);

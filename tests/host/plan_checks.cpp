@@ -125,6 +125,16 @@ static void grid_limits() {
                               1, 1, 64, 0.1f, 1, -1, -1, nullptr, 0, FA_BF16, 1, &p, &c), FA_ERR_INVALID_ARG);
 }
 
+static void scratch_splits() {
+  // 8 x 16 rows of headdim 128: 516 bytes per partial row, 66048 per split
+  EXPECT(fa::scratch_max_splits(8, 16, 1, 128, 16LL << 20), 254);
+  EXPECT(fa::scratch_max_splits(8, 16, 1, 128, 66048), 1);
+  EXPECT(fa::scratch_max_splits(8, 16, 1, 128, 66047), 0);
+  EXPECT(fa::scratch_max_splits(0, 16, 1, 128, 1 << 20), 0);
+  EXPECT(fa::scratch_max_splits(INT_MAX, INT_MAX, 8, 256, 16LL << 20), 0);
+  EXPECT(fa::scratch_max_splits(1, 1, 1, 64, LLONG_MAX), INT_MAX);
+}
+
 static const int kEdge[] = {INT_MIN, -65537, -3, -2, -1, 0, 1, 2, 3, 7, 8, 9, 31, 32, 63, 64, 65, 100, 127, 128, 129,
                             255, 256, 257, 4095, 4096, 65535, 65536, 1 << 20, (1 << 24) - 1, 1 << 24,
                             (1 << 30) - 1, 1 << 30, (1 << 30) + 1, INT_MAX - 1, INT_MAX};
@@ -180,6 +190,7 @@ static void edge_values() {
 int main() {
   derived_fields();
   grid_limits();
+  scratch_splits();
   edge_values();
   if (n_failed) {
     fprintf(stderr, "%d of %d checks failed\n", n_failed, n_checks);

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_varlen", "fa_combine", "fa_fwd", "fa_fwd_kvcache",
-                                    "fa_fwd_splitkv", "fa_fwd_varlen", "fa_status_str"]
+                                    "fa_fwd_kvcache_noalloc", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -210,3 +210,22 @@ def test_grid_just_past_limit_rejected(lib, entry, over):
         assert lib.fa_bwd(*bwd_args(**over)) == -1
     else:
         assert lib.fa_fwd_kvcache(*kvc_args(**over)) == -1
+
+
+def kvc_noalloc_args(**over):
+    a = kvc_args(**over)
+    # fa_fwd_kvcache_noalloc drops out_partial, lse_partial and max_splits
+    del a[15:18]
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lens=None), -1), (dict(out=None), -1), (dict(q=None), -1), (dict(sq=9), -1), (dict(page=100), -1),
+    (dict(nheads_k=3), -1), (dict(cos=FAKE), -1), (dict(headdim=80), -2), (dict(dtype=7), -1),
+    # partials of batch 2 x 8 heads x headdim 128: 2032 splits fit in the 16 MiB buffer, 2033 do not
+    (dict(num_splits=2033), -1),
+    # not even one split fits: 2^20 x 8 rows of headdim 128 need 4 GiB
+    (dict(batch=1 << 20, num_splits=1), -1),
+])
+def test_kvcache_noalloc_rejects_invalid(lib, over, code):
+    assert lib.fa_fwd_kvcache_noalloc(*kvc_noalloc_args(**over)) == code
