@@ -54,22 +54,35 @@ namespace fa {
 // without a mask at seqlen_q >= 4096; everything else uses four.
 constexpr int BC = 64;  // keys per tile
 constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
+// Kernels without ALiBi (headdim 64 and 128) keep the reference maximum without a
+// per-tile row max (refit_reference); 0 takes the row max of every tile instead.
+#ifndef FA_NOMAX
+#define FA_NOMAX 1
+#endif
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: reads as zero
 
 // LDS tiles.  A K row keeps its HD/8 16-byte chunks plus one pad slot (16 lanes
-// reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); a V row
-// keeps two pad slots (the 4 rows that 16 lanes of a transpose read touch land on
-// disjoint 8-bank groups; the two 16-lane groups of one 32-lane half still overlap,
-// a 2-way conflict that a 4-slot pad removes at a measured net loss, its extra loads
-// costing more).  Pad slots are filled with zeros by out-of-range loads.
+// reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); the pad
+// slot is filled with zeros by an out-of-range load.  V is stored in 64-byte column
+// blocks: block db holds columns 32db..32db+31 of the tile's 64 rows, 64 bytes per row,
+// so the 32 lanes that one half of a transpose read serves (4 rows x 32 columns) read
+// 256 contiguous bytes, all 64 banks once, and the tile needs no pad slot.  (Padded
+// rows of HD + 16 columns left a 2-way conflict on every transpose read; HD + 32
+// removed it but its two extra loads per tile cost more than the conflicts.)
 template <int HD, int NW>
 struct Tile {
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static constexpr int CPR = HD / 8;         // 16-byte chunks per K/V row in memory
   static constexpr int KCH = CPR + 1;        // 16-byte slots per K row in LDS
-  static constexpr int VCH = CPR + 2;        // 16-byte slots per V row in LDS
+#ifndef FA_VBLOCK
+#define FA_VBLOCK 1
+#endif
+  // V: with FA_VBLOCK the tile is stored in 64-byte column blocks, [HD / 32][BC rows][4
+  // chunks] (no pad slots, CPR loads per tile); otherwise in padded rows of VCH slots
+  static constexpr int VCH = FA_VBLOCK ? CPR : CPR + 2;  // 1 KiB loads per V tile
   static constexpr int KPITCH = KCH * 16;    // bytes
-  static constexpr int VPITCH = VCH * 16;
+  static constexpr int VPITCH = FA_VBLOCK ? 64 : VCH * 16;  // bytes between V rows (within a block)
+  static constexpr int VBLOCK = FA_VBLOCK ? BC * 64 : 64;   // bytes between 32-column blocks of V
   // 64-lane (1 KiB) direct loads per tile: the tile needs KCH (VCH) of them, load u
   // issued by loading wave u % 4.  A wave skips the loads that would lie wholly past
   // the tile (a wave-uniform test): issuing them as all-zero loads, so that every
@@ -140,8 +153,14 @@ struct KVStream {
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i) {
       const int slot = 64 * (lw + 4 * i) + lane;
-      const int row = slot / T::VCH, ch = slot % T::VCH;
-      voff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
+      if constexpr (FA_VBLOCK) {
+        // slot = (block * BC + row) * 4 + x holds chunk 4 * block + x of the row
+        const int blk = slot / (4 * BC), row = (slot / 4) % BC, x = slot % 4;
+        voff[i] = blk < T::CPR / 4 ? (uint32_t)(row * row_bytes + (4 * blk + x) * 16) : OOB_OFFSET;
+      } else {
+        const int row = slot / T::VCH, ch = slot % T::VCH;
+        voff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(row * row_bytes + ch * 16) : OOB_OFFSET;
+      }
     }
   }
   // tile t starts at key key_lo + t*BC; keys at or past key_hi land as zeros
@@ -232,8 +251,9 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
 template <int HD, typename E>
 __device__ __forceinline__ x8<E> v_operand(const lds_u8* vt, int db, int ci) {
   using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + 16 * ci * T::VPITCH + 64 * db));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (16 * ci + 4) * T::VPITCH + 64 * db));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + 16 * ci * T::VPITCH + T::VBLOCK * db));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + (16 * ci + 4) * T::VPITCH + T::VBLOCK * db));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(x8<E>, both);
@@ -356,6 +376,51 @@ __device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, i
   return to_log2(tile_max(s), cs);
 }
 
+// Reference maximum kept without a per-tile row max (kernels without ALiBi): P(t) is
+// formed against the current reference; only when the tile's exponentials grow past
+// 2^16 in some lane's partial sum (or overflow), which only rising scores cause, or
+// when a row whose reference is still -inf (no visible key so far; its P(t) was formed
+// against 0) sees a visible key, does the tile's exact row max replace the reference, with O
+// and l rescaled and P(t) formed again.  The result is unchanged: O, l and the
+// logsumexp share one reference, whatever it is, and every row with a visible key ends
+// with a finite one.  Returns the new partial sums through lsum0/lsum1.
+template <int HD, typename E>
+__device__ __forceinline__ void refit_reference(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], x8<E> (&pf)[4],
+                                                float cs, float& lsum0, float& lsum1) {
+  bool refit = !(lsum0 + lsum1 <= 65536.f);
+  // a row still without a reference: any visible (finite) score of the tile, even one
+  // whose exponential against 0 underflowed, gives it one
+  if (st.m_run == -INFINITY) refit = refit || lane_max(s_cur) != -INFINITY;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(refit) != 0, 0)) {
+    const float mt = max_with_other_half(to_log2(lane_max(s_cur), cs) + st.b_cur);
+    const float m_new = fmaxf(st.m_run, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    st.m_run = m_new;
+    const float negm2 = (m_new == -INFINITY) ? 0.f : st.b_cur - m_new;
+    lsum0 = 0.f;
+    lsum1 = 0.f;
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+      const int kb = ci >> 1, r0 = 8 * (ci & 1);
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm2));
+        const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm2));
+        pk[e] = pack2<E>(p0, p1);
+        lsum0 += p0;
+        lsum1 += p1;
+      }
+      pf[ci] = __builtin_bit_cast(x8<E>, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    }
+  }
+}
+
 // LDS buffers of the forward loop, as byte addresses.
 struct LdsBufs {
   lds_u8* k[3];        // K tile buffers (NBUF used)
@@ -421,6 +486,10 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
     }
     pf[ci] = __builtin_bit_cast(x8<E>, u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
+  // (not at headdim 256: there the one-wave-per-SIMD kernel with its accumulators in
+  // the AGPRs ran 23% slower with the refit code in the loop)
+  constexpr bool NOMAX = !ALIBI && FA_NOMAX && HD != 256;
+  if constexpr (NOMAX) refit_reference<HD, E>(st, s_cur, pf, cs, lsum0, lsum1);
   // At headdim 256 (one wave per SIMD) keep the row-sum adds in this block, between
   // the products; left alone they sink past the masking branch below.  With two
   // waves per SIMD the sunk adds overlap the other wave's products, which measured
@@ -453,7 +522,7 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   // max of S(t+1) before masking: exact for tiles every row sees in full
   const int j1 = kv.key_lo + (t + 1) * BC;
   float mx = 0.f;  // row max of S(t+1) in log2 units
-  if constexpr (!ALIBI) mx = to_log2(tile_max(s_nxt), cs);
+  if constexpr (!ALIBI && !NOMAX) mx = to_log2(tile_max(s_nxt), cs);
 
   // Issue order: the global loads; LDS operand reads running four products ahead;
   // the S(t+1) products, each followed by two exponentials of tile t and their
@@ -532,9 +601,10 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   }
   st.b_cur = b_nxt;  // tile t's offset was used by P(t) above
 
-  // move the reference maximum only when a row grew by more than 2^8
+  // move the reference maximum only when a row grew by more than 2^8 (without ALiBi,
+  // refit_reference moves it instead, on the next step's exponentials)
   const float m_new = fmaxf(st.m_run, mx);
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > st.m_run + RESCALE_TH) != 0, 0)) {
+  if (!NOMAX && __builtin_expect(__builtin_amdgcn_ballot_w64(m_new > st.m_run + RESCALE_TH) != 0, 0)) {
     // 0 when only m_run is -inf; 1 for a row that has seen no visible key yet
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
     st.l_run *= alpha;
@@ -547,6 +617,166 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   // K(t+2) and V(t+1) (loaded NB-2 steps ago) are in LDS before anyone passes the barrier
   wait_tile_loads<NB == 2 ? 0 : T::MIN_LOADS_PER_STEP>();
   __syncthreads();
+}
+
+// ---- ping-pong schedule of the eight-wave workgroup ---------------------------------
+// The four-wave step above has every wave do the same thing at the same time: all
+// waves form S(t+1) and the exponentials of P(t) (matrix products and vector work,
+// K operand reads), then all waves form O += V(t) P(t) (matrix products and V
+// transpose reads), with one barrier per step.  The V transpose reads of all eight
+// waves then fall into the same half of the step, where LDS bounds it.  Here waves
+// 0-3 (group A, the K loaders) run half a step ahead of waves 4-7 (group B, the V
+// loaders), with a barrier every half step: while one group is in its first half the
+// other is in its second, so every SIMD (one wave of each group) always has one wave
+// issuing exponentials and one issuing V reads beside the matrix products.
+//
+// Half-step h: group A runs half 1 of step h/2 (even h) or half 2 (odd h); group B the
+// same one half-step later.  Buffers (two per tensor, tile j in buffer (j - t_begin) % 2):
+//  * K(t+2) is loaded by group A in its half 1 of step t (h = 2t) into K(t)'s buffer,
+//    whose last reader was group B's half 1 of step t-1 (h = 2t-1); group A waits for
+//    it in its half 2 (h = 2t+1); the first reader is group A at h = 2t+2;
+//  * V(t+1) is loaded by group B in its half 1 of step t (h = 2t+1) into V(t-1)'s
+//    buffer, last read by group B's half 2 of step t-1 (h = 2t); group B waits for it
+//    in its half 2 (h = 2t+2); the first reader is group A at h = 2t+3.
+// The half-step barrier is a plain s_barrier: no fence, so it does not wait for the
+// tile loads still in flight (each loading wave waits for its own before the barrier
+// that precedes their first reader).  Its memory clobber keeps the compiler from
+// moving LDS accesses across it, and the scheduling barriers keep every other
+// instruction (the matrix products included) on its own side.
+__device__ __forceinline__ void half_step_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Half 1 of step t: loads, S(t+1) = K(t+1) Q^T, P(t) (rounded to E into pf) and its row sum.
+template <int HD, typename E, bool LAST, int PAR, bool NOMAX>
+__device__ __forceinline__ void pp_half1(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                         x8<E> (&pf)[4], int t, const KVStream<HD, 8>& kv, const LdsBufs& lb,
+                                         float cs) {
+  using T = Tile<HD, 8>;
+  if constexpr (!LAST) {
+    kv.load_k(lb.k[PAR], t + 2);      // group A only
+    kv.load_v(lb.v[1 - PAR], t + 1);  // group B only
+    qk_tile<HD, E>(s_nxt, lb.kl[1 - PAR], st.qf);
+  }
+  const float negm = (st.m_run == -INFINITY) ? 0.f : st.b_cur - st.m_run;
+  float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+  for (int ci = 0; ci < 4; ++ci) {
+    const int kb = ci >> 1, r0 = 8 * (ci & 1);
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e], cs, negm));
+      const float p1 = fast_exp2(fmaf(s_cur[kb][r0 + 2 * e + 1], cs, negm));
+      pk[e] = pack2<E>(p0, p1);
+      lsum0 += p0;
+      lsum1 += p1;
+    }
+    pf[ci] = __builtin_bit_cast(x8<E>, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  }
+  if constexpr (NOMAX) refit_reference<HD, E>(st, s_cur, pf, cs, lsum0, lsum1);
+  st.l_run += lsum0 + lsum1;
+  if constexpr (!LAST) {
+#ifndef FA_PP_V1
+#define FA_PP_V1 7
+#endif
+#ifndef FA_PP_PF1
+#define FA_PP_PF1 2
+#endif
+    // the loads; K operand reads FA_PP_PF1 products ahead; each S product followed by
+    // FA_PP_V1 vector instructions of P(t) (112 of them: FMA, exponential, row-sum add
+    // per score and one conversion per pair)
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, T::LOADS_PER_STEP, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, FA_PP_PF1, 0);
+#pragma unroll
+    for (int i = 0; i < HD / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_PP_V1, 0);
+    }
+  }
+}
+
+// Half 2 of step t: O += V(t) P(t); then (unless LAST) the max of S(t+1) with its mask
+// and bias, the reference-maximum update, and the wait for this wave's tile loads.
+template <int HD, bool ALIBI, typename E, bool LAST, int PAR>
+__device__ __forceinline__ void pp_half2(FwdState<HD, E>& st, f32x16 (&s_nxt)[2], const x8<E> (&pf)[4], int t,
+                                         const KVStream<HD, 8>& kv, const LdsBufs& lb, int half, float c, float cs,
+                                         float slope, int my_pos, int wl, int wr, int i0, int i_last, int off) {
+#pragma unroll
+  for (int ci = 0; ci < 4; ++ci) {
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db) {
+      const x8<E> a = v_operand<HD, E>(lb.vl[PAR], db, ci);
+      st.oacc[db] = mfma32(a, pf[ci], st.oacc[db]);
+    }
+  }
+#ifndef FA_PP_V2
+#define FA_PP_V2 2
+#endif
+#ifndef FA_PP_PF2
+#define FA_PP_PF2 4
+#endif
+  // V transpose reads FA_PP_PF2 ahead (two per product), FA_PP_V2 vector instructions
+  // (the row max of S(t+1)) after each product
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, FA_PP_PF2, 0);
+#pragma unroll
+  for (int i = 0; i < HD / 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, FA_PP_V2, 0);
+  }
+  if constexpr (LAST) return;
+
+  const int j1 = kv.key_lo + (t + 1) * BC;
+  float mx = 0.f;
+  float b_nxt = 0.f;
+  if constexpr (!ALIBI && FA_NOMAX) {
+    // the mask only; the reference maximum moves in half 1 when needed (refit_reference)
+    const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
+                          (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
+    if (!nxt_full)
+      (void)prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+    st.b_cur = b_nxt;
+    wait_tile_loads<0>();
+    return;
+  }
+  if constexpr (ALIBI) {
+    mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+  } else {
+    mx = to_log2(tile_max(s_nxt), cs);
+    const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
+                          (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
+    if (!nxt_full)
+      mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+  }
+  st.b_cur = b_nxt;
+  const float m_new = fmaxf(st.m_run, mx);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > st.m_run + RESCALE_TH) != 0, 0)) {
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    st.m_run = m_new;
+  }
+  // the tile loads this wave issued in its half 1 have landed before the next barrier
+  wait_tile_loads<0>();
+}
+
+// One step in the ping-pong order: half 1, barrier, half 2, barrier.
+template <int HD, bool ALIBI, typename E, bool LAST, int PAR>
+__device__ __forceinline__ void pp_step(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                                        x8<E> (&pf)[4], int t, const KVStream<HD, 8>& kv, const LdsBufs& lb,
+                                        int half, float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
+                                        int i_last, int off) {
+  pp_half1<HD, E, LAST, PAR, !ALIBI && FA_NOMAX>(st, s_cur, s_nxt, pf, t, kv, lb, cs);
+  half_step_barrier();
+  pp_half2<HD, ALIBI, E, LAST, PAR>(st, s_nxt, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
+  half_step_barrier();
 }
 
 // One work item: (batch, head, query tile[, key split]) number `item` of `items`.
@@ -717,7 +947,33 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   // the decode form) the item's last tile takes the short LAST step: +1-3.5% on 2k-4k
   // launches; elsewhere its extra code spilled in the loop.
   constexpr bool SHORT_LAST = !DEC && (HD == 128 || (HD == 64 && (!ALIBI || !SPLIT)));
-  if constexpr (SHORT_LAST) {
+#ifndef FA_PINGPONG
+#define FA_PINGPONG 1
+#endif
+  if constexpr (NW == 8 && FA_PINGPONG && !DEC && !SPLIT) {
+    // eight waves: the ping-pong order (group B starts half a step behind group A and
+    // ends half a step after it; both pass the same number of barriers)
+    const bool group_a = wave < 4;
+    x8<E> pf[4];
+    if (!group_a) half_step_barrier();
+    int t = t_begin;
+    for (; t + 2 < t_end; t += 2) {
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+                                      off);
+      pp_step<HD, ALIBI, E, false, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+                                      i_last, off);
+    }
+    if (t + 1 < t_end) {
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+                                      off);
+      pp_step<HD, ALIBI, E, true, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+                                     i_last, off);
+    } else if (t < t_end) {
+      pp_step<HD, ALIBI, E, true, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+                                     off);
+    }
+    if (group_a) half_step_barrier();
+  } else if constexpr (SHORT_LAST) {
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
       tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,

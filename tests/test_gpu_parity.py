@@ -219,3 +219,51 @@ def test_binding_errors_on_gpu():
     k = torch.zeros(1, 4, 2, 96, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(fa.FAError):
         fa.flash_attn_func(k, k, k)
+
+
+# Scores that rise along the keys: key j is scaled by 1 + 4j/Sk and softmax_scale is 1,
+# so every later key tile holds far larger scores than the first one.  Kernels without
+# ALiBi keep the reference maximum from the first tile until a tile's exponentials
+# grow past a threshold (or overflow), then refit it to that tile's row max; these
+# cases run that refit on most tiles, in the four-wave (1000 rows) and eight-wave
+# (4096 rows, headdim 128, unmasked) launches and under a causal mask.
+RISING_CASES = [
+    # b, h, sq, sk, d, causal
+    (1, 2, 1000, 1000, 128, False),
+    (1, 2, 4096, 4096, 128, False),
+    (1, 2, 777, 1300, 64, True),
+    (1, 1, 600, 900, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", RISING_CASES, ids=[f"b{c[0]}h{c[1]}_sq{c[2]}_sk{c[3]}_d{c[4]}"
+                                                     f"{'_causal' if c[5] else ''}" for c in RISING_CASES])
+def test_rising_scores_match_oracle(case):
+    b, h, sq, sk, d, causal = case
+    announce(f"rising scores {case}")
+    q, k, v = make_qkv(b, sq, sk, h, d, seed=sq + sk)
+    ramp = (1.0 + 4.0 * torch.arange(sk, dtype=torch.float32) / sk).view(1, sk, 1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    out, lse = gpu_fwd(q, k, v, 1.0, causal, -1, -1, None)
+    ref_out, ref_lse = oracle.attention_forward(q, k, v, 1.0, causal)
+    check_lse(lse, ref_lse)
+    check_out(out, ref_out)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_far_negative_scores_under_window(d):
+    """Every score near -1000: a row's exponentials against a reference of 0 all
+    underflow.  Under a sliding window (and bottom-right alignment with Sq < Sk) many
+    rows see no key in their block's first tiles, so they still have no reference when
+    their first visible keys arrive; they must get one from those keys' scores."""
+    b, h, sq, sk = 1, 2, 192, 450
+    announce(f"far negative scores d{d}")
+    g = torch.Generator().manual_seed(d)
+    q = (4.0 + 0.05 * torch.randn(b, sq, h, d, generator=g)).to(torch.bfloat16)
+    k = (-4.0 + 0.05 * torch.randn(b, sk, h, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(b, sk, h, d, generator=g).to(torch.bfloat16)
+    for wl, wr in ((30, 20), (100, 0)):
+        out, lse = gpu_fwd(q, k, v, 1.0, False, wl, wr, None)
+        ref_out, ref_lse = oracle.attention_forward(q, k, v, 1.0, False, wl, wr)
+        check_lse(lse, ref_lse)
+        check_out(out, ref_out)
