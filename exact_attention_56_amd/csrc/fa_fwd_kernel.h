@@ -49,9 +49,9 @@
 
 namespace fa {
 
-// A workgroup has NW = 4 or 8 waves of 32 query rows each.  Eight waves (256 rows)
-// halve the K/V traffic from L2 per flop and measured faster for headdim 128
-// without a mask at seqlen_q >= 4096; everything else uses four.
+// A workgroup has NW = 4 or 8 waves of 32 query rows each.  Eight waves (256 rows,
+// the ping-pong schedule below) halve the K/V traffic from L2 per flop; headdim 128
+// uses them where they measured faster (fwd_waves), everything else four.
 constexpr int BC = 64;  // keys per tile
 constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2^8
 // Kernels without ALiBi (headdim 64 and 128) keep the reference maximum without a
