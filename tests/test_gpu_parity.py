@@ -67,10 +67,16 @@ FWD_CASES = [
     (1, 2, 384, 768, 64, False, 100, -1, False, None),
     (1, 2, 96, 1200, 128, True, 700, 0, True, None),
     (1, 2, 1, 700, 128, True, -1, -1, True, None),
-    # headdim 128 without a mask from 4096 query rows on: eight-wave (256-row) workgroups
+    # headdim 128 without a mask from 2048 query rows on, and with a plain causal mask
+    # from 8192: eight-wave (256-row) workgroups in the ping-pong schedule
     (1, 1, 4096 + 77, 3001, 128, False, -1, -1, False, None),
     (1, 1, 4352, 4352, 128, False, -1, -1, True, None),
     (1, 1, 4095, 333, 128, False, -1, -1, False, None),
+    (1, 1, 2047, 2100, 128, False, -1, -1, False, None),
+    (2, 1, 2048, 1999, 128, False, -1, -1, False, None),
+    (1, 1, 8192 + 40, 8192 + 40, 128, True, -1, -1, False, None),
+    (1, 1, 8200, 9100, 128, True, -1, -1, True, None),
+    (1, 1, 8191, 8191, 128, True, -1, -1, False, None),
 ]
 
 
@@ -101,6 +107,8 @@ VARLEN_CASES = [
     ((520, 1), (700, 1000), 6, 3, 64, True, 100, 0, True),
     # a sequence of at least 4096 rows without a mask: the eight-wave launch, grouped heads
     ((4100, 50), (4100, 3000), 2, 1, 128, False, -1, -1, False),
+    # causal with a sequence of at least 8192 rows: the eight-wave causal launch
+    ((8197, 300), (8197, 300), 2, 1, 128, True, -1, -1, False),
 ]
 
 
