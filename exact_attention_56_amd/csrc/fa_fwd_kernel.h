@@ -270,31 +270,33 @@ __device__ __forceinline__ int vt_lane_offset(int lane) {
   return (8 * (g >> 1) + (r >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
 }
 
-// ALiBi: turn the raw scores of one tile into log2 units with the bias added,
-// scale*log2e*s - slope*log2e*|pos - key|.  Without ALiBi the scores stay raw.
-__device__ __forceinline__ void bias_tile(f32x16 (&s)[2], int j0, int my_pos, float c, float slope, int half) {
+// ALiBi (page "2.4"): the bias -slope * |pos - key| of key j0 + 8*half + koff, koff =
+// 32kb + 16(r/8) + r%8, is linear in koff on a tile whose keys all lie on one side of
+// the row's position: slope * koff + b to the left, with b = slope * (j0 + 8*half -
+// pos), and -slope * koff - b to the right.  The scores stay in raw units with the
+// koff part folded in, t = s + (+-slope / c) * koff (one FMA per score); the per-lane
+// part b is carried beside the tile, so that t * c + b is the biased score in log2
+// units (exact row max, and p = exp2(t * c + b - m) in one FMA as without ALiBi).  A
+// tile that straddles a row's position takes the left form; its keys right of the
+// position (visible only without a causal mask) then get -2 * slope * (key - pos) / c
+// more, which makes their bias exact.  slope and c here are in log2 units.
+__device__ __forceinline__ void bias_tile(f32x16 (&s)[2], float c, float slope, int j0, int my_pos, int half,
+                                          bool right, bool straddle) {
+  const float gc = (right ? -slope : slope) / c;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // key held by (lane, r): see k_lds_row for the row order
-      const int key = j0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-      s[kb][r] = s[kb][r] * c - slope * fabsf((float)(my_pos - key));
-    }
+    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(gc, (float)(32 * kb + 16 * (r >> 3) + (r & 7)), s[kb][r]);
   }
-}
-
-// ALiBi on a tile whose keys all lie on one side of every row's aligned position:
-// |pos - key| is then linear in the key, so the bias splits into slope*koff (the
-// key's offset inside the tile, the same for every lane) and a per-lane part that
-// the caller carries as the tile's log2 offset.  Stored scores become
-// scale*log2e*s + sgn*slope*log2e*koff, with sgn = +1 left of the rows, -1 right.
-__device__ __forceinline__ void bias_tile_linear(f32x16 (&s)[2], float c, float slope, bool right) {
-  if (right) slope = -slope;
+  if (straddle) {
+    const float dpos = (float)(my_pos - j0 - 8 * half);  // pos - key = dpos - koff
+    const float k2 = 2.f * slope / c;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, slope * (float)(32 * kb + 16 * (r >> 3) + (r & 7)));
+      for (int r = 0; r < 16; ++r)
+        s[kb][r] = fmaf(k2, fminf(dpos - (float)(32 * kb + 16 * (r >> 3) + (r & 7)), 0.f), s[kb][r]);
+    }
   }
 }
 
@@ -351,29 +353,30 @@ struct FwdState {
   float b_cur;              // log2 offset to add to the stored scores of the tile in s_cur (ALiBi)
 };
 
-// Turn the raw S^T of tile t (first key j0) into stored scores: mask where the tile
-// crosses a mask boundary, add the ALiBi bias (exactly, or split off as a per-lane
-// offset on tiles where it is linear).  Sets `b` to this lane's log2 offset (stored
-// score * cs + b is the score in log2 units) and returns the row max in log2 units.
+// Prepare the raw S^T of tile t (first key j0): with ALiBi fold in the bias (bias_tile)
+// and set this lane's log2 offset b; mask where the tile crosses a mask boundary.
+// Stored scores times `cs`, plus b, are the scores in log2 units.  Returns the tile's
+// row max in log2 units.
 template <bool ALIBI>
 __device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, int key_hi, int my_pos, int wl, int wr,
                                              int i0, int i_last, int off, float c, float cs, float slope, int half) {
-  const bool full = (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
+  const bool full =
+      (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
   b = 0.f;
   if constexpr (ALIBI) {
     const bool left = j0 + BC - 1 <= i0 + off;  // every key at or before every row's position
     const bool right = j0 >= i_last + off;      // every key at or after every row's position
-    if (full && (left || right)) {
-      bias_tile_linear(s, c, slope, right);
-      const float d = slope * (float)(j0 + 8 * half - my_pos);
-      b = right ? -d : d;
-      // the two half-waves hold different keys, so each adds its own offset first
-      return max_with_other_half(lane_max(s) + b);
-    }
-    bias_tile(s, j0, my_pos, c, slope, half);
+    const bool rgt = right && !left;
+    const float d = slope * (float)(j0 + 8 * half - my_pos);
+    b = rgt ? -d : d;
+    // on a straddling tile the keys right of a row's position are visible only
+    // without a causal mask (wr != 0)
+    bias_tile(s, c, slope, j0, my_pos, half, rgt, !left && !right && wr != 0);
   }
   if (!full) mask_tile(s, j0, key_hi, my_pos, wl, wr, half);
-  return to_log2(tile_max(s), cs);
+  const float mx = to_log2(lane_max(s), cs);
+  // the two half-waves hold different keys, so each adds its own offset first
+  return max_with_other_half(mx == -INFINITY ? mx : mx + b);
 }
 
 // Reference maximum kept without a per-tile row max (kernels without ALiBi): P(t) is
@@ -923,7 +926,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   float slope = 0.f;
   if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + my_h] * kLog2e;  // bias in log2 units
   // multiplier turning the stored scores into log2 units
-  const float cs = ALIBI ? 1.f : c;
+  const float cs = c;
 
   f32x16 s_a[2], s_b[2];
 
