@@ -280,9 +280,11 @@ __device__ __forceinline__ int vt_lane_offset(int lane) {
 // tile that straddles a row's position takes the left form; its keys right of the
 // position (visible only without a causal mask) then get -2 * slope * (key - pos) / c
 // more, which makes their bias exact.  slope and c here are in log2 units.
-__device__ __forceinline__ void bias_tile(f32x16 (&s)[2], float c, float slope, int j0, int my_pos, int half,
-                                          bool right, bool straddle) {
-  const float gc = (right ? -slope : slope) / c;
+template <bool DIV>
+__device__ __forceinline__ void bias_tile(f32x16 (&s)[2], float slope, float c, float slope_c, int j0, int my_pos,
+                                          int half, bool right, bool straddle) {
+  // slope_c = slope / c, formed once per row (DIV: divided here, see prep_scores)
+  const float gc = DIV ? (right ? -slope : slope) / c : (right ? -slope_c : slope_c);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -290,7 +292,7 @@ __device__ __forceinline__ void bias_tile(f32x16 (&s)[2], float c, float slope, 
   }
   if (straddle) {
     const float dpos = (float)(my_pos - j0 - 8 * half);  // pos - key = dpos - koff
-    const float k2 = 2.f * slope / c;
+    const float k2 = DIV ? 2.f * slope / c : 2.f * slope_c;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -357,9 +359,13 @@ struct FwdState {
 // and set this lane's log2 offset b; mask where the tile crosses a mask boundary.
 // Stored scores times `cs`, plus b, are the scores in log2 units.  Returns the tile's
 // row max in log2 units.
-template <bool ALIBI>
+// slope_c = slope / cs is formed once per row by the caller, except at headdim 256
+// (DIV): there the one-wave-per-SIMD kernel ran 17% slower with any other form than
+// with both divisions of bias_tile on every tile.
+template <bool ALIBI, bool DIV = false>
 __device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, int key_hi, int my_pos, int wl, int wr,
-                                             int i0, int i_last, int off, float c, float cs, float slope, int half) {
+                                             int i0, int i_last, int off, float cs, float slope, float slope_c,
+                                             int half) {
   const bool full =
       (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
   b = 0.f;
@@ -371,7 +377,7 @@ __device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, i
     b = rgt ? -d : d;
     // on a straddling tile the keys right of a row's position are visible only
     // without a causal mask (wr != 0)
-    bias_tile(s, c, slope, j0, my_pos, half, rgt, !left && !right && wr != 0);
+    bias_tile<DIV>(s, slope, cs, slope_c, j0, my_pos, half, rgt, !left && !right && wr != 0);
   }
   if (!full) mask_tile(s, j0, key_hi, my_pos, wl, wr, half);
   const float mx = to_log2(lane_max(s), cs);
@@ -439,7 +445,7 @@ struct LdsBufs {
 template <int HD, int NW, bool ALIBI, typename E, bool LAST, int PAR, typename KV>
 __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int t,
                                           int t_begin, const KV& kv, const LdsBufs& lb, int half,
-                                          float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
+                                          float slope_c, float cs, float slope, int my_pos, int wl, int wr, int i0,
                                           int i_last, int off) {
   using T = Tile<HD, NW>;
   constexpr int NB = T::NBUF;
@@ -595,12 +601,14 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   // ALiBi tiles, and tiles crossing a mask boundary: bias / mask, then take the max again
   float b_nxt = 0.f;
   if constexpr (ALIBI) {
-    mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+    mx = prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                       i0, i_last, off, cs, slope, slope_c, half);
   } else {
     const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
                           (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
     if (!nxt_full)
-      mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+      mx = prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                         i0, i_last, off, cs, slope, slope_c, half);
   }
   st.b_cur = b_nxt;  // tile t's offset was used by P(t) above
 
@@ -706,8 +714,9 @@ __device__ __forceinline__ void pp_half1(FwdState<HD, E>& st, const f32x16 (&s_c
 // and bias, the reference-maximum update, and the wait for this wave's tile loads.
 template <int HD, bool ALIBI, typename E, bool LAST, int PAR>
 __device__ __forceinline__ void pp_half2(FwdState<HD, E>& st, f32x16 (&s_nxt)[2], const x8<E> (&pf)[4], int t,
-                                         const KVStream<HD, 8>& kv, const LdsBufs& lb, int half, float c, float cs,
-                                         float slope, int my_pos, int wl, int wr, int i0, int i_last, int off) {
+                                         const KVStream<HD, 8>& kv, const LdsBufs& lb, int half, float slope_c,
+                                         float cs, float slope, int my_pos, int wl, int wr, int i0, int i_last,
+                                         int off) {
 #pragma unroll
   for (int ci = 0; ci < 4; ++ci) {
 #pragma unroll
@@ -741,19 +750,22 @@ __device__ __forceinline__ void pp_half2(FwdState<HD, E>& st, f32x16 (&s_nxt)[2]
     const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
                           (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
     if (!nxt_full)
-      (void)prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+      (void)prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                          i0, i_last, off, cs, slope, slope_c, half);
     st.b_cur = b_nxt;
     wait_tile_loads<0>();
     return;
   }
   if constexpr (ALIBI) {
-    mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+    mx = prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                       i0, i_last, off, cs, slope, slope_c, half);
   } else {
     mx = to_log2(tile_max(s_nxt), cs);
     const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
                           (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
     if (!nxt_full)
-      mx = prep_scores<ALIBI>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+      mx = prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                         i0, i_last, off, cs, slope, slope_c, half);
   }
   st.b_cur = b_nxt;
   const float m_new = fmaxf(st.m_run, mx);
@@ -774,11 +786,13 @@ __device__ __forceinline__ void pp_half2(FwdState<HD, E>& st, f32x16 (&s_nxt)[2]
 template <int HD, bool ALIBI, typename E, bool LAST, int PAR>
 __device__ __forceinline__ void pp_step(FwdState<HD, E>& st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                                         x8<E> (&pf)[4], int t, const KVStream<HD, 8>& kv, const LdsBufs& lb,
-                                        int half, float c, float cs, float slope, int my_pos, int wl, int wr, int i0,
+                                        int half, float slope_c, float cs, float slope, int my_pos, int wl, int wr,
+                                        int i0,
                                         int i_last, int off) {
   pp_half1<HD, E, LAST, PAR, !ALIBI && FA_NOMAX>(st, s_cur, s_nxt, pf, t, kv, lb, cs);
   half_step_barrier();
-  pp_half2<HD, ALIBI, E, LAST, PAR>(st, s_nxt, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last, off);
+  pp_half2<HD, ALIBI, E, LAST, PAR>(st, s_nxt, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
+                                    off);
   half_step_barrier();
 }
 
@@ -925,6 +939,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const float c = p.scale_log2;
   float slope = 0.f;
   if constexpr (ALIBI) slope = p.alibi[(long)b * p.alibi_bstride + my_h] * kLog2e;  // bias in log2 units
+  // the bias step per key in raw score units (bias_tile); headdim 256 divides per tile
+  const float slope_c = (ALIBI && HD != 256) ? slope / c : 0.f;
   // multiplier turning the stored scores into log2 units
   const float cs = c;
 
@@ -941,7 +957,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     __syncthreads();
     qk_tile<HD, E>(s_a, lb.kl[0], st.qf);
     const int j0 = key_lo + t_begin * BC;
-    st.m_run = prep_scores<ALIBI>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr, i0, i_last, off, c, cs, slope, half);
+    st.m_run = prep_scores<ALIBI, HD == 256>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr,
+                                             i0, i_last, off, cs, slope, slope_c, half);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
 
@@ -961,45 +978,45 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     if (!group_a) half_step_barrier();
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
-      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
                                       off);
-      pp_step<HD, ALIBI, E, false, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+      pp_step<HD, ALIBI, E, false, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0,
                                       i_last, off);
     }
     if (t + 1 < t_end) {
-      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
                                       off);
-      pp_step<HD, ALIBI, E, true, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
+      pp_step<HD, ALIBI, E, true, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0,
                                      i_last, off);
     } else if (t < t_end) {
-      pp_step<HD, ALIBI, E, true, 0>(st, s_a, s_b, pf, t, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, true, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
                                      off);
     }
     if (group_a) half_step_barrier();
   } else if constexpr (SHORT_LAST) {
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
-      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
-                                            i_last, off);
-      tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr,
+      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
                                             i0, i_last, off);
+      tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
+                                            wr, i0, i_last, off);
     }
     if (t + 1 < t_end) {  // two tiles left
-      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
-                                            i_last, off);
-      tile_step<HD, NW, ALIBI, E, true, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr,
-                                           i0, i_last, off);
+      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
+                                            i0, i_last, off);
+      tile_step<HD, NW, ALIBI, E, true, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
+                                           wr, i0, i_last, off);
     } else if (t < t_end) {  // one tile left
-      tile_step<HD, NW, ALIBI, E, true, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
-                                           i_last, off);
+      tile_step<HD, NW, ALIBI, E, true, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
+                                           i0, i_last, off);
     }
   } else {
     for (int t = t_begin; t < t_end; t += 2) {
-      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr, i0,
-                                            i_last, off);
-      if (t + 1 >= t_end) break;
-      tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, c, cs, slope, my_pos, wl, wr,
+      tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
                                             i0, i_last, off);
+      if (t + 1 >= t_end) break;
+      tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
+                                            wr, i0, i_last, off);
     }
   }
   f32x16* const oacc = st.oacc;
