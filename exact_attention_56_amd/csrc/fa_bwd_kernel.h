@@ -344,24 +344,34 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
       vspan = khi - klo;
     }
     x8<E> dsf[4];
+    // P^T and dS^T of the tile; the masked form only where the tile crosses a mask
+    // boundary or the end (two explicit branches: left to itself the compiler computed
+    // the mask of every score and selected, which was half the vector work of a full tile)
+    auto scores = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-      const int kb = ci >> 1, r0 = 8 * (ci & 1);
-      f32x16 tmp;
+      for (int ci = 0; ci < 4; ++ci) {
+        const int kb = ci >> 1, r0 = 8 * (ci & 1);
+        f32x16 tmp;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = j0 + 32 * kb + 16 * (r0 / 8) + 8 * half + e;
-        float x = fmaf(s[kb][r0 + e], c, -lrow2);
-        if constexpr (ALIBI) x += alibi_log2(slope2, my_pos, key);
-        float pv = fast_exp2(x);
-        if (!full) {
-          const bool vis = vspan >= 0 && (uint32_t)(key - vlo) <= (uint32_t)vspan && my_q < Sq;
-          pv = vis ? pv : 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const int key = j0 + 32 * kb + 16 * (r0 / 8) + 8 * half + e;
+          float x = fmaf(s[kb][r0 + e], c, -lrow2);
+          if constexpr (ALIBI) x += alibi_log2(slope2, my_pos, key);
+          float pv = fast_exp2(x);
+          if constexpr (MASKED) {
+            const bool vis = vspan >= 0 && (uint32_t)(key - vlo) <= (uint32_t)vspan && my_q < Sq;
+            pv = vis ? pv : 0.f;
+          }
+          tmp[e] = pv * (dp[kb][r0 + e] - drow);
         }
-        tmp[e] = pv * (dp[kb][r0 + e] - drow);
+        dsf[ci] = pack_rows<E>(tmp, 0);
       }
-      dsf[ci] = pack_rows<E>(tmp, 0);
-    }
+    };
+    if (full)
+      scores(std::false_type{});
+    else
+      scores(std::true_type{});
 
     // dQ^T += K^T dS^T
 #pragma unroll
@@ -466,30 +476,45 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     st.row_stride = (int)rs;
     st.row_bytes = (int)rs * 2;
     st.init(wave, lane);
-    // L and D of a tile: wave 0 loads L, wave 1 loads D (4 bytes per lane, rows past
-    // the end read as zeros; L is scaled and -inf handled when read)
-    auto load_ld = [&](lds_u8* dst, int t) {
-      if (wave < 2) {
+    // L and D of a tile.  Wave 1 loads D straight into LDS (4 bytes per lane, rows past
+    // the end read as zeros).  Wave 0 loads L into a register and, once it has landed,
+    // stores it to LDS in log2 units with -inf (a row that saw no key) and rows past the
+    // end as +inf, so that every P of such a row is exp2(-inf) = 0: the per-score loop
+    // then needs one FMA before the exponential, where scaling and testing each of its
+    // 32 copies of L cost three vector instructions per score.
+    auto load_d = [&](lds_u8* dst, int t) {
+      if (wave == 1) {
         const int r0 = t * DKV_TILE;
-        const float* src = (wave == 0 ? p.lse : p.delta) + loff + r0;
+        const float* src = p.delta + loff + r0;
         const int n = max(0, min(DKV_TILE, Sq - r0)) * 4;
         const auto rsr = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, dst + LDBYTES * wave, 4, 4 * lane, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, dst + LDBYTES, 4, 4 * lane, 0, 0, 0);
       }
     };
+    auto load_l = [&](int t) {  // wave 0: this lane's row of tile t
+      const int r = t * DKV_TILE + lane;
+      return (lane < DKV_TILE && r < Sq) ? p.lse[loff + r] : -INFINITY;
+    };
+    auto put_l = [&](lds_u8* dst, float l) {  // wave 0
+      if (lane < DKV_TILE) ((__attribute__((address_space(3))) float*)dst)[lane] = l == -INFINITY ? INFINITY : l * kLog2e;
+    };
+    float lraw = -INFINITY;  // wave 0: L of this lane's row of the next tile, in flight
 
     if (t_begin < t_end) {
       st.load(lds, lds + GOFF, t_begin);
-      load_ld(lds + LOFF, t_begin);
+      load_d(lds + LOFF, t_begin);
+      if (wave == 0) lraw = load_l(t_begin);
     }
     for (int t = t_begin; t < t_end; ++t) {
       const int cur = (t - t_begin) & 1;
       wait_tile_loads<0>();
+      if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
       __syncthreads();
       if (t + 1 < t_end) {
         lds_u8* nb = lds + (cur ^ 1) * BUF;
         st.load(nb, nb + GOFF, t + 1);
-        load_ld(nb + LOFF, t + 1);
+        load_d(nb + LOFF, t + 1);
+        if (wave == 0) lraw = load_l(t + 1);
       }
       const lds_u8* qt = lds + cur * BUF;
       const lds_u8* gt = qt + GOFF;
@@ -512,31 +537,40 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
                         (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
       x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
+      // P and dS of the tile; the masked form only where the tile crosses a mask
+      // boundary or the end (explicit branches, as in dq_kernel)
+      auto scores = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
   #pragma unroll
-      for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
-        const int qb = cc >> 1, ci = cc & 1;
-        const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
-        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-        const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
-        const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
-        const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
-        const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
-        f32x16 pt, dt;
+        for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+          const int qb = cc >> 1, ci = cc & 1;
+          const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
+          typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+          const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+          const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+          const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+          const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+          f32x16 pt, dt;
   #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float l = e < 4 ? l_a[e] : l_b[e - 4];
-          const float dd = e < 4 ? d_a[e] : d_b[e - 4];
-          const int qi = i0 + qrow + e;
-          float x = fmaf(s[qb][8 * ci + e], c, -l * kLog2e);
-          if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
-          float pv = (l == -INFINITY) ? 0.f : fast_exp2(x);
-          if (!full) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
-          pt[e] = pv;
-          dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+          for (int e = 0; e < 8; ++e) {
+            const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
+            const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+            const int qi = i0 + qrow + e;
+            float x = fmaf(s[qb][8 * ci + e], c, -l2);
+            if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+            float pv = fast_exp2(x);
+            if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+            pt[e] = pv;
+            dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+          }
+          pf[cc] = pack_rows<E>(pt, 0);
+          dsf[cc] = pack_rows<E>(dt, 0);
         }
-        pf[cc] = pack_rows<E>(pt, 0);
-        dsf[cc] = pack_rows<E>(dt, 0);
-      }
+      };
+      if (full)
+        scores(std::false_type{});
+      else
+        scores(std::true_type{});
 
   #pragma unroll
       for (int cc = 0; cc < 2 * DKV_QB; ++cc)
