@@ -1,37 +1,28 @@
-// fa_bwd.hip - instantiates the delta and dK/dV passes of the backward (headdim 64,
-// 128 and 256, bf16 and fp16; the dQ pass too at 256) and launches the three passes in
-// order on one stream:
-// delta, dK/dV, dQ (padded or packed batches, grouped K/V heads).
+// fa_bwd.hip - instantiates the dK/dV pass of the backward (headdim 64, 128 and 256,
+// bf16 and fp16; the dQ pass too at 256) and launches the two passes in order on one
+// stream: dQ (which also writes D), then dK/dV (padded or packed batches, grouped K/V
+// heads).
 #include "fa_bwd_kernel.h"
 
 namespace fa {
 
 template <int HD, typename E>
 static hipError_t launch_bwd_hd(const BwdParams& p, hipStream_t stream) {
-  // delta runs over rows of [rows, H, D]; a packed batch is one sequence of total_q rows
-  // for it (its [H, total_q] output is then the [1, H, total_q] layout)
-  BwdParams pd = p;
-  if (p.cu_q != nullptr) {
-    pd.batch = 1;
-    pd.seqlen_q = (int)p.lse_head_stride;
-  }
-  const long rows = (long)pd.batch * pd.seqlen_q * pd.nheads;
-  const int rows_per_block = delta_rows_per_block(HD);
-  hipLaunchKernelGGL((delta_kernel<HD, E>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
-                     0, stream, pd, rows);
-  // dK/dV must not run on a delta that was never written
-  const hipError_t ed = hipGetLastError();
-  if (ed != hipSuccess) return ed;
+  // dQ first: besides dQ it writes D = rowsum(dO o O) of every query row, which the
+  // dK/dV pass reads, so dK/dV must not start before it (one stream: it does not)
+  hipError_t e;
+  if constexpr (HD == 256)
+    e = launch_dq_hd<256, E>(p, stream);  // accumulators in AGPRs: compiled here
+  else
+    e = HD == 64 ? launch_dq_d64(p, stream) : launch_dq_d128(p, stream);
+  if (e != hipSuccess) return e;
   const bool alibi = p.alibi != nullptr;
   const int kv_items = p.batch * p.nheads_k * p.num_k_tiles;
   if (alibi)
     hipLaunchKernelGGL((dkdv_kernel<HD, true, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
   else
     hipLaunchKernelGGL((dkdv_kernel<HD, false, E>), dim3(kv_items), dim3(256), 0, stream, p, kv_items);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if constexpr (HD == 256) return launch_dq_hd<256, E>(p, stream);  // accumulators in AGPRs: compiled here
-  return HD == 64 ? launch_dq_d64(p, stream) : launch_dq_d128(p, stream);
+  return hipGetLastError();
 }
 
 template <typename E>

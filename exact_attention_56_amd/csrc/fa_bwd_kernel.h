@@ -12,13 +12,14 @@
 // "并行性 / 反向传播" (one block per column block of K and V).
 //
 // Design for CDNA4:
-//  * three kernels: delta_kernel (D = rowsum(dO o O), fp32), dkdv_kernel (one
-//    workgroup per 128 keys of a (batch, head): K and V of its keys stay in registers
-//    while 32-query tiles of Q, dO, L, D stream through LDS) and dq_kernel (one
-//    workgroup per 128 queries: Q and dO stay in registers while 64-key tiles of K and
-//    V stream through LDS).  dQ gets its own pass instead of atomic adds from the
-//    key-block workgroups: every output element is written once, so the results are
-//    deterministic, and no fp32 accumulation buffer is needed;
+//  * two kernels, run in this order: dq_kernel (one workgroup per 128 queries: Q and
+//    dO stay in registers while 64-key tiles of K and V stream through LDS; it also
+//    forms D = rowsum(dO o O) of its rows in fp32 and writes it out) and dkdv_kernel
+//    (one workgroup per 128 keys of a (batch, head): K and V of its keys stay in
+//    registers while query tiles of Q, dO, L, D stream through LDS).  dQ gets its own
+//    pass instead of atomic adds from the key-block workgroups: every output element
+//    is written once, so the results are deterministic, and no fp32 accumulation
+//    buffer is needed;
 //  * all products are v_mfma_f32_32x32x16_bf16 with transposed outputs where that
 //    keeps row statistics lane-local: the dq kernel holds S^T, dP^T (lane = query),
 //    the dkdv kernel S, dP (lane = key);
@@ -155,39 +156,6 @@ __device__ __forceinline__ void store_rows(uint16_t* base, long row_stride, int 
     }
 }
 
-// ---------------------------------------------------------------------------------
-// delta_kernel: D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32.  One
-// wave per 8 rows; HD/8 lanes per row, 16 bytes each, then a lane-group sum.
-template <int HD, typename E>
-__global__ __launch_bounds__(256) void delta_kernel(BwdParams p, long rows) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
-  constexpr int LPR = HD / 8;       // lanes per row
-  constexpr int RPW = 64 / LPR;     // rows per wave
-  const int lane = threadIdx.x & 63;
-  const long row = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;  // row = (b*Sq + i)*H + h
-  const int c = lane % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 o = *(const u32x4*)(p.out + row * HD + 8 * c);
-    const u32x4 g = *(const u32x4*)(p.dout + row * HD + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += widen_lo<E>(o[e]) * widen_lo<E>(g[e]);
-      acc += widen_hi<E>(o[e]) * widen_hi<E>(g[e]);
-    }
-  }
-#pragma unroll
-  for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && c == 0) {
-    const int h = (int)(row % p.nheads);
-    const long bi = row / p.nheads;  // b * Sq + i
-    const int i = (int)(bi % p.seqlen_q);
-    const int b = (int)(bi / p.seqlen_q);
-    p.delta[((long)b * p.nheads + h) * p.seqlen_q + i] = acc;
-  }
-#endif
-}
-
 // Rows of sequence b: the first q and k row and the lengths; padded batches use the
 // common lengths.  The first lse/delta element of (b, h) is lse_row(p, b, h, q_start, Sq).
 struct SeqRows {
@@ -281,19 +249,48 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   const int t_begin = hi >= lo ? lo / DQ_TILE : 0;
   const int t_end = hi >= lo ? hi / DQ_TILE + 1 : 0;
 
+  // the first K/V tile is on its way to LDS while this wave loads its rows and forms D
+  Stream st;
+  st.abase = p.k + koff;
+  st.bbase = p.v + koff;
+  st.lo = 0;
+  st.hi = Sk;
+  st.row_stride = (int)rsk;
+  st.row_bytes = (int)rsk * 2;
+  st.init(wave, lane);
+  if (t_begin < t_end) st.load(lds, lds + 2 * Stream::ABYTES, t_begin);
+
   x8<E> qf[HD / 16], gf[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
     qf[kk] = row_fragment<E>(p.q + qoff, rs, my_q, Sq, kk, half, p.q_and, p.q_sign);
     gf[kk] = row_fragment<E>(p.dout + qoff, rs, my_q, Sq, kk, half, 0xffffffffu, 0u);
   }
-  // L in log2 units (an empty row gets +inf, so that every P of it is 0) and D
-  float lrow2 = INFINITY, drow = 0.f;
+  // D = rowsum(dO o O) of this lane's row in fp32: the lane holds half of the row's dO
+  // (gf) and reads the same half of O; the other half-wave holds the rest.  Written to
+  // delta for the dK/dV pass, which runs after this one.
+  float dpart = 0.f;
+  if (my_q < Sq) {
+    const uint16_t* orow = p.out + qoff + (long)my_q * rs;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      const u32x4 o = *(const u32x4*)(orow + 16 * kk + 8 * half);
+      const u32x4 g = __builtin_bit_cast(u32x4, gf[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart = fmaf(widen_lo<E>(o[e]), widen_lo<E>(g[e]), dpart);
+        dpart = fmaf(widen_hi<E>(o[e]), widen_hi<E>(g[e]), dpart);
+      }
+    }
+  }
+  const float drow = sum_with_other_half(dpart);
+  // L in log2 units (an empty row gets +inf, so that every P of it is 0)
+  float lrow2 = INFINITY;
   if (my_q < Sq) {
     const long li = lse_row(p, b, h, sr) + my_q;
     const float l = p.lse[li];
     lrow2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    drow = p.delta[li];
+    if (half == 0) p.delta[li] = drow;
   }
   const float c = p.scale_log2;
   float slope2 = 0.f;
@@ -303,16 +300,6 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) dq[db] = f32x16{};
 
-  Stream st;
-  st.abase = p.k + koff;
-  st.bbase = p.v + koff;
-  st.lo = 0;
-  st.hi = Sk;
-  st.row_stride = (int)rsk;
-  st.row_bytes = (int)rsk * 2;
-  st.init(wave, lane);
-
-  if (t_begin < t_end) st.load(lds, lds + 2 * Stream::ABYTES, t_begin);
   for (int t = t_begin; t < t_end; ++t) {
     const int cur = (t - t_begin) & 1;
     wait_tile_loads<0>();

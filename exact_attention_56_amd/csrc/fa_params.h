@@ -60,7 +60,7 @@ struct BwdParams {
   const uint16_t* out;    // bf16/fp16 [B, Sq, H, D]  forward output
   const uint16_t* dout;   // bf16/fp16 [B, Sq, H, D]  upstream gradient
   const float* lse;       // fp32 [B, H, Sq]     forward logsumexp (natural log)
-  float* delta;           // fp32 [B, H, Sq]     D, written by delta_kernel
+  float* delta;           // fp32 [B, H, Sq]     D, written by dq_kernel, read by dkdv_kernel
   uint16_t* dq;           // bf16/fp16 [B, Sq, H, D]
   uint16_t* dk;           // bf16/fp16 [B, Sk, H_k, D]
   uint16_t* dv;           // bf16/fp16 [B, Sk, H_k, D]
@@ -128,10 +128,6 @@ constexpr int DEC_UNROLL = FA_DEC_UNROLL;
 // Key rows one decode step covers per wave (blocks of a paged cache must hold a whole
 // number of them): DEC_UNROLL * 64 / (headdim / 8).
 inline int decode_step_keys(int headdim) { return DEC_UNROLL * 64 / (headdim / 8); }
-
-// Rows of [rows, H, D] one delta_kernel workgroup reduces: four waves, headdim / 8 lanes
-// per row.
-inline int delta_rows_per_block(int headdim) { return 4 * (64 / (headdim / 8)); }
 
 // Size of the device buffer that holds the split partials of fa_fwd_kvcache_noalloc
 // (one per GPU, for the life of the process).

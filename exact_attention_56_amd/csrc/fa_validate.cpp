@@ -151,11 +151,10 @@ void bwd_from_fwd(const FwdParams& f, float softmax_scale, const void* out, cons
   p->num_k_tiles = (int)ceil_div(f.seqlen_k, BWD_ROWS);
 }
 
-// The three grids of the backward: delta over `rows` rows of [rows, H, D], dK/dV over
-// key tiles of every K/V head, dQ over query tiles of every query head.
-bool bwd_grids_ok(const BwdParams& p, long long rows, int headdim) {
-  return grid_ok(ceil_div(rows, delta_rows_per_block(headdim)), BLOCK_THREADS) &&
-         grid_ok((long long)p.batch * p.nheads_k * p.num_k_tiles, BLOCK_THREADS) &&
+// The two grids of the backward: dK/dV over key tiles of every K/V head, dQ over query
+// tiles of every query head.
+bool bwd_grids_ok(const BwdParams& p) {
+  return grid_ok((long long)p.batch * p.nheads_k * p.num_k_tiles, BLOCK_THREADS) &&
          grid_ok((long long)p.batch * p.nheads * p.num_q_tiles, BLOCK_THREADS);
 }
 
@@ -344,7 +343,7 @@ int plan_bwd(const void* q, const void* k, const void* v, const void* out, const
                          window_right, alibi_slopes, alibi_per_batch, dtype, &f);
   if (st != FA_OK) return st;
   bwd_from_fwd(f, softmax_scale, out, lse, dout, dq, dk, dv, delta, p);
-  return bwd_grids_ok(*p, (long long)batch * seqlen_q * nheads, headdim) ? FA_OK : FA_ERR_INVALID_ARG;
+  return bwd_grids_ok(*p) ? FA_OK : FA_ERR_INVALID_ARG;
 }
 
 int plan_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -372,7 +371,7 @@ int plan_bwd_varlen(const void* q, const void* k, const void* v, const void* out
   p->cu_q = cu_seqlens_q;
   p->cu_k = cu_seqlens_k;
   p->lse_head_stride = total_q;
-  return bwd_grids_ok(*p, (long long)total_q * nheads, headdim) ? FA_OK : FA_ERR_INVALID_ARG;
+  return bwd_grids_ok(*p) ? FA_OK : FA_ERR_INVALID_ARG;
 }
 
 }  // namespace fa

@@ -125,8 +125,8 @@ int main(void) {
          FA_ERR_INVALID_ARG);
   EXPECT(fa_bwd(P, P, P, P, F, P, P, P, P, F, 1, 4, 4, 2, 32, 0.125f, 0, -1, -1, NULL, 0, FA_BF16, s),
          FA_ERR_UNSUPPORTED);
-  /* the delta grid at headdim 256 (8 rows per workgroup): 2^27 rows make 2^24 workgroups */
-  EXPECT(fa_bwd(P, P, P, P, F, P, P, P, P, F, 1, 1 << 24, 128, 8, 256, 0.0625f, 0, -1, -1, NULL, 0, FA_BF16, s),
+  /* the dQ grid: 2^23 (batch, head) pairs of two 128-row query tiles make 2^24 workgroups */
+  EXPECT(fa_bwd(P, P, P, P, F, P, P, P, P, F, 1 << 23, 256, 128, 1, 256, 0.0625f, 0, -1, -1, NULL, 0, FA_BF16, s),
          FA_ERR_INVALID_ARG);
 
   /* fa_bwd_varlen */
@@ -134,7 +134,8 @@ int main(void) {
                        0, FA_BF16, s), FA_ERR_INVALID_ARG);
   EXPECT(fa_bwd_varlen(P, P, P, P, F, P, P, P, P, F, I, I, 2, 8, 8, 10, 0, 4, 2, 128, 0.125f, 0, -1, -1, NULL,
                        0, FA_BF16, s), FA_ERR_INVALID_ARG);
-  EXPECT(fa_bwd_varlen(P, P, P, P, F, P, P, P, P, F, I, I, 2, 8, 8, 1 << 27, 12, 1, 1, 256, 0.0625f, 0, -1, -1,
+  /* the dQ grid: 2^23 sequences of up to two 128-row query tiles make 2^24 workgroups */
+  EXPECT(fa_bwd_varlen(P, P, P, P, F, P, P, P, P, F, I, I, 1 << 23, 256, 8, 12, 12, 1, 1, 256, 0.0625f, 0, -1, -1,
                        NULL, 0, FA_BF16, s), FA_ERR_INVALID_ARG);
 
   if (n_failed) {

@@ -105,15 +105,16 @@ static void grid_limits() {
   // combine: one workgroup per row
   EXPECT(fa::plan_combine(F, F, P, F, 1, 16777215, 1, 64, 2, FA_BF16, &c), FA_OK);
   EXPECT(fa::plan_combine(F, F, P, F, 1, 16777216, 1, 64, 2, FA_BF16, &c), FA_ERR_INVALID_ARG);
-  // backward delta: headdim 64 reduces 32 rows per workgroup, 128 16, 256 8
-  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 1, 16777215 * 8, 64, 1, 256, 0.1f, 0, -1, -1, nullptr, 0,
+  // backward: dQ runs one workgroup per 128 query rows, dK/dV one per 128 keys of every
+  // (batch, head); each grid holds at most 2^24 - 1 workgroups of 256 threads
+  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 8388607, 256, 128, 1, 128, 0.1f, 0, -1, -1, nullptr, 0,
                       FA_BF16, &bp), FA_OK);
-  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 1, 16777215 * 8 + 1, 64, 1, 256, 0.1f, 0, -1, -1, nullptr, 0,
+  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 8388608, 256, 128, 1, 128, 0.1f, 0, -1, -1, nullptr, 0,
                       FA_BF16, &bp), FA_ERR_INVALID_ARG);
-  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 1, 16777215 * 16, 64, 1, 128, 0.1f, 0, -1, -1, nullptr, 0,
+  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 8388608, 128, 256, 1, 64, 0.1f, 0, -1, -1, nullptr, 0,
+                      FA_BF16, &bp), FA_ERR_INVALID_ARG);
+  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 16777215, 128, 128, 1, 256, 0.1f, 0, -1, -1, nullptr, 0,
                       FA_BF16, &bp), FA_OK);
-  EXPECT(fa::plan_bwd(P, P, P, P, F, P, P, P, P, F, 1, 16777215 * 16 + 1, 64, 1, 128, 0.1f, 0, -1, -1, nullptr, 0,
-                      FA_BF16, &bp), FA_ERR_INVALID_ARG);
   // KV-cache combine grid: batch * heads * seqlen_q rows
   EXPECT(fa::plan_fwd_kvcache(P, P, P, I, nullptr, 256, 1, nullptr, nullptr, 0, nullptr, nullptr, 0, P, F, F, F, 1,
                               16777215, 1, 1, 1, 64, 0.1f, 1, -1, -1, nullptr, 0, FA_BF16, 1, &p, &c), FA_OK);

@@ -191,9 +191,8 @@ def test_binding_requires_gpu_tensors():
     ("fwd", dict(batch=1 << 17, seqlen_q=128, seqlen_k=128, nheads=128, headdim=64)),  # 2^24 four-wave groups
     ("fwd", dict(batch=493448, seqlen_q=4224, seqlen_k=4224, nheads=1, headdim=128)),  # 8388616 eight-wave groups
     ("combine", dict(seqlen_q=1 << 24)),                                             # one workgroup per row
-    ("bwd", dict(seqlen_q=(1 << 24) * 8, seqlen_k=64, nheads=1, headdim=256)),       # delta: 8 rows per group
-    ("bwd", dict(seqlen_q=(1 << 24) * 16, seqlen_k=64, nheads=1, headdim=128)),      # delta: 16 rows per group
-    ("bwd", dict(seqlen_q=(1 << 24) * 32, seqlen_k=64, nheads=1, headdim=64)),       # delta: 32 rows per group
+    ("bwd", dict(batch=1 << 23, seqlen_q=256, seqlen_k=128, nheads=1, headdim=128)),  # dQ: 2^24 query tiles
+    ("bwd", dict(batch=1 << 23, seqlen_q=128, seqlen_k=256, nheads=1, headdim=256)),  # dK/dV: 2^24 key tiles
     ("kvcache", dict(batch=1 << 21, nheads=8, nheads_k=8, num_splits=1, table=None, page=256)),  # combine rows
     ("splitkv", dict(batch=1 << 16, seqlen_q=1, seqlen_k=64, nheads=16, headdim=64)),  # decode workgroups (16 splits)
 ])
