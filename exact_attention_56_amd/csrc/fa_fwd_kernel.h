@@ -904,6 +904,16 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const int i_last = DEC ? (min(r0 + BR, rows_total) - 1) / G : min(r0 + BR, Sq) - 1;
   const int off = Sk - Sq;  // query i sits at key position i + off
   const int wl = p.window_left, wr = p.window_right;
+  // Positions of this wave's first and last row: the per-tile mask and ALiBi tests use
+  // them, so a tile that crosses a mask boundary only within the other waves' rows is a
+  // full tile for this wave (a wave of 32 rows meets about half as many boundary tiles
+  // as the block of 128).  A wave whose rows are all past the end takes the last row.
+#ifndef FA_WAVE_TESTS
+#define FA_WAVE_TESTS 1
+#endif
+  const int wr0 = r0 + wave * 32;
+  const int i0w = FA_WAVE_TESTS ? (DEC ? min(wr0, rows_total - 1) / G : min(wr0, Sq - 1)) : i0;
+  const int ilw = FA_WAVE_TESTS ? (DEC ? min(wr0 + 31, rows_total - 1) / G : min(wr0 + 31, Sq - 1)) : i_last;
 
   // Key tiles that any row of this block can see.
   int lo = key_lo, hi = key_hi - 1;
@@ -958,7 +968,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     qk_tile<HD, E>(s_a, lb.kl[0], st.qf);
     const int j0 = key_lo + t_begin * BC;
     st.m_run = prep_scores<ALIBI, HD == 256>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr,
-                                             i0, i_last, off, cs, slope, slope_c, half);
+                                             i0w, ilw, off, cs, slope, slope_c, half);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
 
@@ -978,18 +988,18 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     if (!group_a) half_step_barrier();
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
-      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0w, ilw,
                                       off);
-      pp_step<HD, ALIBI, E, false, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0,
-                                      i_last, off);
+      pp_step<HD, ALIBI, E, false, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0w,
+                                      ilw, off);
     }
     if (t + 1 < t_end) {
-      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, false, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0w, ilw,
                                       off);
-      pp_step<HD, ALIBI, E, true, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0,
-                                     i_last, off);
+      pp_step<HD, ALIBI, E, true, 1>(st, s_b, s_a, pf, t + 1, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0w,
+                                     ilw, off);
     } else if (t < t_end) {
-      pp_step<HD, ALIBI, E, true, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0, i_last,
+      pp_step<HD, ALIBI, E, true, 0>(st, s_a, s_b, pf, t, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr, i0w, ilw,
                                      off);
     }
     if (group_a) half_step_barrier();
@@ -997,26 +1007,37 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     int t = t_begin;
     for (; t + 2 < t_end; t += 2) {
       tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
-                                            i0, i_last, off);
+                                            i0w, ilw, off);
       tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
-                                            wr, i0, i_last, off);
+                                            wr, i0w, ilw, off);
     }
+    // The last step has no loads and no barrier: a wave that sees no key of the last tile
+    // (a window's first rows, the rows left of a causal diagonal) skips it.
+    auto wave_sees = [&](int tt) {
+      const int j0 = key_lo + tt * BC;
+      int klo = key_lo, khi = key_hi - 1;
+      if (wl >= 0) klo = max(klo, i0w + off - wl);
+      if (wr >= 0) khi = min(khi, ilw + off + wr);
+      return !FA_WAVE_TESTS || (j0 <= khi && j0 + BC - 1 >= klo);
+    };
     if (t + 1 < t_end) {  // two tiles left
       tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
-                                            i0, i_last, off);
-      tile_step<HD, NW, ALIBI, E, true, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
-                                           wr, i0, i_last, off);
+                                            i0w, ilw, off);
+      if (wave_sees(t + 1))
+        tile_step<HD, NW, ALIBI, E, true, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos,
+                                             wl, wr, i0w, ilw, off);
     } else if (t < t_end) {  // one tile left
-      tile_step<HD, NW, ALIBI, E, true, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
-                                           i0, i_last, off);
+      if (wave_sees(t))
+        tile_step<HD, NW, ALIBI, E, true, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
+                                             wr, i0w, ilw, off);
     }
   } else {
     for (int t = t_begin; t < t_end; t += 2) {
       tile_step<HD, NW, ALIBI, E, false, 0>(st, s_a, s_b, t, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl, wr,
-                                            i0, i_last, off);
+                                            i0w, ilw, off);
       if (t + 1 >= t_end) break;
       tile_step<HD, NW, ALIBI, E, false, 1>(st, s_b, s_a, t + 1, t_begin, kv, lb, half, slope_c, cs, slope, my_pos, wl,
-                                            wr, i0, i_last, off);
+                                            wr, i0w, ilw, off);
     }
   }
   f32x16* const oacc = st.oacc;
