@@ -321,8 +321,11 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 
     // P^T and dS^T.  Register r of block kb holds key j0 + 32 kb + 16 (r / 8) + 8 half + r % 8.
     const int j0 = t * DQ_TILE;
-    const bool full = (j0 + DQ_TILE <= Sk) && (wl < 0 || j0 >= i_last + off - wl) &&
-                      (wr < 0 || j0 + DQ_TILE - 1 <= i0 + off + wr);
+    // every (query of this wave, key of the tile) pair visible: the wave's own 32 rows
+    // decide, so a tile that a mask boundary crosses only in other waves' rows is full here
+    const int wi0 = min(i0 + 32 * wave, Sq - 1), wil = min(i0 + 32 * wave + 31, Sq - 1);
+    const bool full = (j0 + DQ_TILE <= Sk) && (wl < 0 || j0 >= wil + off - wl) &&
+                      (wr < 0 || j0 + DQ_TILE - 1 <= wi0 + off + wr);
     int vlo = 0, vspan = -1;  // visible keys of this row: [vlo, vlo + vspan]
     if (!full) {
       const int klo = wl < 0 ? 0 : max(0, my_pos - wl);
@@ -520,9 +523,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
 
       // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
       const int i0 = t * DKV_TILE;
-      // every (query of the tile, key of the block) pair visible, no query past the end
-      const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= j_last) &&
-                        (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= j0);
+      // every (query of the tile, key of this wave) pair visible, no query past the end:
+      // the wave's own 32 keys decide, as in dq_kernel
+      const int wj0 = min(j0 + 32 * wave, Sk - 1), wjl = min(j0 + 32 * wave + 31, Sk - 1);
+      const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= wjl) &&
+                        (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= wj0);
       x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
       // P and dS of the tile; the masked form only where the tile crosses a mask
       // boundary or the end (explicit branches, as in dq_kernel)
