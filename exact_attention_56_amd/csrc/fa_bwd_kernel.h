@@ -495,83 +495,96 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       load_d(lds + LOFF, t_begin);
       if (wave == 0) lraw = load_l(t_begin);
     }
-    for (int t = t_begin; t < t_end; ++t) {
-      const int cur = (t - t_begin) & 1;
-      wait_tile_loads<0>();
-      if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
-      __syncthreads();
-      if (t + 1 < t_end) {
-        lds_u8* nb = lds + (cur ^ 1) * BUF;
-        st.load(nb, nb + GOFF, t + 1);
-        load_d(nb + LOFF, t + 1);
-        if (wave == 0) lraw = load_l(t + 1);
-      }
-      const lds_u8* qt = lds + cur * BUF;
-      const lds_u8* gt = qt + GOFF;
-      const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
-
-      f32x16 s[DKV_QB], dp[DKV_QB];
-  #pragma unroll
-      for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
-  #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk)
-  #pragma unroll
-        for (int qb = 0; qb < DKV_QB; ++qb) {
-          s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
-          dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
+    // One query tile: S, dP, then P and dS (MASKED: with the mask, for tiles that a mask
+    // boundary or the end crosses), then dV and dK.
+    auto step = [&](int t, auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+        const int cur = (t - t_begin) & 1;
+        wait_tile_loads<0>();
+        if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
+        __syncthreads();
+        if (t + 1 < t_end) {
+          lds_u8* nb = lds + (cur ^ 1) * BUF;
+          st.load(nb, nb + GOFF, t + 1);
+          load_d(nb + LOFF, t + 1);
+          if (wave == 0) lraw = load_l(t + 1);
         }
+        const lds_u8* qt = lds + cur * BUF;
+        const lds_u8* gt = qt + GOFF;
+        const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
 
-      // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
-      const int i0 = t * DKV_TILE;
-      // every (query of the tile, key of this wave) pair visible, no query past the end:
-      // the wave's own 32 keys decide, as in dq_kernel
-      const int wj0 = min(j0 + 32 * wave, Sk - 1), wjl = min(j0 + 32 * wave + 31, Sk - 1);
-      const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= wjl) &&
-                        (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= wj0);
-      x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
-      // P and dS of the tile; the masked form only where the tile crosses a mask
-      // boundary or the end (explicit branches, as in dq_kernel)
-      auto scores = [&](auto masked) {
-        constexpr bool MASKED = decltype(masked)::value;
-  #pragma unroll
-        for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
-          const int qb = cc >> 1, ci = cc & 1;
-          const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
-          typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-          const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
-          const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
-          const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
-          const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
-          f32x16 pt, dt;
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
-            const float dd = e < 4 ? d_a[e] : d_b[e - 4];
-            const int qi = i0 + qrow + e;
-            float x = fmaf(s[qb][8 * ci + e], c, -l2);
-            if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
-            float pv = fast_exp2(x);
-            if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
-            pt[e] = pv;
-            dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+        f32x16 s[DKV_QB], dp[DKV_QB];
+    #pragma unroll
+        for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
+    #pragma unroll
+        for (int kk = 0; kk < HD / 16; ++kk)
+    #pragma unroll
+          for (int qb = 0; qb < DKV_QB; ++qb) {
+            s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
+            dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
           }
-          pf[cc] = pack_rows<E>(pt, 0);
-          dsf[cc] = pack_rows<E>(dt, 0);
-        }
-      };
-      if (full)
-        scores(std::false_type{});
-      else
-        scores(std::true_type{});
 
-  #pragma unroll
-      for (int cc = 0; cc < 2 * DKV_QB; ++cc)
-  #pragma unroll
-        for (int db = 0; db < HD / 32; ++db) {
-          dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
-          dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
+        // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
+        const int i0 = t * DKV_TILE;
+        x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
+        {
+    #pragma unroll
+          for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+            const int qb = cc >> 1, ci = cc & 1;
+            const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
+            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+            const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+            const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+            const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+            const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+            f32x16 pt, dt;
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
+              const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+              const int qi = i0 + qrow + e;
+              float x = fmaf(s[qb][8 * ci + e], c, -l2);
+              if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+              float pv = fast_exp2(x);
+              if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+              pt[e] = pv;
+              dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+            }
+            pf[cc] = pack_rows<E>(pt, 0);
+            dsf[cc] = pack_rows<E>(dt, 0);
+          }
         }
+
+    #pragma unroll
+        for (int cc = 0; cc < 2 * DKV_QB; ++cc)
+    #pragma unroll
+          for (int db = 0; db < HD / 32; ++db) {
+            dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
+            dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
+          }
+    };
+    // The tiles every (query, key of this wave) pair of which is visible, with no query
+    // past the end, form one range [tf_begin, tf_end): run there without the mask, in a
+    // loop of its own, so that the mask costs nothing on them and the loop body is one
+    // block (an explicit branch per tile cost the products' overlap with the
+    // exponentials; the compiler's own select computed the mask on every tile).  Every
+    // wave passes the same number of steps, each with one barrier.
+    const int wj0 = min(j0 + 32 * wave, Sk - 1), wjl = min(j0 + 32 * wave + 31, Sk - 1);
+    int tf_lo = 0, tf_hi = Sq / DKV_TILE;  // full tiles: tf_lo <= t < tf_hi
+    if (wr >= 0) {
+      const int x = wjl - off - wr;  // needs t * DKV_TILE >= x
+      tf_lo = x <= 0 ? 0 : (x + DKV_TILE - 1) / DKV_TILE;
     }
+    if (wl >= 0) {
+      const int y = wj0 - off + wl - DKV_TILE + 1;  // needs t * DKV_TILE <= y
+      tf_hi = min(tf_hi, y < 0 ? 0 : y / DKV_TILE + 1);
+    }
+    const int tf_begin = min(max(t_begin, tf_lo), t_end);
+    const int tf_end = max(tf_begin, min(t_end, tf_hi));
+    int t = t_begin;
+    for (; t < tf_begin; ++t) step(t, std::true_type{});
+    for (; t < tf_end; ++t) step(t, std::false_type{});
+    for (; t < t_end; ++t) step(t, std::true_type{});
   }  // query heads of the group
   if (my_k < Sk) {
     store_rows<HD, E>(p.dk + koff, rsk, my_k, dk, p.scale, half);
