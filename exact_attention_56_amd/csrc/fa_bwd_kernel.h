@@ -300,7 +300,10 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) dq[db] = f32x16{};
 
-  for (int t = t_begin; t < t_end; ++t) {
+  // One key tile: S^T, dP^T, then P^T and dS^T (MASKED: with the mask, for tiles that a
+  // mask boundary or the end crosses), then dQ^T.
+  auto step = [&](int t, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = (t - t_begin) & 1;
     wait_tile_loads<0>();
     __syncthreads();  // tile t is in LDS; everyone is done with the other buffer
@@ -321,47 +324,32 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 
     // P^T and dS^T.  Register r of block kb holds key j0 + 32 kb + 16 (r / 8) + 8 half + r % 8.
     const int j0 = t * DQ_TILE;
-    // every (query of this wave, key of the tile) pair visible: the wave's own 32 rows
-    // decide, so a tile that a mask boundary crosses only in other waves' rows is full here
-    const int wi0 = min(i0 + 32 * wave, Sq - 1), wil = min(i0 + 32 * wave + 31, Sq - 1);
-    const bool full = (j0 + DQ_TILE <= Sk) && (wl < 0 || j0 >= wil + off - wl) &&
-                      (wr < 0 || j0 + DQ_TILE - 1 <= wi0 + off + wr);
     int vlo = 0, vspan = -1;  // visible keys of this row: [vlo, vlo + vspan]
-    if (!full) {
+    if constexpr (MASKED) {
       const int klo = wl < 0 ? 0 : max(0, my_pos - wl);
       const int khi = wr < 0 ? Sk - 1 : min(Sk - 1, my_pos + wr);
       vlo = klo;
       vspan = khi - klo;
     }
     x8<E> dsf[4];
-    // P^T and dS^T of the tile; the masked form only where the tile crosses a mask
-    // boundary or the end (two explicit branches: left to itself the compiler computed
-    // the mask of every score and selected, which was half the vector work of a full tile)
-    auto scores = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int ci = 0; ci < 4; ++ci) {
-        const int kb = ci >> 1, r0 = 8 * (ci & 1);
-        f32x16 tmp;
+    for (int ci = 0; ci < 4; ++ci) {
+      const int kb = ci >> 1, r0 = 8 * (ci & 1);
+      f32x16 tmp;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = j0 + 32 * kb + 16 * (r0 / 8) + 8 * half + e;
-          float x = fmaf(s[kb][r0 + e], c, -lrow2);
-          if constexpr (ALIBI) x += alibi_log2(slope2, my_pos, key);
-          float pv = fast_exp2(x);
-          if constexpr (MASKED) {
-            const bool vis = vspan >= 0 && (uint32_t)(key - vlo) <= (uint32_t)vspan && my_q < Sq;
-            pv = vis ? pv : 0.f;
-          }
-          tmp[e] = pv * (dp[kb][r0 + e] - drow);
+      for (int e = 0; e < 8; ++e) {
+        const int key = j0 + 32 * kb + 16 * (r0 / 8) + 8 * half + e;
+        float x = fmaf(s[kb][r0 + e], c, -lrow2);
+        if constexpr (ALIBI) x += alibi_log2(slope2, my_pos, key);
+        float pv = fast_exp2(x);
+        if constexpr (MASKED) {
+          const bool vis = vspan >= 0 && (uint32_t)(key - vlo) <= (uint32_t)vspan && my_q < Sq;
+          pv = vis ? pv : 0.f;
         }
-        dsf[ci] = pack_rows<E>(tmp, 0);
+        tmp[e] = pv * (dp[kb][r0 + e] - drow);
       }
-    };
-    if (full)
-      scores(std::false_type{});
-    else
-      scores(std::true_type{});
+      dsf[ci] = pack_rows<E>(tmp, 0);
+    }
 
     // dQ^T += K^T dS^T
 #pragma unroll
@@ -369,7 +357,26 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 #pragma unroll
       for (int db = 0; db < HD / 32; ++db)
         dq[db] = mfma32(tr_operand<KP, E>(kt, lane, db, ci), dsf[ci], dq[db]);
+  };
+  // The tiles every (query of this wave, key) pair of which is visible, with no key past
+  // the end, form one range [tf_begin, tf_end): run there without the mask, in a loop of
+  // its own, as in dkdv_kernel.  Every wave passes the same number of steps.
+  const int wi0 = min(i0 + 32 * wave, Sq - 1), wil = min(i0 + 32 * wave + 31, Sq - 1);
+  int tf_lo = 0, tf_hi = Sk / DQ_TILE;  // full tiles: tf_lo <= t < tf_hi
+  if (wl >= 0) {
+    const int x = wil + off - wl;  // needs t * DQ_TILE >= x
+    tf_lo = x <= 0 ? 0 : (x + DQ_TILE - 1) / DQ_TILE;
   }
+  if (wr >= 0) {
+    const int y = wi0 + off + wr - DQ_TILE + 1;  // needs t * DQ_TILE <= y
+    tf_hi = min(tf_hi, y < 0 ? 0 : y / DQ_TILE + 1);
+  }
+  const int tf_begin = min(max(t_begin, tf_lo), t_end);
+  const int tf_end = max(tf_begin, min(t_end, tf_hi));
+  int t = t_begin;
+  for (; t < tf_begin; ++t) step(t, std::true_type{});
+  for (; t < tf_end; ++t) step(t, std::false_type{});
+  for (; t < t_end; ++t) step(t, std::true_type{});
   if (my_q < Sq) store_rows<HD, E>(p.dq + qoff, rs, my_q, dq, p.scale, half);
 #endif
 }
@@ -499,69 +506,67 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     // boundary or the end crosses), then dV and dK.
     auto step = [&](int t, auto masked) {
       constexpr bool MASKED = decltype(masked)::value;
-        const int cur = (t - t_begin) & 1;
-        wait_tile_loads<0>();
-        if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
-        __syncthreads();
-        if (t + 1 < t_end) {
-          lds_u8* nb = lds + (cur ^ 1) * BUF;
-          st.load(nb, nb + GOFF, t + 1);
-          load_d(nb + LOFF, t + 1);
-          if (wave == 0) lraw = load_l(t + 1);
-        }
-        const lds_u8* qt = lds + cur * BUF;
-        const lds_u8* gt = qt + GOFF;
-        const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
+      const int cur = (t - t_begin) & 1;
+      wait_tile_loads<0>();
+      if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
+      __syncthreads();
+      if (t + 1 < t_end) {
+        lds_u8* nb = lds + (cur ^ 1) * BUF;
+        st.load(nb, nb + GOFF, t + 1);
+        load_d(nb + LOFF, t + 1);
+        if (wave == 0) lraw = load_l(t + 1);
+      }
+      const lds_u8* qt = lds + cur * BUF;
+      const lds_u8* gt = qt + GOFF;
+      const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
 
-        f32x16 s[DKV_QB], dp[DKV_QB];
-    #pragma unroll
-        for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
-    #pragma unroll
-        for (int kk = 0; kk < HD / 16; ++kk)
-    #pragma unroll
-          for (int qb = 0; qb < DKV_QB; ++qb) {
-            s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
-            dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
-          }
-
-        // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
-        const int i0 = t * DKV_TILE;
-        x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
-        {
-    #pragma unroll
-          for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
-            const int qb = cc >> 1, ci = cc & 1;
-            const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
-            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-            const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
-            const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
-            const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
-            const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
-            f32x16 pt, dt;
-    #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
-              const float dd = e < 4 ? d_a[e] : d_b[e - 4];
-              const int qi = i0 + qrow + e;
-              float x = fmaf(s[qb][8 * ci + e], c, -l2);
-              if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
-              float pv = fast_exp2(x);
-              if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
-              pt[e] = pv;
-              dt[e] = pv * (dp[qb][8 * ci + e] - dd);
-            }
-            pf[cc] = pack_rows<E>(pt, 0);
-            dsf[cc] = pack_rows<E>(dt, 0);
-          }
+      f32x16 s[DKV_QB], dp[DKV_QB];
+#pragma unroll
+      for (int qb = 0; qb < DKV_QB; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < DKV_QB; ++qb) {
+          s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
+          dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
         }
 
-    #pragma unroll
-        for (int cc = 0; cc < 2 * DKV_QB; ++cc)
-    #pragma unroll
-          for (int db = 0; db < HD / 32; ++db) {
-            dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
-            dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
-          }
+      // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
+      const int i0 = t * DKV_TILE;
+      x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
+#pragma unroll
+      for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+        const int qb = cc >> 1, ci = cc & 1;
+        const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+        const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+        const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+        const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+        f32x16 pt, dt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
+          const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+          const int qi = i0 + qrow + e;
+          float x = fmaf(s[qb][8 * ci + e], c, -l2);
+          if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+          float pv = fast_exp2(x);
+          if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+          pt[e] = pv;
+          dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+        }
+        pf[cc] = pack_rows<E>(pt, 0);
+        dsf[cc] = pack_rows<E>(dt, 0);
+      }
+
+#pragma unroll
+      for (int cc = 0; cc < 2 * DKV_QB; ++cc)
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db) {
+          dv[db] = mfma32(tr_operand<QP, E>(gt, lane, db, cc), pf[cc], dv[db]);
+          dk[db] = mfma32(tr_operand<QP, E>(qt, lane, db, cc), dsf[cc], dk[db]);
+        }
     };
     // The tiles every (query, key of this wave) pair of which is visible, with no query
     // past the end, form one range [tf_begin, tf_end): run there without the mask, in a
