@@ -502,10 +502,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       load_d(lds + LOFF, t_begin);
       if (wave == 0) lraw = load_l(t_begin);
     }
-    // One query tile: S, dP, then P and dS (MASKED: with the mask, for tiles that a mask
-    // boundary or the end crosses), then dV and dK.
-    auto step = [&](int t, auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
+    // One query tile: S, dP, then P and dS, then dV and dK.  MODE 0: no mask (every pair
+    // visible); 1: with the mask (a mask boundary or the end crosses the tile); 2: which of
+    // the two is decided per tile, by a branch around P and dS (headdim 256, below).
+    auto step = [&](int t, auto mode) {
+      constexpr int MODE = decltype(mode)::value;
       const int cur = (t - t_begin) & 1;
       wait_tile_loads<0>();
       if (wave == 0) put_l(lds + cur * BUF + LOFF, lraw);
@@ -534,30 +535,44 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
       const int i0 = t * DKV_TILE;
       x8<E> pf[2 * DKV_QB], dsf[2 * DKV_QB];
+      auto scores = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
-        const int qb = cc >> 1, ci = cc & 1;
-        const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
-        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-        const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
-        const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
-        const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
-        const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
-        f32x16 pt, dt;
+        for (int cc = 0; cc < 2 * DKV_QB; ++cc) {
+          const int qb = cc >> 1, ci = cc & 1;
+          const int qrow = 16 * cc + 8 * half;  // first tile row of this chunk
+          typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+          const f32x4 l_a = *(const lds_f32x4*)(lt + qrow);
+          const f32x4 l_b = *(const lds_f32x4*)(lt + qrow + 4);
+          const f32x4 d_a = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow);
+          const f32x4 d_b = *(const lds_f32x4*)(lt + LDBYTES / 4 + qrow + 4);
+          f32x16 pt, dt;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
-          const float dd = e < 4 ? d_a[e] : d_b[e - 4];
-          const int qi = i0 + qrow + e;
-          float x = fmaf(s[qb][8 * ci + e], c, -l2);
-          if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
-          float pv = fast_exp2(x);
-          if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
-          pt[e] = pv;
-          dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+          for (int e = 0; e < 8; ++e) {
+            const float l2 = e < 4 ? l_a[e] : l_b[e - 4];  // L in log2 units, +inf: P = 0
+            const float dd = e < 4 ? d_a[e] : d_b[e - 4];
+            const int qi = i0 + qrow + e;
+            float x = fmaf(s[qb][8 * ci + e], c, -l2);
+            if constexpr (ALIBI) x += alibi_log2(slope2, qi + off, my_k);
+            float pv = fast_exp2(x);
+            if constexpr (MASKED) pv = ((uint32_t)(qi - qlo) <= (uint32_t)(qhi - qlo) && qlo <= qhi) ? pv : 0.f;
+            pt[e] = pv;
+            dt[e] = pv * (dp[qb][8 * ci + e] - dd);
+          }
+          pf[cc] = pack_rows<E>(pt, 0);
+          dsf[cc] = pack_rows<E>(dt, 0);
         }
-        pf[cc] = pack_rows<E>(pt, 0);
-        dsf[cc] = pack_rows<E>(dt, 0);
+      };
+      if constexpr (MODE == 2) {
+        const int wj0 = min(j0 + 32 * wave, Sk - 1), wjl = min(j0 + 32 * wave + 31, Sk - 1);
+        const bool full = (i0 + DKV_TILE <= Sq) && (wr < 0 || i0 + off + wr >= wjl) &&
+                          (wl < 0 || i0 + DKV_TILE - 1 + off - wl <= wj0);
+        if (full)
+          scores(std::false_type{});
+        else
+          scores(std::true_type{});
+      } else {
+        scores(std::bool_constant<MODE == 1>{});
       }
 
 #pragma unroll
@@ -586,10 +601,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     }
     const int tf_begin = min(max(t_begin, tf_lo), t_end);
     const int tf_end = max(tf_begin, min(t_end, tf_hi));
-    int t = t_begin;
-    for (; t < tf_begin; ++t) step(t, std::true_type{});
-    for (; t < tf_end; ++t) step(t, std::false_type{});
-    for (; t < t_end; ++t) step(t, std::true_type{});
+    // (at headdim 256 the three loops cost the kernel a third more time: its registers
+    // are full, and the compiler copied the accumulators between the loops; one loop with
+    // the branch around P and dS there)
+    if constexpr (HD == 256) {
+      for (int t = t_begin; t < t_end; ++t) step(t, std::integral_constant<int, 2>{});
+    } else {
+      int t = t_begin;
+      for (; t < tf_begin; ++t) step(t, std::integral_constant<int, 1>{});
+      for (; t < tf_end; ++t) step(t, std::integral_constant<int, 0>{});
+      for (; t < t_end; ++t) step(t, std::integral_constant<int, 1>{});
+    }
   }  // query heads of the group
   if (my_k < Sk) {
     store_rows<HD, E>(p.dk + koff, rsk, my_k, dk, p.scale, half);
