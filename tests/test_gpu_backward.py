@@ -42,6 +42,11 @@ BWD_CASES = [
     (1, 2, 257, 129, 256, True, -1, -1, True, None),
     (2, 1, 130, 130, 256, True, 30, 0, False, None),
     (1, 1, 1024, 1024, 256, False, -1, -1, False, None),
+    # windows wide enough that each wave has masked tiles, then tiles it sees in full, then
+    # masked tiles again (the three loop ranges of both passes)
+    (1, 2, 1024, 1024, 128, True, 300, 0, False, None),
+    (1, 2, 700, 900, 64, False, 200, 150, True, None),
+    (1, 1, 600, 600, 256, True, 200, 0, False, None),
 ]
 
 
