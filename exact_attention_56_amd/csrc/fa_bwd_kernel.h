@@ -300,15 +300,18 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db) dq[db] = f32x16{};
 
-  // One key tile: S^T, dP^T, then P^T and dS^T (MASKED: with the mask, for tiles that a
-  // mask boundary or the end crosses), then dQ^T.
-  auto step = [&](int t, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
+  // One key tile: S^T, dP^T, then P^T and dS^T, then dQ^T.  MODE 0: every pair visible;
+  // 1: with the mask (a mask boundary or the end crosses the tile); 2: no key of the tile
+  // is visible to this wave: only its share of the loads and the barrier.
+  auto step = [&](int t, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool MASKED = MODE == 1;
     const int cur = (t - t_begin) & 1;
     wait_tile_loads<0>();
     __syncthreads();  // tile t is in LDS; everyone is done with the other buffer
     if (t + 1 < t_end)
       st.load(lds + (cur ^ 1) * Stream::ABYTES, lds + 2 * Stream::ABYTES + (cur ^ 1) * Stream::BBYTES, t + 1);
+    if constexpr (MODE == 2) return;
     const lds_u8* kt = lds + cur * Stream::ABYTES;
     const lds_u8* vt = lds + 2 * Stream::ABYTES + cur * Stream::BBYTES;
 
@@ -360,8 +363,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
   };
   // The tiles every (query of this wave, key) pair of which is visible, with no key past
   // the end, form one range [tf_begin, tf_end): run there without the mask, in a loop of
-  // its own, as in dkdv_kernel.  Every wave passes the same number of steps.
+  // its own, as in dkdv_kernel; the tiles with any key visible to the wave form a range
+  // [tv_begin, tv_end) around it, and outside that the wave only loads and meets the
+  // barrier (under a causal mask the block's first rows see one 64-key tile fewer than
+  // its last).  Every wave passes the same number of steps.
   const int wi0 = min(i0 + 32 * wave, Sq - 1), wil = min(i0 + 32 * wave + 31, Sq - 1);
+  const int kvlo = wl < 0 ? 0 : max(0, wi0 + off - wl), kvhi = wr < 0 ? Sk - 1 : min(Sk - 1, wil + off + wr);
+  const int tv_begin = kvhi < kvlo ? t_end : min(max(t_begin, kvlo / DQ_TILE), t_end);
+  const int tv_end = kvhi < kvlo ? t_end : max(tv_begin, min(t_end, kvhi / DQ_TILE + 1));
   int tf_lo = 0, tf_hi = Sk / DQ_TILE;  // full tiles: tf_lo <= t < tf_hi
   if (wl >= 0) {
     const int x = wil + off - wl;  // needs t * DQ_TILE >= x
@@ -371,12 +380,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
     const int y = wi0 + off + wr - DQ_TILE + 1;  // needs t * DQ_TILE <= y
     tf_hi = min(tf_hi, y < 0 ? 0 : y / DQ_TILE + 1);
   }
-  const int tf_begin = min(max(t_begin, tf_lo), t_end);
-  const int tf_end = max(tf_begin, min(t_end, tf_hi));
+  const int tf_begin = min(max(tv_begin, tf_lo), tv_end);
+  const int tf_end = max(tf_begin, min(tv_end, tf_hi));
   int t = t_begin;
-  for (; t < tf_begin; ++t) step(t, std::true_type{});
-  for (; t < tf_end; ++t) step(t, std::false_type{});
-  for (; t < t_end; ++t) step(t, std::true_type{});
+  for (; t < tv_begin; ++t) step(t, std::integral_constant<int, 2>{});
+  for (; t < tf_begin; ++t) step(t, std::integral_constant<int, 1>{});
+  for (; t < tf_end; ++t) step(t, std::integral_constant<int, 0>{});
+  for (; t < tv_end; ++t) step(t, std::integral_constant<int, 1>{});
+  for (; t < t_end; ++t) step(t, std::integral_constant<int, 2>{});
   if (my_q < Sq) store_rows<HD, E>(p.dq + qoff, rs, my_q, dq, p.scale, half);
 #endif
 }
