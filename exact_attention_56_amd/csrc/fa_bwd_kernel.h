@@ -515,7 +515,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
     }
     // One query tile: S, dP, then P and dS, then dV and dK.  MODE 0: no mask (every pair
     // visible); 1: with the mask (a mask boundary or the end crosses the tile); 2: which of
-    // the two is decided per tile, by a branch around P and dS (headdim 256, below).
+    // the two is decided per tile, by a branch around P and dS (headdim 256, below); 3: no
+    // pair visible: only this wave's share of the loads and the barrier.
     auto step = [&](int t, auto mode) {
       constexpr int MODE = decltype(mode)::value;
       const int cur = (t - t_begin) & 1;
@@ -528,6 +529,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
         load_d(nb + LOFF, t + 1);
         if (wave == 0) lraw = load_l(t + 1);
       }
+      if constexpr (MODE == 3) return;  // no query of the tile sees a key of this wave
       const lds_u8* qt = lds + cur * BUF;
       const lds_u8* gt = qt + GOFF;
       const __attribute__((address_space(3))) float* lt = (const __attribute__((address_space(3))) float*)(qt + LOFF);
@@ -610,8 +612,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       const int y = wj0 - off + wl - DKV_TILE + 1;  // needs t * DKV_TILE <= y
       tf_hi = min(tf_hi, y < 0 ? 0 : y / DKV_TILE + 1);
     }
-    const int tf_begin = min(max(t_begin, tf_lo), t_end);
-    const int tf_end = max(tf_begin, min(t_end, tf_hi));
+    // the tiles with any query that sees a key of this wave: [tv_begin, tv_end)
+    const int qvlo = wr < 0 ? 0 : max(0, wj0 - off - wr), qvhi = wl < 0 ? Sq - 1 : min(Sq - 1, wjl - off + wl);
+    const int tv_begin = qvhi < qvlo ? t_end : min(max(t_begin, qvlo / DKV_TILE), t_end);
+    const int tv_end = qvhi < qvlo ? t_end : max(tv_begin, min(t_end, qvhi / DKV_TILE + 1));
+    const int tf_begin = min(max(tv_begin, tf_lo), tv_end);
+    const int tf_end = max(tf_begin, min(tv_end, tf_hi));
     // (at headdim 256 the three loops cost the kernel a third more time: its registers
     // are full, and the compiler copied the accumulators between the loops; one loop with
     // the branch around P and dS there)
@@ -619,9 +625,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
       for (int t = t_begin; t < t_end; ++t) step(t, std::integral_constant<int, 2>{});
     } else {
       int t = t_begin;
+      for (; t < tv_begin; ++t) step(t, std::integral_constant<int, 3>{});
       for (; t < tf_begin; ++t) step(t, std::integral_constant<int, 1>{});
       for (; t < tf_end; ++t) step(t, std::integral_constant<int, 0>{});
-      for (; t < t_end; ++t) step(t, std::integral_constant<int, 1>{});
+      for (; t < tv_end; ++t) step(t, std::integral_constant<int, 1>{});
+      for (; t < t_end; ++t) step(t, std::integral_constant<int, 3>{});
     }
   }  // query heads of the group
   if (my_k < Sk) {
