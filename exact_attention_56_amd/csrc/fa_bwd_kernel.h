@@ -113,8 +113,8 @@ template <int PITCH, typename E>
 __device__ __forceinline__ x8<E> tr_operand(const lds_u8* tile, int lane, int db, int ci) {
   const int g = lane >> 4, r = lane & 15;
   const lds_u8* p = tile + (8 * (g >> 1) + (r >> 2)) * PITCH + (16 * (g & 1) + 4 * (r & 3)) * 2;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * ci * PITCH + 64 * db));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (16 * ci + 4) * PITCH + 64 * db));
+  const s16x4 lo = lds_read_tr(p + 16 * ci * PITCH + 64 * db);
+  const s16x4 hi = lds_read_tr(p + (16 * ci + 4) * PITCH + 64 * db);
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   return __builtin_bit_cast(x8<E>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }

@@ -98,15 +98,21 @@ constexpr int BLOCK_THREADS = 256;
 // neither causal mask nor window from 2048 query rows, and with a plain causal mask
 // from 8192; four otherwise.  Measured against four waves (MI355X, 16 heads x 128,
 // batch 16384 / seqlen): unmasked +2.5% at 2k, +6-7% at 4k-16k; causal -4% at 2k,
-// even at 4k, +5% at 16k.
+// even at 4k, +5% at 16k.  With ALiBi under a causal mask four waves at every length:
+// that kernel runs the key tiles right to left (launch_fwd_hd), +10% at 16k against
+// the eight-wave kernel's left-to-right order.
 #ifndef FA_EIGHT_WAVE_ROWS
 #define FA_EIGHT_WAVE_ROWS 2048
 #endif
 #ifndef FA_EIGHT_WAVE_CAUSAL_ROWS
 #define FA_EIGHT_WAVE_CAUSAL_ROWS 8192
 #endif
-inline int fwd_waves(int headdim, bool split, int window_left, int window_right, int seqlen_q) {
+#ifndef FA_ALIBI_CAUSAL_4W
+#define FA_ALIBI_CAUSAL_4W 1
+#endif
+inline int fwd_waves(int headdim, bool split, int window_left, int window_right, int seqlen_q, bool alibi) {
   if (headdim != 128 || split || window_left >= 0) return 4;
+  if (FA_ALIBI_CAUSAL_4W && alibi && window_right == 0) return 4;
   if (window_right < 0) return seqlen_q >= FA_EIGHT_WAVE_ROWS ? 8 : 4;
   return (window_right == 0 && seqlen_q >= FA_EIGHT_WAVE_CAUSAL_ROWS) ? 8 : 4;
 }

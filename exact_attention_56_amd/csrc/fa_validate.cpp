@@ -112,7 +112,7 @@ int prepare(const void* q, const void* k, const void* v, int batch, int seqlen_q
 
 // Grid of the matrix-core forward over p (eight-wave launches use 256-row tiles).
 bool fwd_grid_ok(const FwdParams& p, int headdim, bool split) {
-  const int nw = fwd_waves(headdim, split, p.window_left, p.window_right, p.seqlen_q);
+  const int nw = fwd_waves(headdim, split, p.window_left, p.window_right, p.seqlen_q, p.alibi != nullptr);
   const long long tiles = ceil_div(p.seqlen_q, 32 * nw);
   return grid_ok((long long)p.batch * p.nheads * tiles * (split ? p.num_splits : 1), 64 * nw);
 }

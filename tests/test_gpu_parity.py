@@ -77,6 +77,13 @@ FWD_CASES = [
     (1, 1, 8192 + 40, 8192 + 40, 128, True, -1, -1, False, None),
     (1, 1, 8200, 9100, 128, True, -1, -1, True, None),
     (1, 1, 8191, 8191, 128, True, -1, -1, False, None),
+    # ALiBi under a causal mask (key tiles right to left, no per-tile maximum): many tiles,
+    # rows that see no key (Sq > Sk), a left window, a negative scale (scores that rise
+    # from tile to tile refit the reference)
+    (1, 8, 1500, 1500, 128, True, -1, -1, True, None),
+    (1, 4, 700, 400, 64, True, -1, -1, True, None),
+    (2, 8, 1030, 1100, 64, True, 256, 0, True, None),
+    (1, 2, 600, 600, 64, True, -1, -1, True, -0.1),
 ]
 
 
