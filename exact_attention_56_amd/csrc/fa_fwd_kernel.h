@@ -60,10 +60,18 @@ constexpr float RESCALE_TH = 8.0f;  // log2 units: keep a stale max while p <= 2
 #define FA_NOMAX 1
 #endif
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // buffer offset past any tile: reads as zero
+// The ALiBi kernels with the keys right to left (causal; headdim 64 and 128) add the
+// linear bias on the matrix cores: the K rows' pad slots hold each row's key index and
+// the Q side a split of the bias step (qk_tile); the loads then leave the pad slots alone.
+#ifndef FA_ALIBI_AUG
+#define FA_ALIBI_AUG 1
+#endif
+constexpr uint32_t PAD_KEEP = 0xffffffffu;  // K slot offset: a pad slot the loads skip
 
 // LDS tiles.  A K row keeps its HD/8 16-byte chunks plus one pad slot (16 lanes
 // reading one chunk column of 16 rows then hit 16 distinct 4-bank groups); the pad
-// slot is filled with zeros by an out-of-range load.  V is stored in 64-byte column
+// slot is filled with zeros by an out-of-range load (or, in the causal ALiBi kernels,
+// holds the row's key index for the bias product, see qk_tile).  V is stored in 64-byte column
 // blocks: block db holds columns 32db..32db+31 of the tile's 64 rows, 64 bytes per row,
 // so the 32 lanes that one half of a transpose read serves (4 rows x 32 columns) read
 // 256 contiguous bytes, all 64 banks once, and the tile needs no pad slot.  (Padded
@@ -151,6 +159,9 @@ template <int HD, int NW, bool REV_ = false>
 struct KVStream {
   using T = Tile<HD, NW>;
   static constexpr bool REV = REV_;
+  // the pad slots hold key indices (not at headdim 256: its one-wave-per-SIMD kernel ran
+  // 15% slower with the two extra products, against +5% on the local ALiBi workload)
+  static constexpr bool KEEP_PAD = REV && FA_ALIBI_AUG && HD != 256;
   const uint16_t* kbase;
   const uint16_t* vbase;
   int key_lo, key_hi, row_bytes;
@@ -169,7 +180,8 @@ struct KVStream {
     for (int i = 0; i < T::KPW; ++i) {
       const int slot = 64 * (lw + 4 * i) + lane;
       const int row = slot / T::KCH, ch = slot % T::KCH;
-      koff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(k_lds_row(row) * row_bytes + ch * 16) : OOB_OFFSET;
+      koff[i] = (row < BC && ch < T::CPR) ? (uint32_t)(k_lds_row(row) * row_bytes + ch * 16)
+                : (KEEP_PAD && row < BC) ? PAD_KEEP : OOB_OFFSET;
     }
 #pragma unroll
     for (int i = 0; i < T::VPW; ++i) {
@@ -197,8 +209,12 @@ struct KVStream {
     const auto rs = tile_rsrc(kbase + (long)j0 * row_stride, none ? 0 : key_hi - j0, row_bytes);
 #pragma unroll
     for (int i = 0; i < T::KPW; ++i)
-      if (lw + 4 * i < T::KCH)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)koff[i], 0, 0, 0);
+      if (lw + 4 * i < T::KCH) {
+        // (a lane of a skipped pad slot writes nothing: direct loads place each lane's
+        // 16 bytes by its lane index)
+        if (!KEEP_PAD || koff[i] != PAD_KEEP)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + 1024 * (lw + 4 * i), 16, (int)koff[i], 0, 0, 0);
+      }
   }
   __device__ __forceinline__ void load_v(lds_u8* dst, int t) const {
     if (!loads_v) return;
@@ -259,8 +275,12 @@ __device__ __forceinline__ void wait_tile_loads() {
 
 // S^T (64 keys x 32 queries of this wave) = K_tile Q^T, two 32x32 blocks.
 // `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
-template <int HD, typename E>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const x8<E> (&qf)[HD / 16]) {
+// AUG: one more product per block adds g * (key index in the tile) to every score: A is
+// the rows' pad slots (key index k three times, then zeros), B this lane's `baug` (g in
+// three parts of E, half-wave 0; zeros in half-wave 1), at byte offset aug_off from kt.
+template <int HD, typename E, bool AUG = false>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const x8<E> (&qf)[HD / 16],
+                                        const x8<E>& baug = x8<E>{}, int aug_off = 0) {
   using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   s[0] = f32x16{};
   s[1] = f32x16{};
@@ -270,6 +290,13 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
     for (int kb = 0; kb < 2; ++kb) {
       const x8<E> a = *(const __attribute__((address_space(3))) x8<E>*)(kt + 32 * kb * T::KPITCH + 32 * kk);
       s[kb] = mfma32(a, qf[kk], s[kb]);
+    }
+  }
+  if constexpr (AUG) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const x8<E> a = *(const __attribute__((address_space(3))) x8<E>*)(kt + aug_off + 32 * kb * T::KPITCH);
+      s[kb] = mfma32(a, baug, s[kb]);
     }
   }
 }
@@ -381,6 +408,8 @@ struct FwdState {
   float m_run;              // reference maximum of the exponentials (log2 units)
   float l_run;              // this lane's share of the row sum against m_run
   float b_cur;              // log2 offset to add to the stored scores of the tile in s_cur (ALiBi)
+  x8<E> baug;               // B operand of the bias product (qk_tile, AUG)
+  int aug_off;              // byte offset of this lane's pad slot from its K operand address
 };
 
 // Prepare the raw S^T of tile t (first key j0): with ALiBi fold in the bias (bias_tile)
@@ -390,14 +419,19 @@ struct FwdState {
 // slope_c = slope / cs is formed once per row by the caller, except at headdim 256
 // (DIV): there the one-wave-per-SIMD kernel ran 17% slower with any other form than
 // with both divisions of bias_tile on every tile.
-template <bool ALIBI, bool DIV = false>
+// AUG (causal ALiBi, keys right to left): the products already added slope/cs times the
+// key's index in the tile, so only the offset b = slope * (j0 - position) remains; every
+// visible key is at or left of the row's position, where that linear form is exact.
+template <bool ALIBI, bool DIV = false, bool AUG = false>
 __device__ __forceinline__ float prep_scores(f32x16 (&s)[2], float& b, int j0, int key_hi, int my_pos, int wl, int wr,
                                              int i0, int i_last, int off, float cs, float slope, float slope_c,
                                              int half) {
   const bool full =
       (j0 + BC <= key_hi) && (wl < 0 || j0 >= i_last + off - wl) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr);
   b = 0.f;
-  if constexpr (ALIBI) {
+  if constexpr (AUG) {
+    b = slope * (float)(j0 - my_pos);
+  } else if constexpr (ALIBI) {
     const bool left = j0 + BC - 1 <= i0 + off;  // every key at or before every row's position
     const bool right = j0 >= i_last + off;      // every key at or after every row's position
     const bool rgt = right && !left;
@@ -501,7 +535,8 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   }
 
   // S(t+1) = K(t+1) Q^T
-  if constexpr (!LAST) qk_tile<HD, E>(s_nxt, lb.kl[b1], st.qf);
+  constexpr bool AUG = ALIBI && KV::KEEP_PAD;
+  if constexpr (!LAST) qk_tile<HD, E, AUG>(s_nxt, lb.kl[b1], st.qf, st.baug, st.aug_off);
 
   // P(t) = exp2(S(t) * cs - m), rounded to E for the P V product
   const float negm = (st.m_run == -INFINITY) ? 0.f : st.b_cur - st.m_run;
@@ -629,8 +664,8 @@ __device__ __forceinline__ void tile_step(FwdState<HD, E>& st, const f32x16 (&s_
   // ALiBi tiles, and tiles crossing a mask boundary: bias / mask, then take the max again
   float b_nxt = 0.f;
   if constexpr (ALIBI) {
-    mx = prep_scores<ALIBI, HD == 256>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
-                                       i0, i_last, off, cs, slope, slope_c, half);
+    mx = prep_scores<ALIBI, HD == 256, AUG>(s_nxt, b_nxt, j1, kv.key_hi, my_pos, wl, wr,
+                                            i0, i_last, off, cs, slope, slope_c, half);
   } else {
     const bool nxt_full = (j1 + BC <= kv.key_hi) && (wl < 0 || j1 >= i_last + off - wl) &&
                           (wr < 0 || j1 + BC - 1 <= i0 + off + wr);
@@ -984,6 +1019,26 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const float slope_c = (ALIBI && HD != 256) ? slope / c : 0.f;
   // multiplier turning the stored scores into log2 units
   const float cs = c;
+  constexpr bool AUG = ALIBI && decltype(kv)::KEEP_PAD;
+  if constexpr (AUG) {
+    // the bias step per key in raw score units, g = slope / c, as three parts of E
+    // (their sum is g to about 24 bits): the B operand of the bias product
+    const float g = slope / c;
+    const float g_hi = widen_lo<E>(pack2<E>(g, 0.f));
+    const float g_mid = widen_lo<E>(pack2<E>(g - g_hi, 0.f));
+    const float g_lo = g - g_hi - g_mid;
+    const u32x4 bq = half == 0 ? u32x4{pack2<E>(g_hi, g_mid), pack2<E>(g_lo, 0.f), 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    st.baug = __builtin_bit_cast(x8<E>, bq);
+    st.aug_off = 2 * HD - 16 * half;
+    // A operand: the pad slot of LDS row r holds its key index k_lds_row(r) three times
+    // (exact in E), then zeros; written once per K buffer, the loads skip those slots
+    if (tid < T::NBUF * BC) {
+      const int r = tid % BC;
+      const float k = (float)k_lds_row(r);
+      *(__attribute__((address_space(3))) u32x4*)(lds + (tid / BC) * T::KBYTES + r * T::KPITCH + 2 * HD) =
+          u32x4{pack2<E>(k, k), pack2<E>(k, 0.f), 0u, 0u};
+    }
+  }
 
   f32x16 s_a[2], s_b[2];
 
@@ -996,9 +1051,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
     for (int j = 0; j + 1 < T::NBUF; ++j) kv.load_v(lb.v[j], t_begin + j);
     wait_tile_loads<0>();
     __syncthreads();
-    qk_tile<HD, E>(s_a, lb.kl[0], st.qf);
+    qk_tile<HD, E, AUG>(s_a, lb.kl[0], st.qf, st.baug, st.aug_off);
     const int j0 = kv.tile_key(t_begin);
-    st.m_run = prep_scores<ALIBI, HD == 256>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr,
+    st.m_run = prep_scores<ALIBI, HD == 256, AUG>(s_a, st.b_cur, j0, key_hi, my_pos, wl, wr,
                                              i0w, ilw, off, cs, slope, slope_c, half);
     __syncthreads();  // every wave is done with K(t_begin) before the loop refills its buffer
   }
