@@ -520,7 +520,7 @@ def main():
                               "convention_gflop": round(convention_flops(c.w) / 1e9, 2)}
 
     kernels = " and ".join(f"fa::fwd_kernel<{c.w.headdim},{fwd_waves(c.w.headdim, c.w.seqlen_q, c.w.causal)},"
-                           f"false,false,__bf16> ({c.w.name})" for c in cases)
+                           f"false,false,__bf16,false> ({c.w.name})" for c in cases)
     result = {
         "metric": METRIC,
         "value": round(value, 2),

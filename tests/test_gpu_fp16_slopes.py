@@ -48,6 +48,10 @@ FWD_CASES = [
     (1, 2, 1000, 200, 64, True, -1, -1, "none", "fp16", None),
     (2, 2, 257, 257, 256, True, -1, -1, "batch", "bf16", None),
     (3, 2, 333, 517, 128, False, 30, 60, "batch", "bf16", None),
+    # causal ALiBi (keys right to left, the bias on the matrix cores) with fp16 operands:
+    # the bias step split into fp16 parts, a negative scale
+    (1, 4, 700, 700, 128, True, -1, -1, "head", "fp16", None),
+    (2, 4, 1100, 1100, 64, True, 300, 0, "batch", "fp16", -0.2),
     # eight-wave (256-row) workgroups: headdim 128, no mask, >= 4096 query rows
     (1, 1, 4352, 4352, 128, False, -1, -1, "none", "fp16", None),
     (2, 1, 4100, 3001, 128, False, -1, -1, "batch", "fp16", None),
