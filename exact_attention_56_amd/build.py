@@ -28,7 +28,8 @@ SOURCES = [
     ("fa_fwd_d256.hip", []),
     ("fa_fwd_launch.hip", []),
     # backward: the dQ pass keeps its accumulators in arch VGPRs (two waves per SIMD);
-    # the dK/dV pass holds two accumulators per wave and uses the accumulation registers
+    # the dK/dV pass is left to the compiler's choice: accumulation registers at headdim 256
+    # (one wave per SIMD), arch VGPRs at 128 (two waves per SIMD, V in LDS)
     ("fa_bwd_dq.hip", VGPR_FORM),
     ("fa_bwd.hip", []),
     ("fa_decode_kernel.hip", []),

@@ -37,15 +37,24 @@ namespace fa {
 
 constexpr int BWD_NW = 4;        // waves per workgroup
 constexpr int DQ_TILE = 64;      // keys per streamed tile (dq kernel)
-// Queries per streamed tile (dkdv kernel).  Headdim 128 takes 64 (two independent
-// 32-query blocks per wave: the kernel runs one wave per SIMD there, so it has the
-// registers); headdim 64 takes 32, which keeps it at two waves per SIMD; headdim 256
-// takes 32 (one wave per SIMD: K and V of 32 keys fill 128 registers, dK and dV 256).
+// Queries per streamed tile (dkdv kernel): 32.  Headdim 64 keeps two waves per SIMD that
+// way; headdim 256 runs one wave per SIMD (K and V of 32 keys fill 128 registers, dK and dV
+// 256).  Headdim 128 without V in LDS (below) takes 64: two independent 32-query blocks per
+// wave at one wave per SIMD.
 #ifndef FA_DKV_TILE128
 #define FA_DKV_TILE128 64
 #endif
+// Headdim 128 with V in LDS (VLDS): each wave keeps only K of its 32 keys in registers and
+// reads V from one LDS copy of the workgroup's 128 keys; with 32-query tiles the kernel then
+// fits two waves per SIMD, where one wave per SIMD left it bound by the LDS reads one wave
+// can receive.
+#ifndef FA_DKV_VLDS
+#define FA_DKV_VLDS 1
+#endif
 template <int HD>
-constexpr int dkv_tile() { return HD == 128 ? FA_DKV_TILE128 : 32; }
+constexpr bool dkv_vlds() { return HD == 128 && FA_DKV_VLDS; }
+template <int HD>
+constexpr int dkv_tile() { return HD == 128 ? (dkv_vlds<HD>() ? 32 : FA_DKV_TILE128) : 32; }
 
 // Two bf16 [rows][row_stride] tensors streamed tile by tile (ROWS rows) into LDS in
 // natural row order, rows SA (SB) 16-byte slots apart; direct-to-LDS buffer loads,
@@ -56,7 +65,7 @@ struct PairStream {
   static constexpr int CPR = HD / 8;
   static constexpr int LA = (ROWS * SA + 63) / 64, LB = (ROWS * SB + 63) / 64;
   static constexpr int PWA = (LA + BWD_NW - 1) / BWD_NW, PWB = (LB + BWD_NW - 1) / BWD_NW;
-  static constexpr int ABYTES = 1024 * BWD_NW * PWA, BBYTES = 1024 * BWD_NW * PWB;
+  static constexpr int ABYTES = 1024 * LA, BBYTES = 1024 * LB;  // loads wholly past a tile are not issued
   static_assert(SA >= CPR && SB >= CPR, "a row holds its chunks");
   const uint16_t* abase;
   const uint16_t* bbase;
@@ -399,18 +408,22 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p, int items) {
 //   P = exp2(S c + bias - L'), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by transpose reads; P, dS as B operands)
 template <int HD, bool ALIBI, typename E>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dkv_vlds<HD>() ? 2 : 1))) void dkdv_kernel(
+    BwdParams p, int items) {
   constexpr int DKV_TILE = dkv_tile<HD>(), DKV_QB = DKV_TILE / 32;
+  constexpr bool VLDS = dkv_vlds<HD>();
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature
   constexpr int QS = HD / 8 + 2;  // Q and dO rows: both read both ways
   using Stream = PairStream<HD, DKV_TILE, QS, QS>;
   constexpr int QP = QS * 16;
   constexpr int LDBYTES = 256;    // L' and D of one tile (fp32, 64 lanes x 4 bytes each)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (Stream::ABYTES + Stream::BBYTES + 2 * LDBYTES)];
+  constexpr int VP = (HD / 8 + 1) * 16;  // VLDS: bytes per V row in LDS (16-byte reads, no conflicts)
+  constexpr int VBYTES = VLDS ? BWD_ROWS * VP : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (Stream::ABYTES + Stream::BBYTES + 2 * LDBYTES) + VBYTES];
   lds_u8* const lds = (lds_u8*)smem;
-  // buffer i at lds + i * BUF: Q tile, dO tile, then L and D
+  // buffer i at lds + i * BUF: Q tile, dO tile, then L and D; VLDS: V of the keys after both
   constexpr int BUF = Stream::ABYTES + Stream::BBYTES + 2 * LDBYTES;
-  constexpr int GOFF = Stream::ABYTES, LOFF = Stream::ABYTES + Stream::BBYTES;
+  constexpr int GOFF = Stream::ABYTES, LOFF = Stream::ABYTES + Stream::BBYTES, VOFF = 2 * BUF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,12 +465,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
   const int t_begin = hi >= lo ? lo / DKV_TILE : 0;
   const int t_end = hi >= lo ? hi / DKV_TILE + 1 : 0;
 
-  x8<E> kf[HD / 16], vf[HD / 16];
+  x8<E> kf[HD / 16], vf[VLDS ? 1 : HD / 16];
+  // VLDS: this lane's 16-byte slots of its key's V row in LDS (B operand of dP = dO V^T)
+  const lds_u8* const vrow = lds + VOFF + (32 * wave + lrow) * VP + 16 * half;
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
     kf[kk] = row_fragment<E>(p.k + koff, rsk, my_k, Sk, kk, half, p.q_and, p.q_sign);
-    vf[kk] = row_fragment<E>(p.v + koff, rsk, my_k, Sk, kk, half, 0xffffffffu, 0u);
+    const x8<E> v = row_fragment<E>(p.v + koff, rsk, my_k, Sk, kk, half, 0xffffffffu, 0u);
+    if constexpr (VLDS)
+      *(__attribute__((address_space(3))) x8<E>*)(lds + VOFF + (32 * wave + lrow) * VP + 16 * half + 32 * kk) = v;
+    else
+      vf[kk] = v;
   }
+  // (the first tile's barrier orders these stores before any read)
   const float c = p.scale_log2;
   // visible queries of this key: c_i in [my_k - wr, my_k + wl]
   const int qlo = wr < 0 ? 0 : max(0, my_k - wr - off);
@@ -542,7 +562,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p, int items) {
 #pragma unroll
         for (int qb = 0; qb < DKV_QB; ++qb) {
           s[qb] = mfma32(row_operand<QP, E>(qt, lrow, half, qb, kk), kf[kk], s[qb]);
-          dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vf[kk], dp[qb]);
+          const x8<E> vb = VLDS ? *(const __attribute__((address_space(3))) x8<E>*)(vrow + 32 * kk) : vf[VLDS ? 0 : kk];
+          dp[qb] = mfma32(row_operand<QP, E>(gt, lrow, half, qb, kk), vb, dp[qb]);
         }
 
       // register r of block qb holds query i0 + 32 qb + 16 (r / 8) + 8 half + r % 8 of the tile
