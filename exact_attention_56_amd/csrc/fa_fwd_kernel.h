@@ -277,10 +277,12 @@ __device__ __forceinline__ void wait_tile_loads() {
 // `kt` points at this lane's row lrow, 16-byte slot `half`, of a K buffer.
 // AUG: one more product per block adds g * (key index in the tile) to every score: A is
 // the rows' pad slots (key index k three times, then zeros), B this lane's `baug` (g in
-// three parts of E, half-wave 0; zeros in half-wave 1), at byte offset aug_off from kt.
+// three bf16 parts, half-wave 0; zeros in half-wave 1), at byte offset aug_off from kt.
+// The bias product is bf16 whatever E is: with fp16 a large g (a steep slope over a small
+// softmax scale) would overflow, bf16 has fp32's range.
 template <int HD, typename E, bool AUG = false>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const x8<E> (&qf)[HD / 16],
-                                        const x8<E>& baug = x8<E>{}, int aug_off = 0) {
+                                        const x8<__bf16>& baug = x8<__bf16>{}, int aug_off = 0) {
   using T = Tile<HD, 4>;  // row pitches only: the same for every wave count
   s[0] = f32x16{};
   s[1] = f32x16{};
@@ -295,7 +297,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kt, const 
   if constexpr (AUG) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const x8<E> a = *(const __attribute__((address_space(3))) x8<E>*)(kt + aug_off + 32 * kb * T::KPITCH);
+      const x8<__bf16> a = *(const __attribute__((address_space(3))) x8<__bf16>*)(kt + aug_off + 32 * kb * T::KPITCH);
       s[kb] = mfma32(a, baug, s[kb]);
     }
   }
@@ -408,7 +410,7 @@ struct FwdState {
   float m_run;              // reference maximum of the exponentials (log2 units)
   float l_run;              // this lane's share of the row sum against m_run
   float b_cur;              // log2 offset to add to the stored scores of the tile in s_cur (ALiBi)
-  x8<E> baug;               // B operand of the bias product (qk_tile, AUG)
+  x8<__bf16> baug;          // B operand of the bias product (qk_tile, AUG)
   int aug_off;              // byte offset of this lane's pad slot from its K operand address
 };
 
@@ -1021,22 +1023,23 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, uint8_t* smem, int 
   const float cs = c;
   constexpr bool AUG = ALIBI && decltype(kv)::KEEP_PAD;
   if constexpr (AUG) {
-    // the bias step per key in raw score units, g = slope / c, as three parts of E
+    // the bias step per key in raw score units, g = slope / c, as three bf16 parts
     // (their sum is g to about 24 bits): the B operand of the bias product
     const float g = slope / c;
-    const float g_hi = widen_lo<E>(pack2<E>(g, 0.f));
-    const float g_mid = widen_lo<E>(pack2<E>(g - g_hi, 0.f));
+    const float g_hi = widen_lo<__bf16>(pack2<__bf16>(g, 0.f));
+    const float g_mid = widen_lo<__bf16>(pack2<__bf16>(g - g_hi, 0.f));
     const float g_lo = g - g_hi - g_mid;
-    const u32x4 bq = half == 0 ? u32x4{pack2<E>(g_hi, g_mid), pack2<E>(g_lo, 0.f), 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-    st.baug = __builtin_bit_cast(x8<E>, bq);
+    const u32x4 bq = half == 0 ? u32x4{pack2<__bf16>(g_hi, g_mid), pack2<__bf16>(g_lo, 0.f), 0u, 0u}
+                               : u32x4{0u, 0u, 0u, 0u};
+    st.baug = __builtin_bit_cast(x8<__bf16>, bq);
     st.aug_off = 2 * HD - 16 * half;
     // A operand: the pad slot of LDS row r holds its key index k_lds_row(r) three times
-    // (exact in E), then zeros; written once per K buffer, the loads skip those slots
+    // (exact in bf16), then zeros; written once per K buffer, the loads skip those slots
     if (tid < T::NBUF * BC) {
       const int r = tid % BC;
       const float k = (float)k_lds_row(r);
       *(__attribute__((address_space(3))) u32x4*)(lds + (tid / BC) * T::KBYTES + r * T::KPITCH + 2 * HD) =
-          u32x4{pack2<E>(k, k), pack2<E>(k, 0.f), 0u, 0u};
+          u32x4{pack2<__bf16>(k, k), pack2<__bf16>(k, 0.f), 0u, 0u};
     }
   }
 

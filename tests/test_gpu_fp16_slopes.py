@@ -52,6 +52,10 @@ FWD_CASES = [
     # the bias step split into fp16 parts, a negative scale
     (1, 4, 700, 700, 128, True, -1, -1, "head", "fp16", None),
     (2, 4, 1100, 1100, 64, True, 300, 0, "batch", "fp16", -0.2),
+    # a tiny scale: the bias step per key in raw score units (slope / scale) is far past
+    # the fp16 range, so the bias product runs in bf16
+    (1, 4, 300, 300, 64, True, -1, -1, "head", "fp16", 1e-6),
+    (1, 4, 300, 300, 128, True, 100, 0, "head", "fp16", 1e-6),
     # eight-wave (256-row) workgroups: headdim 128, no mask, >= 4096 query rows
     (1, 1, 4352, 4352, 128, False, -1, -1, "none", "fp16", None),
     (2, 1, 4100, 3001, 128, False, -1, -1, "batch", "fp16", None),
